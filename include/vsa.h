@@ -1,0 +1,184 @@
+/*
+ * vsa.h - C ABI of the MI355X (gfx950) library for hierarchical video sparse
+ * attention: VSA, plus the variable-length key lists of VSA2.
+ *
+ * Sources, cited by page title and section:
+ *   [VSA-abs]  "VSA: Faster Video Diffusion with Trainable Sparse Attention",
+ *              Abstract (arXiv).
+ *   [VSA-sum]  "Faster Video Diffusion with Trainable Sparse Attention"
+ *              (AI-extracted summary page): Approach, Key results,
+ *              Limitations.
+ *   [VSA2-abs] "Improving Video Sparse Attention with Fine-grained Router and
+ *              Sparse Rebasing", Abstract (arXiv).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is a DEVICE pointer unless marked "host".
+ *    Buffers are dense and row-major.  The caller owns all memory; the
+ *    library allocates nothing and keeps no state between calls.
+ *  - Work is queued on `stream` (0 = the null stream).  No call waits for
+ *    the GPU; results are ready when the stream has drained.
+ *  - Arguments are checked before anything is queued.  On any error the
+ *    call returns a non-zero vsa_status and queues nothing.  VSA_ERR_HIP
+ *    reports a failed kernel launch (hipGetLastError after queueing).
+ *  - dtype: VSA_F32 or VSA_BF16 for q, k, v, gates, out and gradients.
+ *    Arithmetic: bf16 operands feed MFMA with fp32 accumulation; softmax,
+ *    pooling and the coarse stage run in fp32; each output is rounded once
+ *    (round to nearest even).  VSA_F32 uses fp32 arithmetic throughout.
+ *  - Shapes: B batch, `heads` heads, head_dim D in {64, 128}; a latent grid
+ *    of T x H x W tokens, N = T*H*W, each of T, H, W a positive multiple of
+ *    4 ([VSA-sum, Limitations]).  Nc = N / 64 cubes.
+ *  - Token order is raster, token (t, y, x) at (t*H + y)*W + x.
+ *    q, k, v, out, dout, dq, dk, dv: [B, N, heads, D].
+ *    gate_c, gate_f, dgate_c, dgate_f: [B, N, heads] (one scalar per token
+ *    and head, broadcast over D).
+ *  - Cubes ([VSA-sum, Approach]): token (t, y, x) lies in cube
+ *    ((t/4)*(H/4) + y/4)*(W/4) + x/4, at slot ((t%4)*4 + y%4)*4 + x%4.
+ *  - Softmax scale is 1/sqrt(D) in both stages.
+ */
+#ifndef VSA_H
+#define VSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VSA_OK = 0,
+  VSA_ERR_INVALID_ARG = 1, /* bad shape, null pointer, topk out of range  */
+  VSA_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, dtype, size  */
+  VSA_ERR_WORKSPACE = 3,   /* workspace_bytes below the required size     */
+  VSA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed  */
+} vsa_status;
+
+typedef enum { VSA_F32 = 0, VSA_BF16 = 1 } vsa_dtype;
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* vsa_status_string(int status);
+
+/* ------------------------------------------------------------------ sizes
+ * Bytes of device scratch each call needs.  0 means the shape is invalid.
+ * n_list_entries: total number of (query cube, key cube) pairs, i.e.
+ * B*heads*Nc*topk for the fixed top-K path, kv_offsets[B*heads*Nc] for
+ * the variable-length path.  Host functions, no GPU work.
+ */
+size_t vsa_forward_workspace_bytes(int B, int heads, int head_dim,
+                                   int T, int H, int W, int dtype);
+size_t vsa_backward_workspace_bytes(int B, int heads, int head_dim,
+                                    int T, int H, int W, int dtype,
+                                    int64_t n_list_entries);
+/* Size of the forward->backward state ("saved"): fp32 coarse output
+ * [B,heads,Nc,D], coarse log-sum-exp [B,heads,Nc], fine log-sum-exp
+ * [B,heads,N] and fine output [B,heads,N,D] (cube-major token order). */
+size_t vsa_saved_bytes(int B, int heads, int head_dim, int T, int H, int W);
+
+/* ---------------------------------------------------------------- forward
+ * vsa_forward: the whole operator ([VSA-sum, Approach]; [VSA-abs]).
+ *  1. permute tokens into cube-major order and mean-pool Q, K, V per cube;
+ *  2. dense cube-to-cube attention on the pooled tensors -> coarse output
+ *     Oc per cube (broadcast to the cube's 64 tokens);
+ *  3. per query cube, the topk key cubes with the largest coarse logits,
+ *     ties to the lower cube index, written ascending to
+ *     sel_idx [B, heads, Nc, topk] (int32);
+ *  4. fine attention of every query token over the 64*topk tokens of its
+ *     cube's selection (online softmax);
+ *  5. out = gate_c * Oc + gate_f * O_fine.
+ * topk in [1, Nc].  `saved` (vsa_saved_bytes) may be NULL for inference;
+ * pass it to vsa_backward.  workspace: vsa_forward_workspace_bytes.
+ */
+int vsa_forward(const void* q, const void* k, const void* v,
+                const void* gate_c, const void* gate_f,
+                int B, int heads, int head_dim, int T, int H, int W,
+                int topk, int dtype,
+                void* out, int32_t* sel_idx, void* saved,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* block_sparse_attn_varlen: as vsa_forward, but step 3 is replaced by a
+ * caller-given list of key cubes per query cube ([VSA2-abs]: each query
+ * attends a variable number of key-value pairs; the router that would make
+ * the lists is not defined on the pages and is not implemented).
+ * kv_offsets [B*heads*Nc + 1] (int32, non-decreasing, kv_offsets[0] = 0)
+ * indexes kv_ids, lists ordered by (b, h, query cube).  n_list_entries
+ * (host) equals kv_offsets[B*heads*Nc].  Ids must lie in [0, Nc) and be
+ * distinct within a list; any order.  An empty list gives O_fine = 0.
+ * Out-of-range ids are not checked on the GPU: the caller guarantees them.
+ */
+int block_sparse_attn_varlen(const void* q, const void* k, const void* v,
+                             const void* gate_c, const void* gate_f,
+                             int B, int heads, int head_dim, int T, int H, int W,
+                             const int32_t* kv_offsets, const int32_t* kv_ids,
+                             int64_t n_list_entries, int dtype,
+                             void* out, void* saved,
+                             void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* --------------------------------------------------------------- backward
+ * Gradients of sum(dout * out) for a forward run with `saved` non-NULL
+ * ([VSA-abs]: one operator trained end-to-end).  The selection is held
+ * fixed (no gradient through the discrete choice); the coarse stage carries
+ * gradient to the pooled tensors, which spread it evenly over each cube's
+ * 64 tokens.  sel_idx / kv lists must be the ones the forward used.
+ * Outputs dq, dk, dv [B,N,heads,D], dgate_c, dgate_f [B,N,heads] are
+ * overwritten.  workspace: vsa_backward_workspace_bytes with
+ * n_list_entries = B*heads*Nc*topk (resp. the varlen total).
+ */
+int vsa_backward(const void* q, const void* k, const void* v,
+                 const void* gate_c, const void* gate_f, const void* dout,
+                 const int32_t* sel_idx, const void* saved,
+                 int B, int heads, int head_dim, int T, int H, int W,
+                 int topk, int dtype,
+                 void* dq, void* dk, void* dv, void* dgate_c, void* dgate_f,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+int block_sparse_attn_varlen_backward(
+    const void* q, const void* k, const void* v,
+    const void* gate_c, const void* gate_f, const void* dout,
+    const int32_t* kv_offsets, const int32_t* kv_ids, int64_t n_list_entries,
+    const void* saved,
+    int B, int heads, int head_dim, int T, int H, int W, int dtype,
+    void* dq, void* dk, void* dv, void* dgate_c, void* dgate_f,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------ stage calls
+ * The forward's steps one at a time, for per-stage checks and timing.
+ * Internal layouts (all written by vsa_cube_permute_pool):
+ *   qp, kp: [B, heads, Nc, 64, D], token slot-major inside each cube;
+ *   vt:     [B, heads, Nc, D, 64], V transposed per cube, with the 64 keys
+ *           stored in MFMA order: inside every group of 16 keys, position
+ *           p holds key (p & 3) + 8*((p >> 2) & 1) + 4*((p >> 3) & 1)
+ *           of that group;
+ *   qc, kc, vc: fp32 [B, heads, Nc, D] cube means.
+ * Element type of qp/kp/vt is `dtype`.
+ */
+int vsa_cube_permute_pool(const void* q, const void* k, const void* v,
+                          int B, int heads, int head_dim, int T, int H, int W,
+                          int dtype, void* qp, void* kp, void* vt,
+                          float* qc, float* kc, float* vc, hipStream_t stream);
+
+/* Coarse stage: Oc [B,heads,Nc,D] fp32, lse_c [B,heads,Nc] fp32 and, when
+ * topk > 0, sel_idx [B,heads,Nc,topk]; topk == 0 skips the selection. */
+int vsa_coarse_topk(const float* qc, const float* kc, const float* vc,
+                    int B, int heads, int head_dim, int n_cubes, int topk,
+                    float* oc, float* lse_c, int32_t* sel_idx,
+                    hipStream_t stream);
+
+/* Fine stage + gated combine.  Key lists: when kv_offsets is NULL, list r
+ * is kv_ids[r*topk .. r*topk + topk); otherwise the CSR lists as in
+ * block_sparse_attn_varlen (topk ignored).  lse_f [B,heads,N] and
+ * o_fine [B,heads,N,D] (fp32, cube-major) are written only if non-NULL
+ * (both or neither). */
+int vsa_fine_forward(const void* qp, const void* kp, const void* vt,
+                     const float* oc, const void* gate_c, const void* gate_f,
+                     int B, int heads, int head_dim, int T, int H, int W,
+                     const int32_t* kv_offsets, const int32_t* kv_ids, int topk,
+                     int dtype, void* out, float* lse_f, float* o_fine,
+                     hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VSA_H */

@@ -1,0 +1,84 @@
+"""Helpers shared by the GPU parity tests: device upload of seeded inputs,
+the tolerance checks and the top-K comparison rule.  Nothing here computes
+attention; expected values come from the fp64 oracle."""
+import math
+import sys
+
+import numpy as np
+import torch
+
+# Parity bars.  fp32 path: max abs 1e-4.  bf16 inputs with fp32
+# accumulation: max abs 2e-2 and relative RMS 4e-3 over the whole tensor.
+F32_MAX_ABS = 1e-4
+BF16_MAX_ABS = 2e-2
+BF16_REL_RMS = 4e-3
+# Near-tie exemption for top-K rows, read on probabilities: the K-th and
+# (K+1)-th coarse probabilities within a factor (1 - 1e-3), i.e. logits
+# within -ln(1 - 1e-3).
+TIE_LOGIT_GAP = -math.log1p(-1e-3)
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x, dtype):
+    """fp32 numpy (bf16-exact when dtype is bf16) -> contiguous GPU tensor."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(dtype).cuda().contiguous()
+
+
+def host64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def assert_close(actual, expected, dtype, what=""):
+    actual = np.asarray(actual, dtype=np.float64)
+    expected = np.asarray(expected, dtype=np.float64)
+    assert actual.shape == expected.shape, (what, actual.shape, expected.shape)
+    assert np.all(np.isfinite(actual)), f"{what}: non-finite values"
+    err = np.abs(actual - expected)
+    max_abs = float(err.max()) if err.size else 0.0
+    if dtype == torch.float32:
+        assert max_abs <= F32_MAX_ABS, f"{what}: max abs {max_abs:.3e} > {F32_MAX_ABS}"
+        return max_abs, None
+    denom = float(np.linalg.norm(expected))
+    rel = float(np.linalg.norm(actual - expected)) / denom if denom > 0 else float(np.linalg.norm(actual))
+    assert max_abs <= BF16_MAX_ABS, f"{what}: max abs {max_abs:.3e} > {BF16_MAX_ABS}"
+    assert rel <= BF16_REL_RMS, f"{what}: rel RMS {rel:.3e} > {BF16_REL_RMS}"
+    return max_abs, rel
+
+
+def check_selection_row(sel_row, logits_row, K):
+    """GPU top-K ids of one query cube against the fp64 logits.
+
+    Returns True when the row equals the exact top-K (logit desc, index asc),
+    False when it differs only at a near-tie (every differing cube within
+    TIE_LOGIT_GAP of the K-th logit); raises otherwise.  The ids must be K
+    distinct, ascending values in range.
+    """
+    sel_row = np.asarray(sel_row, dtype=np.int64)
+    nc = logits_row.shape[0]
+    assert sel_row.shape == (K,)
+    assert np.all(np.diff(sel_row) > 0), f"ids not strictly ascending: {sel_row}"
+    assert sel_row.min() >= 0 and sel_row.max() < nc
+    order = np.lexsort((np.arange(nc), -logits_row))
+    ref = np.sort(order[:K])
+    if np.array_equal(ref, sel_row):
+        return True
+    kth = logits_row[order[K - 1]]
+    diff = np.setxor1d(ref, sel_row)
+    bad = diff[np.abs(logits_row[diff] - kth) > TIE_LOGIT_GAP]
+    assert bad.size == 0, f"selection differs beyond near-ties: ids {bad}, gaps {logits_row[bad] - kth}"
+    return False
+
+
+def check_selection(sel, S, K):
+    """All rows; returns the number of exempted near-tie rows."""
+    sel = np.asarray(sel)
+    exempt = 0
+    for idx in np.ndindex(sel.shape[:-1]):
+        if not check_selection_row(sel[idx], S[idx], K):
+            exempt += 1
+    return exempt

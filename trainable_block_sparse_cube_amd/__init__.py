@@ -1,0 +1,8 @@
+"""MI355X (gfx950) hierarchical video sparse attention: VSA and the
+variable-length key lists of VSA2, as a C-ABI HIP library (libvsa.so) with
+a thin PyTorch binding."""
+from .ops import (  # noqa: F401
+    block_sparse_attn_varlen, block_sparse_attn_varlen_backward, saved_bytes,
+    vsa_backward, vsa_coarse_topk, vsa_cube_permute_pool, vsa_fine_forward,
+    vsa_forward,
+)

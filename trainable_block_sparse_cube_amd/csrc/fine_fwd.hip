@@ -1,0 +1,353 @@
+// Fine stage: block-sparse token attention over the selected cubes, with the
+// gated combine fused into the epilogue.
+//
+// [VSA-abs] ("VSA: Faster Video Diffusion with Trainable Sparse Attention",
+// Abstract): the fine stage computes token-level attention only inside the
+// tiles picked by the coarse stage, in a block layout.  [VSA-sum, Approach]:
+// each cube maps to one GPU tile and the two stages are combined through
+// gates.  [VSA2-abs]: each query may attend a variable number of key-value
+// pairs, so the key lists may be variable-length (CSR).
+//
+// bf16 kernel (MFMA, gfx950).  One workgroup = 4 waves = one query cube of
+// 64 tokens.  Wave w takes query half qh = w & 1 (slots 32qh..+32) and key
+// half kh = w >> 1 of every selected tile (keys 32kh..+32).  Per tile:
+//   S^T (32 keys x 32 queries) = K * Q^T          D/16 x mfma 32x32x16 bf16
+//   fp32 online softmax along keys: each lane holds one query column, so
+//   the running max/sum are lane-local up to one exchange between the two
+//   half-waves (v_permlane32_swap)
+//   O^T (D x 32) += V^T * P^T                      D/16 x mfma 32x32x16
+// Each wave keeps its own softmax state over its key half; the two halves
+// are merged once at the end (split softmax).  K and V^T tiles (16 KB each
+// at D = 128) are copied straight from global memory into LDS
+// (global_load_lds, no register staging) with an XOR chunk swizzle, double
+// buffered: tile t+1 streams in while tile t is computed, one barrier per
+// tile.  The epilogue divides by the row sum, mixes in the coarse output
+// with the two gates, rounds once to bf16 and scatters rows back to raster
+// token order.
+//
+// fp32 kernel: plain VALU, one wave per query cube, one lane per query
+// token; it serves the fp32 path, where no reduced precision is allowed.
+#include "vsa_device.h"
+#include "vsa_launch.h"
+
+namespace vsa {
+
+namespace {
+
+__device__ __forceinline__ int raster_token(int c, int s, int Hg, int Wg) {
+  const int W4 = Wg >> 2, H4 = Hg >> 2;
+  const int ct = c / (H4 * W4), cy = (c / W4) % H4, cx = c % W4;
+  return ((4 * ct + (s >> 4)) * Hg + 4 * cy + ((s >> 2) & 3)) * Wg + 4 * cx + (s & 3);
+}
+
+// XOR swizzles of 16-byte chunk columns in LDS tiles (bank-conflict-free
+// MFMA operand reads).  K tile rows are D*2 bytes; V^T rows are 128 bytes.
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (D == 128) return row & 15;
+  else return (row ^ (row >> 3)) & 7;
+}
+__device__ __forceinline__ int swz_v(int row) { return (row ^ (row >> 3)) & 7; }
+
+// vmcnt-only wait (expcnt and lgkmcnt left at their maxima), gfx9 encoding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One 16-byte global -> LDS copy per lane; lane l of the wave writes LDS
+// bytes [16 l, 16 l + 16) past `lds_wave_base` (wave-uniform).
+__device__ __forceinline__ void copy16_to_lds(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
+    const bf16* __restrict__ qp, const bf16* __restrict__ kp, const bf16* __restrict__ vt,
+    const float* __restrict__ oc, const bf16* __restrict__ gc, const bf16* __restrict__ gf,
+    int nh, int nc, int Hg, int Wg,
+    const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk,
+    float scale_log2,
+    bf16* __restrict__ out, float* __restrict__ lse_f, float* __restrict__ o_fine) {
+  constexpr int KS = D / 16;          // k-steps of S^T over head_dim
+  constexpr int KCH = D / 8;          // 16-byte chunks per K row
+  constexpr int TILE_CH = 64 * KCH;   // chunks per K (and per V^T) tile
+  constexpr int LD = TILE_CH / 256;   // copy instructions per wave per tile and tensor
+  constexpr int MD = D / 32;          // m-blocks of O^T
+  // Lazy rescaling: the running max moves only when a tile's max exceeds
+  // it by more than this many powers of two (exact; bounds p by 2^8).
+  constexpr float kRescale = 8.f;
+
+  // Two buffers (tile parity) of K and V^T.  Separate arrays, picked at run
+  // time, so that the compiler adds no waits of its own for the copies; the
+  // waits below (vmcnt + barrier) order every copy before its reads.
+  __shared__ __align__(16) u32x4 k_lds0[TILE_CH];
+  __shared__ __align__(16) u32x4 k_lds1[TILE_CH];
+  __shared__ __align__(16) u32x4 v_lds0[TILE_CH];
+  __shared__ __align__(16) u32x4 v_lds1[TILE_CH];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int qh = wave & 1;   // query half: slots 32*qh .. +32
+  const int kh = wave >> 1;  // key half of every tile: keys 32*kh .. +32
+  const int ql = lane & 31, hf = lane >> 5;
+
+  const int blk = blockIdx.x;  // (b*nh + h)*nc + c
+  const int bh = blk / nc;
+  const int c = blk - bh * nc;
+  const int64_t N = (int64_t)nc * 64;
+  int start, n;
+  if (offs) { start = offs[blk]; n = offs[blk + 1] - start; }
+  else { start = blk * topk; n = topk; }
+  const int32_t* list = ids + start;
+  const int64_t bh_tiles = (int64_t)bh * nc;
+
+  // Copy K tile and V^T tile of key cube kc into buffer `buf`, XOR-swizzled:
+  // the lane landing on LDS chunk P = (row, phys) fetches chunk phys ^ swz.
+  auto copy_tile = [&](int kc, int buf) {
+    const bf16* ksrc = kp + (bh_tiles + kc) * 64 * D;
+    const bf16* vsrc = vt + (bh_tiles + kc) * 64 * D;
+    u32x4* kdst = buf ? k_lds1 : k_lds0;
+    u32x4* vdst = buf ? v_lds1 : v_lds0;
+#pragma unroll
+    for (int j = 0; j < LD; ++j) {
+      const int P = (4 * j + wave) * 64 + lane;
+      const int krow = P / KCH, kphys = P % KCH;
+      copy16_to_lds(ksrc + (krow * KCH + (kphys ^ swz_k<D>(krow))) * 8, kdst + (4 * j + wave) * 64);
+      const int vrow = P >> 3, vphys = P & 7;
+      copy16_to_lds(vsrc + (vrow * 8 + (vphys ^ swz_v(vrow))) * 8, vdst + (4 * j + wave) * 64);
+    }
+  };
+
+  // Q^T operands: lane (query ql of this half, half-wave hf) holds
+  // d = (D/2)*hf + 8s .. +8.
+  bf16x8 qB[KS];
+  {
+    const bf16* qrow = qp + ((bh_tiles + c) * 64 + 32 * qh + ql) * D + (D / 2) * hf;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qB[s] = *reinterpret_cast<const bf16x8*>(qrow + 8 * s);
+  }
+  if (n > 0) copy_tile(list[0], 0);
+
+  f32x16 oacc[MD];
+#pragma unroll
+  for (int m = 0; m < MD; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[m][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const int krow = 32 * kh + ql;  // this lane's K row (A operand of S^T)
+
+  for (int it = 0; it < n; ++it) {
+    const int buf = it & 1;
+    wait_vmcnt<0>();   // this wave's copies of tile `it` have landed
+    __syncthreads();   // all copies of tile `it` visible; buffer buf^1 free
+    if (it + 1 < n) copy_tile(list[it + 1], buf ^ 1);
+    const u32x4* kb = buf ? k_lds1 : k_lds0;
+    const u32x4* vb = buf ? v_lds1 : v_lds0;
+
+    // Operands of both products are read from LDS up front, so the LDS
+    // latency overlaps the MFMA chain instead of stalling each step.
+    bf16x8 ka[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      ka[s] = *reinterpret_cast<const bf16x8*>(&kb[krow * KCH + ((KS * hf + s) ^ swz_k<D>(krow))]);
+    bf16x8 va[MD][2];
+#pragma unroll
+    for (int m = 0; m < MD; ++m)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int row = 32 * m + ql;
+        va[m][g] = *reinterpret_cast<const bf16x8*>(&vb[row * 8 + ((4 * kh + 2 * g + hf) ^ swz_v(row))]);
+      }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads batched ahead of their MFMAs
+
+    // S^T (32 keys x 32 queries) = K[32kh..] * Q[32qh..]^T
+    f32x16 sacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qB[s], sacc, 0, 0, 0);
+
+    // Online softmax over this wave's 32 keys, per query column ql.
+    float mx = sacc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+    mx = fmaxf(mx, swap_halves(mx)) * scale_log2;
+    const bool grow = mx > m_run + kRescale;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int m = 0; m < MD; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[m][r] *= alpha;
+    }
+    bf16x8 pB[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[8 * g + e], scale_log2, -m_run));
+        l_run += p;
+        pB[g][e] = (bf16)p;
+      }
+
+    // O^T += V^T[:, 32kh..] * P^T : two k-steps of 16 keys.
+#pragma unroll
+    for (int m = 0; m < MD; ++m)
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+        oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[m][g], pB[g], oacc[m], 0, 0, 0);
+  }
+
+  // Merge the two key halves (split softmax): waves with kh = 1 hand their
+  // (m, l, O) to the kh = 0 wave of the same query half through LDS.
+  l_run += swap_halves(l_run);
+  __syncthreads();  // all tile reads done; the buffers are free
+  float* xo = reinterpret_cast<float*>(qh ? k_lds1 : k_lds0);  // 32 q x D floats
+  float* xs = reinterpret_cast<float*>(qh ? v_lds1 : v_lds0);  // m, l per query
+  if (kh == 1) {
+#pragma unroll
+    for (int m = 0; m < MD; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[(m * 16 + r) * 64 + lane] = oacc[m][r];
+    if (hf == 0) { xs[ql] = m_run; xs[32 + ql] = l_run; }
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  const float m_o = xs[ql], l_o = xs[32 + ql];
+  const float m_max = fmaxf(m_run, m_o);
+  const float a_s = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_max);
+  const float a_o = m_o == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_o - m_max);
+  const float l_tot = l_run * a_s + l_o * a_o;
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+
+  // Epilogue: normalise, gate-combine with the coarse output, scatter.
+  const int slot = 32 * qh + ql;
+  const int b = bh / nh, h = bh - b * nh;
+  const int tok = raster_token(c, slot, Hg, Wg);
+  const int64_t gidx = ((int64_t)b * N + tok) * nh + h;
+  const float g_c = (float)gc[gidx], g_f = (float)gf[gidx];
+  const float* ocrow = oc + (bh_tiles + c) * D;
+  bf16* orow = out + gidx * D;
+  float* ofrow = o_fine ? o_fine + ((int64_t)bh * N + (int64_t)c * 64 + slot) * D : nullptr;
+#pragma unroll
+  for (int m = 0; m < MD; ++m)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = 32 * m + 8 * rg + 4 * hf;
+      const f32x4 ocv = *reinterpret_cast<const f32x4*>(ocrow + d0);
+      f32x4 of;
+      bf16x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * rg + i;
+        of[i] = (oacc[m][r] * a_s + xo[(m * 16 + r) * 64 + lane] * a_o) * inv;
+        o[i] = (bf16)fmaf(g_c, ocv[i], g_f * of[i]);
+      }
+      *reinterpret_cast<bf16x4*>(orow + d0) = o;
+      if (ofrow) *reinterpret_cast<f32x4*>(ofrow + d0) = of;
+    }
+  if (lse_f && hf == 0)
+    lse_f[(int64_t)bh * N + (int64_t)c * 64 + slot] =
+        l_tot > 0.f ? (m_max + log2f(l_tot)) * kLn2 : -INFINITY;
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void fine_fwd_f32_kernel(
+    const float* __restrict__ qp, const float* __restrict__ kp, const float* __restrict__ vt,
+    const float* __restrict__ oc, const float* __restrict__ gc, const float* __restrict__ gf,
+    int nh, int nc, int Hg, int Wg,
+    const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk, float scale,
+    float* __restrict__ out, float* __restrict__ lse_f, float* __restrict__ o_fine) {
+  __shared__ float k_lds[64 * D];
+  __shared__ float v_lds[D * 64];
+  const int slot = threadIdx.x;
+  const int blk = blockIdx.x;
+  const int bh = blk / nc;
+  const int c = blk - bh * nc;
+  const int64_t N = (int64_t)nc * 64;
+  int start, n;
+  if (offs) { start = offs[blk]; n = offs[blk + 1] - start; }
+  else { start = blk * topk; n = topk; }
+
+  float qv[D], acc[D];
+  const float* qrow = qp + (((int64_t)bh * nc + c) * 64 + slot) * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) { qv[d] = qrow[d]; acc[d] = 0.f; }
+  float m_run = -INFINITY, l_run = 0.f;
+  for (int it = 0; it < n; ++it) {
+    const int kc = ids[start + it];
+    const float* ks = kp + ((int64_t)bh * nc + kc) * 64 * D;
+    const float* vs = vt + ((int64_t)bh * nc + kc) * 64 * D;
+    __syncthreads();
+    for (int i = slot; i < 64 * D; i += 64) { k_lds[i] = ks[i]; v_lds[i] = vs[i]; }
+    __syncthreads();
+    float sj[64];
+    float mx = -INFINITY;
+    for (int j = 0; j < 64; ++j) {
+      float s = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) s = fmaf(qv[d], k_lds[j * D + d], s);
+      sj[j] = s * scale;
+      mx = fmaxf(mx, sj[j]);
+    }
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = expf(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] *= alpha;
+    for (int p = 0; p < 64; ++p) {  // storage position p holds key vt_key_of_pos(p)
+      const float w = expf(sj[vt_key_of_pos(p)] - m_new);
+      l_run += w;
+#pragma unroll
+      for (int d = 0; d < D; ++d) acc[d] = fmaf(w, v_lds[d * 64 + p], acc[d]);
+    }
+  }
+  const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+  const int b = bh / nh, h = bh - b * nh;
+  const int tok = raster_token(c, slot, Hg, Wg);
+  const int64_t gidx = ((int64_t)b * N + tok) * nh + h;
+  const float g_c = gc[gidx], g_f = gf[gidx];
+  const float* ocrow = oc + ((int64_t)bh * nc + c) * D;
+  float* ofrow = o_fine ? o_fine + ((int64_t)bh * N + (int64_t)c * 64 + slot) * D : nullptr;
+  for (int d = 0; d < D; ++d) {
+    const float of = acc[d] * inv;
+    out[gidx * D + d] = fmaf(g_c, ocrow[d], g_f * of);
+    if (ofrow) ofrow[d] = of;
+  }
+  if (lse_f) lse_f[(int64_t)bh * N + (int64_t)c * 64 + slot] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
+}
+
+template <int D>
+hipError_t launch_fine_d(const FineArgs& a, hipStream_t st) {
+  const int nc = (a.T / 4) * (a.H / 4) * (a.W / 4);
+  const unsigned grid = (unsigned)(a.B * a.heads * nc);
+  const float scale = 1.0f / sqrtf((float)D);
+  if (a.bf16) {
+    fine_fwd_bf16_kernel<D><<<grid, 256, 0, st>>>(
+        (const bf16*)a.qp, (const bf16*)a.kp, (const bf16*)a.vt, a.oc,
+        (const bf16*)a.gc, (const bf16*)a.gf, a.heads, nc, a.H, a.W, a.offs, a.ids, a.topk,
+        scale * kLog2e, (bf16*)a.out, a.lse_f, a.o_fine);
+  } else {
+    fine_fwd_f32_kernel<D><<<grid, 64, 0, st>>>(
+        (const float*)a.qp, (const float*)a.kp, (const float*)a.vt, a.oc,
+        (const float*)a.gc, (const float*)a.gf, a.heads, nc, a.H, a.W, a.offs, a.ids, a.topk,
+        scale, (float*)a.out, a.lse_f, a.o_fine);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fine_forward(const FineArgs& a, hipStream_t st) {
+  return a.D == 128 ? launch_fine_d<128>(a, st) : launch_fine_d<64>(a, st);
+}
+
+}  // namespace vsa

@@ -1,0 +1,114 @@
+// Cube permute + mean pooling (one pass over Q, K, V).
+//
+// [VSA-sum, Approach] ("Faster Video Diffusion with Trainable Sparse
+// Attention", summary page): tokens are grouped into 4x4x4 cubes, each cube
+// is one tile of the fine stage, and Q/K/V are mean-pooled per cube for the
+// coarse stage.  One workgroup handles one (batch, cube, head) of one tensor:
+// it gathers the cube's 64 token rows (each row D contiguous elements in the
+// raster layout), writes them as one contiguous cube-major tile, and reduces
+// the 64 rows to their fp32 mean with wavefront shuffles plus a 4-way LDS
+// combine.  Each tensor can be written in natural order ([64 tokens][D]),
+// transposed ([D][64 tokens], tokens in MFMA order, so that MFMA steps
+// contracting over tokens read 16-byte vectors), or both.  The forward uses
+// natural Q, K and transposed V; the backward natural Q, K, V and
+// transposed Q, K.
+#include "vsa_device.h"
+#include "vsa_launch.h"
+
+namespace vsa {
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void permute_pool_kernel(PermutePoolPtrs p, int nh, int Tg, int Hg, int Wg) {
+  constexpr int EPC = 16 / sizeof(T);     // elements per 16-byte chunk
+  constexpr int CPR = D / EPC;            // chunks per token row
+  constexpr int ROWS_PER_PASS = 256 / CPR;
+  constexpr int PASSES = kCubeTokens / ROWS_PER_PASS;
+  constexpr int VT_PITCH = kCubeTokens + EPC;  // padded LDS row of a transposed tile
+  static_assert(256 % CPR == 0 && kCubeTokens % ROWS_PER_PASS == 0, "tiling");
+
+  __shared__ __align__(16) T vt_lds[D * VT_PITCH];
+  __shared__ float red[4][D];
+
+  const int which = blockIdx.y;  // 0: q, 1: k, 2: v
+  const T* __restrict__ src = (const T*)p.src[which];
+  T* __restrict__ nat = (T*)p.nat[which];
+  T* __restrict__ tr = (T*)p.tr[which];
+  float* __restrict__ pooled = p.pooled[which];
+
+  const int nc = (Tg / 4) * (Hg / 4) * (Wg / 4);
+  const int N = Tg * Hg * Wg;
+  const int h = blockIdx.x % nh;
+  const int bc = blockIdx.x / nh;
+  const int c = bc % nc;
+  const int b = bc / nc;
+  const int W4 = Wg / 4, H4 = Hg / 4;
+  const int ct = c / (H4 * W4), cy = (c / W4) % H4, cx = c % W4;
+  const int64_t tile = ((int64_t)(b * nh + h) * nc + c) * kCubeTokens * D;
+
+  const int tid = threadIdx.x;
+  const int ch = tid % CPR;  // this thread's chunk column, fixed over passes
+  float acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int s = tid / CPR + ps * ROWS_PER_PASS;  // slot in cube
+    const int tok = ((4 * ct + (s >> 4)) * Hg + 4 * cy + ((s >> 2) & 3)) * Wg + 4 * cx + (s & 3);
+    const T* rowp = src + ((int64_t)b * N + tok) * nh * D + (int64_t)h * D;
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(rowp + ch * EPC);
+    T vals[EPC];
+    __builtin_memcpy(vals, &raw, 16);
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] += to_f32(vals[e]);
+    if (nat) *reinterpret_cast<u32x4*>(nat + tile + (int64_t)s * D + ch * EPC) = raw;
+    if (tr) {
+      const int pos = vt_key_of_pos(s);  // storage position of token s
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) vt_lds[(ch * EPC + e) * VT_PITCH + pos] = vals[e];
+    }
+  }
+
+  if (pooled) {
+    // Sum over the lanes of this wave that hold the same chunk column.
+#pragma unroll
+    for (int o = CPR; o < 64; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], o);
+    const int wave = tid >> 6, lane = tid & 63;
+    if (lane < CPR) {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) red[wave][lane * EPC + e] = acc[e];
+    }
+  }
+  __syncthreads();
+  if (pooled) {
+    for (int d = tid; d < D; d += 256) {
+      const float sum = (red[0][d] + red[1][d]) + (red[2][d] + red[3][d]);
+      pooled[((int64_t)(b * nh + h) * nc + c) * D + d] = sum * (1.0f / kCubeTokens);
+    }
+  }
+  if (tr) {
+    constexpr int VCPR = kCubeTokens / EPC;  // chunks per transposed row
+    for (int i = tid; i < D * VCPR; i += 256) {
+      const int d = i / VCPR, cc = i % VCPR;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(&vt_lds[d * VT_PITCH + cc * EPC]);
+      *reinterpret_cast<u32x4*>(tr + tile + (int64_t)d * kCubeTokens + cc * EPC) = val;
+    }
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_pp(const PermutePoolArgs& a, hipStream_t st) {
+  const int nc = (a.T / 4) * (a.H / 4) * (a.W / 4);
+  dim3 grid((unsigned)(a.B * nc * a.heads), 3);
+  permute_pool_kernel<T, D><<<grid, 256, 0, st>>>(a.p, a.heads, a.T, a.H, a.W);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_pool(const PermutePoolArgs& a, hipStream_t st) {
+  if (a.bf16) return a.D == 128 ? launch_pp<bf16, 128>(a, st) : launch_pp<bf16, 64>(a, st);
+  return a.D == 128 ? launch_pp<float, 128>(a, st) : launch_pp<float, 64>(a, st);
+}
+
+}  // namespace vsa

@@ -1,0 +1,226 @@
+// C ABI of the library: argument checks, workspace carving and the order of
+// kernel launches on the caller's stream.  Declarations and the contract of
+// every entry point are in include/vsa.h.
+#include "../../include/vsa.h"
+#include "vsa_launch.h"
+
+#include <climits>
+#include <cmath>
+
+using namespace vsa;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+struct Shape {
+  int B, heads, D, T, H, W, dtype;
+  int64_t N, nc;
+  size_t elt;
+};
+
+// Shape checks shared by every entry point; fills `s` on success.
+int check_shape(int B, int heads, int D, int T, int H, int W, int dtype, Shape* s) {
+  if (B < 1 || heads < 1 || T < 4 || H < 4 || W < 4) return VSA_ERR_INVALID_ARG;
+  if (T % 4 || H % 4 || W % 4) return VSA_ERR_INVALID_ARG;  // whole 4x4x4 cubes only
+  if (dtype != VSA_F32 && dtype != VSA_BF16) return VSA_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return VSA_ERR_UNSUPPORTED;
+  const int64_t N = (int64_t)T * H * W;
+  const int64_t nc = N / 64;
+  if ((int64_t)B * heads > 65535) return VSA_ERR_UNSUPPORTED;  // grid y dimension
+  if (N > INT_MAX / 2 || (int64_t)B * heads * nc > INT_MAX / 2 || (int64_t)B * N * heads > INT_MAX)
+    return VSA_ERR_UNSUPPORTED;
+  if (nc > coarse_max_cubes(D)) return VSA_ERR_UNSUPPORTED;
+  *s = Shape{B, heads, D, T, H, W, dtype, N, nc, dtype == VSA_BF16 ? 2u : 4u};
+  return VSA_OK;
+}
+
+struct FwdWorkspace {
+  void *qp, *kp, *vt;
+  float *qc, *kc, *vc, *oc, *lse_c;
+};
+
+size_t fwd_ws_layout(const Shape& s, char* base, FwdWorkspace* w) {
+  const size_t tile_bytes = align_up((size_t)s.B * s.heads * s.N * s.D * s.elt);
+  const size_t pooled = align_up((size_t)s.B * s.heads * s.nc * s.D * sizeof(float));
+  const size_t lse = align_up((size_t)s.B * s.heads * s.nc * sizeof(float));
+  size_t off = 0;
+  auto take = [&](size_t bytes) { char* p = base ? base + off : nullptr; off += bytes; return (void*)p; };
+  FwdWorkspace t;
+  t.qp = take(tile_bytes); t.kp = take(tile_bytes); t.vt = take(tile_bytes);
+  t.qc = (float*)take(pooled); t.kc = (float*)take(pooled); t.vc = (float*)take(pooled);
+  t.oc = (float*)take(pooled); t.lse_c = (float*)take(lse);
+  if (w) *w = t;
+  return off;
+}
+
+struct Saved {
+  float *oc, *lse_c, *lse_f, *of;
+};
+
+size_t saved_layout(const Shape& s, char* base, Saved* sv) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) { char* p = base ? base + off : nullptr; off += align_up(bytes); return (float*)p; };
+  Saved t;
+  t.oc = take((size_t)s.B * s.heads * s.nc * s.D * sizeof(float));
+  t.lse_c = take((size_t)s.B * s.heads * s.nc * sizeof(float));
+  t.lse_f = take((size_t)s.B * s.heads * s.N * sizeof(float));
+  t.of = take((size_t)s.B * s.heads * s.N * s.D * sizeof(float));
+  if (sv) *sv = t;
+  return off;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_HIP; }
+
+// Shared body of vsa_forward and block_sparse_attn_varlen.
+int forward_impl(const void* q, const void* k, const void* v, const void* gc, const void* gf,
+                 const Shape& s, int topk, const int32_t* offs, const int32_t* ids,
+                 int32_t* sel, void* out, void* saved, void* ws, size_t ws_bytes,
+                 hipStream_t st) {
+  FwdWorkspace w;
+  if (ws_bytes < fwd_ws_layout(s, nullptr, nullptr)) return VSA_ERR_WORKSPACE;
+  fwd_ws_layout(s, (char*)ws, &w);
+  float *oc = w.oc, *lse_c = w.lse_c, *lse_f = nullptr, *of = nullptr;
+  if (saved) {
+    Saved sv;
+    saved_layout(s, (char*)saved, &sv);
+    oc = sv.oc; lse_c = sv.lse_c; lse_f = sv.lse_f; of = sv.of;
+  }
+  const bool bf = s.dtype == VSA_BF16;
+  PermutePoolArgs pa{{{q, k, v}, {w.qp, w.kp, nullptr}, {nullptr, nullptr, w.vt}, {w.qc, w.kc, w.vc}},
+                     s.B, s.heads, s.D, s.T, s.H, s.W, bf};
+  hipError_t e = launch_permute_pool(pa, st);
+  if (e != hipSuccess) return VSA_ERR_HIP;
+  CoarseArgs ca{w.qc, w.kc, w.vc, s.B, s.heads, s.D, (int)s.nc, offs ? 0 : topk, oc, lse_c, sel};
+  e = launch_coarse_topk(ca, st);
+  if (e != hipSuccess) return VSA_ERR_HIP;
+  FineArgs fa{w.qp, w.kp, w.vt, oc, gc, gf, s.B, s.heads, s.D, s.T, s.H, s.W,
+              offs, offs ? ids : sel, topk, bf, out, lse_f, of};
+  return hip_status(launch_fine_forward(fa, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vsa_status_string(int status) {
+  switch (status) {
+    case VSA_OK: return "ok";
+    case VSA_ERR_INVALID_ARG: return "invalid argument";
+    case VSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case VSA_ERR_WORKSPACE: return "workspace too small";
+    case VSA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t vsa_forward_workspace_bytes(int B, int heads, int head_dim, int T, int H, int W, int dtype) {
+  Shape s;
+  if (check_shape(B, heads, head_dim, T, H, W, dtype, &s) != VSA_OK) return 0;
+  return fwd_ws_layout(s, nullptr, nullptr);
+}
+
+size_t vsa_saved_bytes(int B, int heads, int head_dim, int T, int H, int W) {
+  Shape s;
+  if (check_shape(B, heads, head_dim, T, H, W, VSA_F32, &s) != VSA_OK) return 0;
+  return saved_layout(s, nullptr, nullptr);
+}
+
+int vsa_forward(const void* q, const void* k, const void* v, const void* gate_c, const void* gate_f,
+                int B, int heads, int head_dim, int T, int H, int W, int topk, int dtype,
+                void* out, int32_t* sel_idx, void* saved, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  Shape s;
+  int st = check_shape(B, heads, head_dim, T, H, W, dtype, &s);
+  if (st != VSA_OK) return st;
+  if (!q || !k || !v || !gate_c || !gate_f || !out || !sel_idx || !workspace) return VSA_ERR_INVALID_ARG;
+  if (topk < 1 || topk > s.nc) return VSA_ERR_INVALID_ARG;
+  if ((int64_t)B * heads * s.nc * topk > INT_MAX) return VSA_ERR_UNSUPPORTED;
+  return forward_impl(q, k, v, gate_c, gate_f, s, topk, nullptr, nullptr, sel_idx, out, saved,
+                      workspace, workspace_bytes, stream);
+}
+
+int block_sparse_attn_varlen(const void* q, const void* k, const void* v,
+                             const void* gate_c, const void* gate_f,
+                             int B, int heads, int head_dim, int T, int H, int W,
+                             const int32_t* kv_offsets, const int32_t* kv_ids,
+                             int64_t n_list_entries, int dtype, void* out, void* saved,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Shape s;
+  int st = check_shape(B, heads, head_dim, T, H, W, dtype, &s);
+  if (st != VSA_OK) return st;
+  if (!q || !k || !v || !gate_c || !gate_f || !out || !kv_offsets || !workspace) return VSA_ERR_INVALID_ARG;
+  if (n_list_entries < 0 || n_list_entries > (int64_t)B * heads * s.nc * s.nc) return VSA_ERR_INVALID_ARG;
+  if (n_list_entries > 0 && !kv_ids) return VSA_ERR_INVALID_ARG;
+  if (n_list_entries > INT_MAX) return VSA_ERR_UNSUPPORTED;
+  return forward_impl(q, k, v, gate_c, gate_f, s, 0, kv_offsets, kv_ids, nullptr, out, saved,
+                      workspace, workspace_bytes, stream);
+}
+
+int vsa_cube_permute_pool(const void* q, const void* k, const void* v,
+                          int B, int heads, int head_dim, int T, int H, int W, int dtype,
+                          void* qp, void* kp, void* vt, float* qc, float* kc, float* vc,
+                          hipStream_t stream) {
+  Shape s;
+  int st = check_shape(B, heads, head_dim, T, H, W, dtype, &s);
+  if (st != VSA_OK) return st;
+  if (!q || !k || !v || !qp || !kp || !vt || !qc || !kc || !vc) return VSA_ERR_INVALID_ARG;
+  PermutePoolArgs pa{{{q, k, v}, {qp, kp, nullptr}, {nullptr, nullptr, vt}, {qc, kc, vc}},
+                     B, heads, head_dim, T, H, W, dtype == VSA_BF16};
+  return hip_status(launch_permute_pool(pa, stream));
+}
+
+int vsa_coarse_topk(const float* qc, const float* kc, const float* vc,
+                    int B, int heads, int head_dim, int n_cubes, int topk,
+                    float* oc, float* lse_c, int32_t* sel_idx, hipStream_t stream) {
+  if (B < 1 || heads < 1 || n_cubes < 1) return VSA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return VSA_ERR_UNSUPPORTED;
+  if (n_cubes > coarse_max_cubes(head_dim) || (int64_t)B * heads > 65535) return VSA_ERR_UNSUPPORTED;
+  if (topk < 0 || topk > n_cubes) return VSA_ERR_INVALID_ARG;
+  if (!qc || !kc || !vc || !oc || !lse_c || (topk > 0 && !sel_idx)) return VSA_ERR_INVALID_ARG;
+  if ((int64_t)B * heads * n_cubes > INT_MAX / 2 || (int64_t)B * heads * n_cubes * topk > INT_MAX)
+    return VSA_ERR_UNSUPPORTED;
+  CoarseArgs ca{qc, kc, vc, B, heads, head_dim, n_cubes, topk, oc, lse_c, sel_idx};
+  return hip_status(launch_coarse_topk(ca, stream));
+}
+
+int vsa_fine_forward(const void* qp, const void* kp, const void* vt, const float* oc,
+                     const void* gate_c, const void* gate_f,
+                     int B, int heads, int head_dim, int T, int H, int W,
+                     const int32_t* kv_offsets, const int32_t* kv_ids, int topk, int dtype,
+                     void* out, float* lse_f, float* o_fine, hipStream_t stream) {
+  Shape s;
+  int st = check_shape(B, heads, head_dim, T, H, W, dtype, &s);
+  if (st != VSA_OK) return st;
+  if (!qp || !kp || !vt || !oc || !gate_c || !gate_f || !out) return VSA_ERR_INVALID_ARG;
+  if ((lse_f == nullptr) != (o_fine == nullptr)) return VSA_ERR_INVALID_ARG;
+  if (!kv_offsets) {
+    if (topk < 1 || topk > s.nc || !kv_ids) return VSA_ERR_INVALID_ARG;
+    if ((int64_t)B * heads * s.nc * topk > INT_MAX) return VSA_ERR_UNSUPPORTED;
+  }
+  FineArgs fa{qp, kp, vt, oc, gate_c, gate_f, B, heads, head_dim, T, H, W,
+              kv_offsets, kv_ids, topk, dtype == VSA_BF16, out, lse_f, o_fine};
+  return hip_status(launch_fine_forward(fa, stream));
+}
+
+size_t vsa_backward_workspace_bytes(int B, int heads, int head_dim, int T, int H, int W, int dtype,
+                                    int64_t n_list_entries) {
+  (void)B; (void)heads; (void)head_dim; (void)T; (void)H; (void)W; (void)dtype; (void)n_list_entries;
+  return 0;
+}
+
+int vsa_backward(const void*, const void*, const void*, const void*, const void*, const void*,
+                 const int32_t*, const void*, int, int, int, int, int, int, int, int,
+                 void*, void*, void*, void*, void*, void*, size_t, hipStream_t) {
+  return VSA_ERR_UNSUPPORTED;
+}
+
+int block_sparse_attn_varlen_backward(const void*, const void*, const void*, const void*, const void*,
+                                      const void*, const int32_t*, const int32_t*, int64_t, const void*,
+                                      int, int, int, int, int, int, int,
+                                      void*, void*, void*, void*, void*, void*, size_t, hipStream_t) {
+  return VSA_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

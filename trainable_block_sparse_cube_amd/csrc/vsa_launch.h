@@ -1,0 +1,51 @@
+// Host-side launch interface between the C ABI (vsa_api.hip) and the
+// kernel files.  Arguments are validated by the caller of these functions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vsa {
+
+// Per tensor (q, k, v): raster source [B, N, heads, D]; optional outputs
+// natural cube-major tiles [B, heads, Nc, 64, D], transposed tiles
+// [B, heads, Nc, D, 64] (tokens in MFMA order) and fp32 means [B, heads, Nc, D].
+struct PermutePoolPtrs {
+  const void* src[3];
+  void* nat[3];
+  void* tr[3];
+  float* pooled[3];
+};
+struct PermutePoolArgs {
+  PermutePoolPtrs p;
+  int B, heads, D, T, H, W;
+  bool bf16;
+};
+hipError_t launch_permute_pool(const PermutePoolArgs& a, hipStream_t st);
+
+struct CoarseArgs {
+  const float *qc, *kc, *vc;
+  int B, heads, D, nc, topk;
+  float *oc, *lse;
+  int32_t* sel;  // may be null when topk == 0
+};
+// Largest number of cubes the coarse kernel accepts.
+int coarse_max_cubes(int D);
+hipError_t launch_coarse_topk(const CoarseArgs& a, hipStream_t st);
+
+struct FineArgs {
+  const void *qp, *kp, *vt;
+  const float* oc;
+  const void *gc, *gf;  // [B, N, heads]
+  int B, heads, D, T, H, W;
+  const int32_t* offs;  // null: fixed-length lists of `topk`
+  const int32_t* ids;
+  int topk;
+  bool bf16;
+  void* out;            // [B, N, heads, D]
+  float* lse_f;         // [B, heads, N] cube-major, optional
+  float* o_fine;        // [B, heads, N, D] cube-major, optional
+};
+hipError_t launch_fine_forward(const FineArgs& a, hipStream_t st);
+
+}  // namespace vsa

@@ -1,0 +1,182 @@
+"""PyTorch-facing binding of libvsa.so.
+
+Argument marshalling only: shape/dtype checks, output and workspace
+allocation through torch's caching allocator, raw device pointers and the
+current HIP stream handed to the C entry points of include/vsa.h.  Every
+step of the computation runs in the library's HIP kernels; there is no
+fallback path.  Tensors use raster token order:
+q, k, v, out: [B, N, heads, D]; gates: [B, N, heads]; N = T*H*W.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.VSA_F32, torch.bfloat16: _lib.VSA_BF16}
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check_inputs(q, k, v, gate_c, gate_f, grid):
+    if q.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("gate_c", gate_c), ("gate_f", gate_f)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {q.dtype}")
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, N, heads, D] shape")
+    B, N, nh, D = q.shape
+    T, H, W = grid
+    if T * H * W != N:
+        raise ValueError(f"grid {grid} has {T * H * W} tokens, tensors have {N}")
+    if gate_c.shape != (B, N, nh) or gate_f.shape != (B, N, nh):
+        raise ValueError("gates must be [B, N, heads]")
+    return B, N, nh, D, T, H, W, _DT[q.dtype]
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def saved_bytes(B, heads, D, grid):
+    return _lib.load().vsa_saved_bytes(B, heads, D, *grid)
+
+
+def vsa_forward(q, k, v, gate_c, gate_f, grid, topk, save=False):
+    """Returns (out, sel_idx [B, heads, Nc, topk] int32, saved or None)."""
+    lib = _lib.load()
+    B, N, nh, D, T, H, W, dt = _check_inputs(q, k, v, gate_c, gate_f, grid)
+    nc = N // 64
+    out = torch.empty_like(q)
+    sel = torch.empty((B, nh, nc, topk), dtype=torch.int32, device=q.device)
+    saved = _workspace(lib.vsa_saved_bytes(B, nh, D, T, H, W), q.device) if save else None
+    wsb = lib.vsa_forward_workspace_bytes(B, nh, D, T, H, W, dt)
+    ws = _workspace(wsb, q.device)
+    st = lib.vsa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(gate_c), _ptr(gate_f),
+                         B, nh, D, T, H, W, topk, dt, _ptr(out), _ptr(sel), _ptr(saved),
+                         _ptr(ws), wsb, _stream())
+    _lib.check("vsa_forward", st)
+    return out, sel, saved
+
+
+def _check_lists(kv_offsets, kv_ids, B, nh, nc):
+    for name, t in (("kv_offsets", kv_offsets), ("kv_ids", kv_ids)):
+        if not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 GPU tensor")
+    if kv_offsets.shape != (B * nh * nc + 1,):
+        raise ValueError("kv_offsets must have B*heads*Nc + 1 entries")
+
+
+def block_sparse_attn_varlen(q, k, v, gate_c, gate_f, grid, kv_offsets, kv_ids, save=False):
+    """Variable-length key-cube lists (CSR over (b, h, query cube)).
+    Returns (out, saved or None)."""
+    lib = _lib.load()
+    B, N, nh, D, T, H, W, dt = _check_inputs(q, k, v, gate_c, gate_f, grid)
+    nc = N // 64
+    _check_lists(kv_offsets, kv_ids, B, nh, nc)
+    out = torch.empty_like(q)
+    saved = _workspace(lib.vsa_saved_bytes(B, nh, D, T, H, W), q.device) if save else None
+    wsb = lib.vsa_forward_workspace_bytes(B, nh, D, T, H, W, dt)
+    ws = _workspace(wsb, q.device)
+    st = lib.block_sparse_attn_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(gate_c), _ptr(gate_f),
+                                      B, nh, D, T, H, W, _ptr(kv_offsets), _ptr(kv_ids),
+                                      int(kv_ids.numel()), dt, _ptr(out), _ptr(saved),
+                                      _ptr(ws), wsb, _stream())
+    _lib.check("block_sparse_attn_varlen", st)
+    return out, saved
+
+
+def vsa_backward(q, k, v, gate_c, gate_f, dout, sel, saved, grid):
+    """Gradients of sum(dout * out) for a forward run with save=True.
+    Returns (dq, dk, dv, dgate_c, dgate_f)."""
+    lib = _lib.load()
+    B, N, nh, D, T, H, W, dt = _check_inputs(q, k, v, gate_c, gate_f, grid)
+    if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_contiguous():
+        raise ValueError("dout must match q")
+    topk = sel.shape[-1]
+    grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+             torch.empty_like(gate_c), torch.empty_like(gate_f)]
+    wsb = lib.vsa_backward_workspace_bytes(B, nh, D, T, H, W, dt, int(sel.numel()))
+    ws = _workspace(wsb, q.device)
+    st = lib.vsa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(gate_c), _ptr(gate_f), _ptr(dout),
+                          _ptr(sel), _ptr(saved), B, nh, D, T, H, W, topk, dt,
+                          *[_ptr(g) for g in grads], _ptr(ws), wsb, _stream())
+    _lib.check("vsa_backward", st)
+    return tuple(grads)
+
+
+def block_sparse_attn_varlen_backward(q, k, v, gate_c, gate_f, dout, kv_offsets, kv_ids, saved, grid):
+    lib = _lib.load()
+    B, N, nh, D, T, H, W, dt = _check_inputs(q, k, v, gate_c, gate_f, grid)
+    _check_lists(kv_offsets, kv_ids, B, nh, N // 64)
+    grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+             torch.empty_like(gate_c), torch.empty_like(gate_f)]
+    n = int(kv_ids.numel())
+    wsb = lib.vsa_backward_workspace_bytes(B, nh, D, T, H, W, dt, n)
+    ws = _workspace(wsb, q.device)
+    st = lib.block_sparse_attn_varlen_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate_c), _ptr(gate_f), _ptr(dout),
+        _ptr(kv_offsets), _ptr(kv_ids), n, _ptr(saved), B, nh, D, T, H, W, dt,
+        *[_ptr(g) for g in grads], _ptr(ws), wsb, _stream())
+    _lib.check("block_sparse_attn_varlen_backward", st)
+    return tuple(grads)
+
+
+# ------------------------------------------------------------ stage calls
+def vsa_cube_permute_pool(q, k, v, grid):
+    """Returns (qp, kp, vt, qc, kc, vc) in the library's cube-major layouts."""
+    lib = _lib.load()
+    B, N, nh, D = q.shape
+    dt = _DT[q.dtype]
+    nc = N // 64
+    qp = torch.empty((B, nh, nc, 64, D), dtype=q.dtype, device=q.device)
+    kp = torch.empty_like(qp)
+    vt = torch.empty((B, nh, nc, D, 64), dtype=q.dtype, device=q.device)
+    pooled = [torch.empty((B, nh, nc, D), dtype=torch.float32, device=q.device) for _ in range(3)]
+    st = lib.vsa_cube_permute_pool(_ptr(q), _ptr(k), _ptr(v), B, nh, D, *grid, dt,
+                                   _ptr(qp), _ptr(kp), _ptr(vt), *[_ptr(p) for p in pooled], _stream())
+    _lib.check("vsa_cube_permute_pool", st)
+    return (qp, kp, vt, *pooled)
+
+
+def vsa_coarse_topk(qc, kc, vc, topk):
+    """Returns (oc, lse_c, sel or None) for fp32 pooled [B, heads, Nc, D]."""
+    lib = _lib.load()
+    B, nh, nc, D = qc.shape
+    oc = torch.empty_like(qc)
+    lse = torch.empty((B, nh, nc), dtype=torch.float32, device=qc.device)
+    sel = torch.empty((B, nh, nc, topk), dtype=torch.int32, device=qc.device) if topk > 0 else None
+    st = lib.vsa_coarse_topk(_ptr(qc), _ptr(kc), _ptr(vc), B, nh, D, nc, topk,
+                             _ptr(oc), _ptr(lse), _ptr(sel), _stream())
+    _lib.check("vsa_coarse_topk", st)
+    return oc, lse, sel
+
+
+def vsa_fine_forward(qp, kp, vt, oc, gate_c, gate_f, grid, kv_ids, topk=0, kv_offsets=None,
+                     out=None, save=False):
+    """Fine stage + gated combine.  Returns (out, lse_f or None, o_fine or None)."""
+    lib = _lib.load()
+    B, nh, nc, _, D = qp.shape
+    N = nc * 64
+    if out is None:
+        out = torch.empty((B, N, nh, D), dtype=qp.dtype, device=qp.device)
+    lse = of = None
+    if save:
+        lse = torch.empty((B, nh, N), dtype=torch.float32, device=qp.device)
+        of = torch.empty((B, nh, N, D), dtype=torch.float32, device=qp.device)
+    st = lib.vsa_fine_forward(_ptr(qp), _ptr(kp), _ptr(vt), _ptr(oc), _ptr(gate_c), _ptr(gate_f),
+                              B, nh, D, *grid, _ptr(kv_offsets), _ptr(kv_ids), topk,
+                              _DT[qp.dtype], _ptr(out), _ptr(lse), _ptr(of), _stream())
+    _lib.check("vsa_fine_forward", st)
+    return out, lse, of
