@@ -15,7 +15,7 @@
 //      with a bitwise search for the K-th largest key plus a ballot-based
 //      ordered compaction, which also emits the ids ascending; then the
 //      softmax statistics, and S is overwritten by the probabilities;
-//   3. Oc = P * vc with fp32 MFMA, vc streamed through LDS.
+//   3. Oc = P * vc with fp32 MFMA, vc operands read straight from L2.
 // Everything is fp32: the ranking must match an fp64 reference exactly
 // except at near-ties.
 #include "vsa_device.h"
@@ -33,29 +33,107 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ int wave_sum_i(int x) {
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// Largest t such that at least k of the wave's 64 lane values are >= t
+// (k in [1, 64]): greedy bitwise search, one ballot per bit.
+__device__ __forceinline__ uint32_t kth_largest_of_lanes(uint32_t x, int k) {
+  uint32_t thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    if (__popcll(__ballot(x >= cand)) >= k) thr = cand;
+  }
+  return thr;
 }
 
-typedef float f32x4v __attribute__((ext_vector_type(4)));
+// Rank selection for one row held by one wave.  `keys` holds this lane's
+// order keys of entries lane + 64 j (0 past the end; real order keys are
+// never 0).  Writes the topk entries with the largest (key, -index) to
+// out[0..topk), ascending by index.  `cand` is per-wave LDS scratch of
+// 64 * MAXJ words.
+//
+// The K-th largest key is found by a bitwise search over a pruned candidate
+// set: for K <= 64 the K-th largest of the 64 per-lane maxima is a lower
+// bound on the row's K-th largest key (the lane maxima are row entries), so
+// only entries at or above it take part.
+template <int MAXJ>
+__device__ __forceinline__ void select_row(const uint32_t (&keys)[MAXJ], int nc, int topk,
+                                           int lane, uint32_t* __restrict__ cand,
+                                           int32_t* __restrict__ out) {
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  uint32_t lo = 0;
+  if (topk <= 64) {
+    uint32_t lane_max = 0;
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) lane_max = max(lane_max, keys[j]);
+    lo = kth_largest_of_lanes(lane_max, topk);
+  }
+  // Compact the candidates (key >= lo) into LDS.
+  int ncand = 0;
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    if (64 * j < nc) {
+      const bool in = keys[j] >= lo && keys[j] != 0u;
+      const uint64_t m = __ballot(in);
+      if (in) cand[ncand + __popcll(m & lt_mask)] = keys[j];
+      ncand += __popcll(m);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  // K-th largest key among the candidates.  The greedy search starts from
+  // 0: for probes c <= lo every candidate counts (>= K of them, as in the
+  // full row), for c > lo the candidates are all entries >= c, so every
+  // decision matches a search over the whole row.
+  uint32_t thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = thr | (1u << bit);
+    int cnt = 0;
+    for (int i0 = 0; i0 < ncand; i0 += 64) {
+      const int i = i0 + lane;
+      cnt += __popcll(__ballot(i < ncand && cand[i] >= c));
+    }
+    if (cnt >= topk) thr = c;
+  }
+  int n_gt = 0;
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j)
+    if (64 * j < nc) n_gt += __popcll(__ballot(keys[j] > thr));
+  const int need_eq = topk - n_gt;
+  int base = 0, eq_seen = 0;
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    if (64 * j < nc) {
+      const int idx = 64 * j + lane;
+      const bool valid = idx < nc;
+      const bool gt = valid && keys[j] > thr;
+      const bool eq = valid && keys[j] == thr;
+      const uint64_t eq_mask = __ballot(eq);
+      const bool take = gt || (eq && (eq_seen + __popcll(eq_mask & lt_mask)) < need_eq);
+      const uint64_t take_mask = __ballot(take);
+      const int pos = base + __popcll(take_mask & lt_mask);
+      if (take && pos < topk) out[pos] = idx;
+      base += __popcll(take_mask);
+      eq_seen += __popcll(eq_mask);
+    }
+  }
+}
 
 // One workgroup: R = 16 query rows of one (batch, head), 4 waves.
 // Matrix products use v_mfma_f32_16x16x4f32 (fp32 in, fp32 accumulate).
 // Lane l of a 16x16x4 step supplies row/column l % 16 and k-slice l / 16.
-template <int D>
+template <int D, int MAXJ>
 __global__ __launch_bounds__(256, 2) void coarse_topk_kernel(
     const float* __restrict__ qc, const float* __restrict__ kc,
     const float* __restrict__ vc, int nc, int topk, float scale,
     float* __restrict__ oc, float* __restrict__ lse, int32_t* __restrict__ sel) {
   constexpr int R = 16;
   constexpr int DQ = D / 4;          // head_dim slice per lane group
-  constexpr int VCH = 16;            // value rows per LDS chunk
-  constexpr int VPITCH = D + 4;
+  constexpr int NB = D / 64;         // 16-column output blocks per wave
   extern __shared__ float lds[];
-  const int s_pitch = (nc + 19) & ~3;  // room for a zero-padded last value chunk
+  const int s_pitch = (nc + 35) & ~3;  // room for a zero-padded last key block
   float* S = lds;                      // [R][s_pitch]
-  float* vch = S + R * s_pitch;        // [VCH][VPITCH]
+  uint32_t* cand_all = reinterpret_cast<uint32_t*>(S + R * s_pitch);  // [4][64 * MAXJ]
 
   const int bh = blockIdx.y;
   const int row0 = blockIdx.x * R;
@@ -67,7 +145,8 @@ __global__ __launch_bounds__(256, 2) void coarse_topk_kernel(
   const float* vcb = vc + (int64_t)bh * nc * D;
 
   // ---- 1. logits.  Contraction over head_dim: lane group lg covers
-  // d in [lg*DQ, lg*DQ + DQ), one element per k-step.
+  // d in [lg*DQ, lg*DQ + DQ), one element per k-step.  The next 16-key
+  // block's operands are fetched while the current one is multiplied.
   f32x4v qa[DQ / 4];
   {
     const int row = min(row0 + li, nc - 1);  // rows past the end are never stored
@@ -75,17 +154,24 @@ __global__ __launch_bounds__(256, 2) void coarse_topk_kernel(
 #pragma unroll
     for (int i = 0; i < DQ / 4; ++i) qa[i] = src[i];
   }
+  auto load_k = [&](int j0, f32x4v (&kb)[DQ / 4]) {
+    const f32x4v* src = reinterpret_cast<const f32x4v*>(kcb + (int64_t)min(j0 + li, nc - 1) * D + lg * DQ);
+#pragma unroll
+    for (int i = 0; i < DQ / 4; ++i) kb[i] = src[i];
+  };
+  f32x4v kb[DQ / 4], kn[DQ / 4];
+  if (16 * wave < nc) load_k(16 * wave, kn);
   for (int j0 = 16 * wave; j0 < nc; j0 += 64) {
-    const int key = j0 + li;
-    const f32x4v* src = reinterpret_cast<const f32x4v*>(kcb + (int64_t)min(key, nc - 1) * D + lg * DQ);
+#pragma unroll
+    for (int i = 0; i < DQ / 4; ++i) kb[i] = kn[i];
+    if (j0 + 64 < nc) load_k(j0 + 64, kn);
     f32x4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < DQ / 4; ++i) {
-      const f32x4v kb = src[i];
+    for (int i = 0; i < DQ / 4; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][e], kb[e], acc, 0, 0, 0);
-    }
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][e], kb[i][e], acc, 0, 0, 0);
+    const int key = j0 + li;
     if (key < nc) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) S[(4 * lg + r) * s_pitch + key] = acc[r] * scale;
@@ -94,7 +180,6 @@ __global__ __launch_bounds__(256, 2) void coarse_topk_kernel(
   __syncthreads();
 
   // ---- 2. per-row top-K and softmax, one wave per row
-  const uint64_t lt_mask = (1ull << lane) - 1ull;
   for (int rr = wave; rr < R; rr += 4) {
     const int row = row0 + rr;
     float* Srow = S + rr * s_pitch;
@@ -103,67 +188,60 @@ __global__ __launch_bounds__(256, 2) void coarse_topk_kernel(
       continue;
     }
     if (topk > 0) {
-      uint32_t thr = 0;
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = thr | (1u << bit);
-        int cnt = 0;
-        for (int j = lane; j < nc; j += 64) cnt += order_key(Srow[j]) >= cand;
-        if (wave_sum_i(cnt) >= topk) thr = cand;
+      uint32_t keys[MAXJ];
+#pragma unroll
+      for (int j = 0; j < MAXJ; ++j) {
+        const int idx = 64 * j + lane;
+        keys[j] = idx < nc ? order_key(Srow[idx]) : 0u;
       }
-      int n_gt = 0;
-      for (int j = lane; j < nc; j += 64) n_gt += order_key(Srow[j]) > thr;
-      const int need_eq = topk - wave_sum_i(n_gt);
-      int32_t* out = sel + ((int64_t)bh * nc + row) * topk;
-      int base = 0, eq_seen = 0;
-      for (int jb = 0; jb < nc; jb += 64) {
-        const int j = jb + lane;
-        const uint32_t key = j < nc ? order_key(Srow[j]) : 0u;
-        const bool gt = j < nc && key > thr;
-        const bool eq = j < nc && key == thr;
-        const uint64_t eq_mask = __ballot(eq);
-        const bool take = gt || (eq && (eq_seen + __popcll(eq_mask & lt_mask)) < need_eq);
-        const uint64_t take_mask = __ballot(take);
-        const int pos = base + __popcll(take_mask & lt_mask);
-        if (take && pos < topk) out[pos] = j;
-        base += __popcll(take_mask);
-        eq_seen += __popcll(eq_mask);
-      }
+      select_row<MAXJ>(keys, nc, topk, lane, cand_all + wave * 64 * MAXJ,
+                       sel + ((int64_t)bh * nc + row) * topk);
     }
     float m = -INFINITY;
     for (int j = lane; j < nc; j += 64) m = fmaxf(m, Srow[j]);
     m = wave_max(m);
+    // exp(x) as 2^(x log2 e): one v_exp_f32 per entry.
+    const float m2 = m * kLog2e;
     float z = 0.f;
-    for (int j = lane; j < nc; j += 64) z += expf(Srow[j] - m);
+    for (int j = lane; j < nc; j += 64) z += __builtin_amdgcn_exp2f(fmaf(Srow[j], kLog2e, -m2));
     z = wave_sum(z);
     const float inv = 1.0f / z;
-    for (int j = lane; j < s_pitch; j += 64) Srow[j] = j < nc ? expf(Srow[j] - m) * inv : 0.f;
+    for (int j = lane; j < s_pitch; j += 64)
+      Srow[j] = j < nc ? __builtin_amdgcn_exp2f(fmaf(Srow[j], kLog2e, -m2)) * inv : 0.f;
     if (lane == 0) lse[(int64_t)bh * nc + row] = m + logf(z);
   }
+  __syncthreads();
 
-  // ---- 3. Oc = P * vc.  Wave w owns output columns [32w, 32w + 32)
-  // (two 16-column blocks; D = 64 uses one); contraction over keys with
-  // lane group lg taking key j0 + 4t + lg at k-step t.
-  constexpr int NB = D / 64;  // 16-column blocks per wave
+  // ---- 3. Oc = P * vc.  Wave w owns output columns [D/4 * w, +D/4) in
+  // NB blocks of 16; contraction over keys, lane group lg taking key
+  // j0 + 4t + lg at k-step t.  B operands come straight from L2 (vc of one
+  // head is small), the next 32-key block prefetched during the current.
   f32x4v oacc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x4v{0.f, 0.f, 0.f, 0.f};
-  for (int j0 = 0; j0 < nc; j0 += VCH) {
-    __syncthreads();
-    for (int i = tid; i < VCH * (D / 4); i += 256) {
-      const int j = i / (D / 4), d4 = i % (D / 4);
-      f32x4v val = {0.f, 0.f, 0.f, 0.f};
-      if (j0 + j < nc) val = reinterpret_cast<const f32x4v*>(vcb + (int64_t)(j0 + j) * D)[d4];
-      *reinterpret_cast<f32x4v*>(&vch[j * VPITCH + 4 * d4]) = val;
-    }
-    __syncthreads();
+  const int col0 = (D / 4) * wave + li;
+  auto load_v = [&](int j0, float (&vbuf)[8][NB]) {
 #pragma unroll
-    for (int t = 0; t < VCH / 4; ++t) {
-      const int j = 4 * t + lg;
-      const float pa = S[li * s_pitch + j0 + j];
+    for (int t = 0; t < 8; ++t) {
+      const int key = min(j0 + 4 * t + lg, nc - 1);  // P is 0 past the end
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) vbuf[t][nb] = vcb[(int64_t)key * D + col0 + 16 * nb];
+    }
+  };
+  float vb[8][NB], vn[8][NB];
+  load_v(0, vn);
+  for (int j0 = 0; j0 < nc; j0 += 32) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) vb[t][nb] = vn[t][nb];
+    if (j0 + 32 < nc) load_v(j0 + 32, vn);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float pa = S[li * s_pitch + j0 + 4 * t + lg];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-            pa, vch[j * VPITCH + (D / 4) * wave + 16 * nb + li], oacc[nb], 0, 0, 0);
+        oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vb[t][nb], oacc[nb], 0, 0, 0);
     }
   }
 #pragma unroll
@@ -171,33 +249,46 @@ __global__ __launch_bounds__(256, 2) void coarse_topk_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = row0 + 4 * lg + r;
-      if (row < nc) oc[((int64_t)bh * nc + row) * D + (D / 4) * wave + 16 * nb + li] = oacc[nb][r];
+      if (row < nc) oc[((int64_t)bh * nc + row) * D + col0 + 16 * nb] = oacc[nb][r];
     }
 }
 
-size_t coarse_lds_bytes(int D, int nc) {
-  const int s_pitch = (nc + 19) & ~3;
-  return sizeof(float) * ((size_t)16 * s_pitch + (size_t)16 * (D + 4));
+size_t coarse_lds_bytes(int nc, int maxj) {
+  const int s_pitch = (nc + 35) & ~3;
+  return sizeof(float) * ((size_t)16 * s_pitch + (size_t)4 * 64 * maxj);
 }
 
-template <int D>
-hipError_t launch_coarse_d(const CoarseArgs& a, hipStream_t st) {
-  const size_t lds = coarse_lds_bytes(D, a.nc);
-  auto kern = coarse_topk_kernel<D>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
+template <int D, int MAXJ>
+hipError_t launch_coarse_dj(const CoarseArgs& a, hipStream_t st) {
+  const size_t lds = coarse_lds_bytes(a.nc, MAXJ);
+  auto kern = coarse_topk_kernel<D, MAXJ>;
+  // Raise the dynamic LDS limit once per kernel instance (host-side call).
+  static size_t lds_limit = 0;
+  if (lds > lds_limit) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    lds_limit = lds;
+  }
   dim3 grid((unsigned)((a.nc + 15) / 16), (unsigned)(a.B * a.heads));
   kern<<<grid, 256, lds, st>>>(a.qc, a.kc, a.vc, a.nc, a.topk, 1.0f / sqrtf((float)D),
                                 a.oc, a.lse, a.sel);
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_coarse_d(const CoarseArgs& a, hipStream_t st) {
+  if (a.nc <= 16 * 64) return launch_coarse_dj<D, 16>(a, st);
+  return launch_coarse_dj<D, 40>(a, st);
+}
+
 }  // namespace
 
 int coarse_max_cubes(int D) {
-  // 16 rows of logits (padded) and one 16-row value chunk must fit in LDS.
-  const size_t rows = (kLdsBudget / sizeof(float) - 16 * (size_t)(D + 4)) / 16;
-  return (int)rows - 19;
+  (void)D;
+  // 16 rows of logits plus candidate scratch in LDS, and at most 40 key
+  // chunks of 64 per row.
+  const int by_lds = (int)((kLdsBudget / sizeof(float) - 4 * 64 * 40) / 16) - 35;
+  return by_lds < 40 * 64 ? by_lds : 40 * 64;
 }
 
 hipError_t launch_coarse_topk(const CoarseArgs& a, hipStream_t st) {
