@@ -30,8 +30,10 @@
  *    4 ([VSA-sum, Limitations]).  Nc = N / 64 cubes.
  *  - Token order is raster, token (t, y, x) at (t*H + y)*W + x.
  *    q, k, v, out, dout, dq, dk, dv: [B, N, heads, D].
- *    gate_c, gate_f, dgate_c, dgate_f: [B, N, heads] (one scalar per token
- *    and head, broadcast over D).
+ *    gate_c, gate_f: [B, N, heads] (one scalar per token and head,
+ *    broadcast over D).  dgate_c, dgate_f: [B, N, heads], always fp32: they
+ *    are D-long dot products whose magnitude (~10 at unit-scale inputs)
+ *    puts bf16 rounding above the accuracy the method is checked to.
  *  - Cubes ([VSA-sum, Approach]): token (t, y, x) lies in cube
  *    ((t/4)*(H/4) + y/4)*(W/4) + x/4, at slot ((t%4)*4 + y%4)*4 + x%4.
  *  - Softmax scale is 1/sqrt(D) in both stages.
@@ -122,8 +124,9 @@ int block_sparse_attn_varlen(const void* q, const void* k, const void* v,
  * fixed (no gradient through the discrete choice); the coarse stage carries
  * gradient to the pooled tensors, which spread it evenly over each cube's
  * 64 tokens.  sel_idx / kv lists must be the ones the forward used.
- * Outputs dq, dk, dv [B,N,heads,D], dgate_c, dgate_f [B,N,heads] are
- * overwritten.  workspace: vsa_backward_workspace_bytes with
+ * Outputs dq, dk, dv [B,N,heads,D] (dtype) and dgate_c, dgate_f [B,N,heads]
+ * (fp32) are overwritten.  Only dtype VSA_BF16 is built (VSA_F32 returns
+ * VSA_ERR_UNSUPPORTED).  workspace: vsa_backward_workspace_bytes with
  * n_list_entries = B*heads*Nc*topk (resp. the varlen total).
  */
 int vsa_backward(const void* q, const void* k, const void* v,

@@ -325,3 +325,72 @@ def query_cube_output(q, k, v, gc, gf, grid, b, h, c, key_ids, scale=None):
         of = np.zeros((64, D))
     o = _as64(gc[b, rows, h])[:, None] * oc_row[None, :] + _as64(gf[b, rows, h])[:, None] * of
     return rows, o, oc_row, logits
+
+
+def backward_sampled(q, k, v, gc, gf, dout, grid, key_lists_bh, b, h, query_cubes, key_cubes,
+                     scale=None):
+    """Gradients of sum(dout * o) for one (batch, head), restricted to a few
+    cubes, with the same formulas as backward(): dq, dg_c and dg_f of the
+    tokens of `query_cubes`; dk and dv of the tokens of `key_cubes`.  Used
+    for sampled checks where the full backward is too slow.
+
+    key_lists_bh[c]: key cube ids of query cube c for this (b, h).
+    Returns dict: for each query cube c, ("dq", c) -> [64, D] and
+    ("dgc", c), ("dgf", c) -> [64]; for each key cube j, ("dk", j), ("dv", j)
+    -> [64, D]; rows ordered as cube_members(...)[cube].
+    """
+    T, H, W = grid
+    qb = _as64(q[b, :, h]); kb = _as64(k[b, :, h]); vb = _as64(v[b, :, h])
+    G = _as64(dout[b, :, h]); gcb = _as64(gc[b, :, h]); gfb = _as64(gf[b, :, h])
+    D = qb.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    members = cube_members(T, H, W)
+    cube, _ = token_cube_map(T, H, W)
+    nc = members.shape[0]
+    qc, kc, vc = pool(qb, T, H, W), pool(kb, T, H, W), pool(vb, T, H, W)
+    oc, S, lse_c = coarse_attention(qc, kc, vc, scale)
+    # coarse backward (whole head; it is small)
+    dOc = np.zeros((nc, D))
+    np.add.at(dOc, cube, gcb[:, None] * G)
+    Pc = np.exp(S - lse_c[:, None])
+    dVc = Pc.T @ dOc
+    dSc = Pc * (dOc @ vc.T - np.sum(dOc * oc, axis=1)[:, None])
+    dQc = scale * (dSc @ kc)
+    dKc = scale * (dSc.T @ qc)
+    key_set = set(int(j) for j in key_cubes)
+    needed = set(int(c) for c in query_cubes)
+    for c in range(nc):
+        if key_set.intersection(int(j) for j in key_lists_bh[c]):
+            needed.add(c)
+    out = {}
+    for j in key_set:
+        out[("dk", j)] = dKc[j][None, :].repeat(64, 0) / CUBE_TOKENS
+        out[("dv", j)] = dVc[j][None, :].repeat(64, 0) / CUBE_TOKENS
+    for c in sorted(needed):
+        rows = members[c]
+        ids = np.asarray(key_lists_bh[c], dtype=np.int64)
+        if c in query_cubes:
+            out[("dq", c)] = dQc[c][None, :].repeat(64, 0) / CUBE_TOKENS
+        if ids.size == 0:
+            if c in query_cubes:
+                out[("dgc", c)] = np.sum(G[rows] * oc[c], axis=1)
+                out[("dgf", c)] = np.zeros(64)
+            continue
+        keys = members[ids].ravel()
+        P, _ = _softmax_rows(scale * (qb[rows] @ kb[keys].T))
+        of = P @ vb[keys]
+        dOf = gfb[rows][:, None] * G[rows]
+        delta = np.sum(dOf * of, axis=1)
+        dS = P * (dOf @ vb[keys].T - delta[:, None])
+        if c in query_cubes:
+            out[("dq", c)] = out[("dq", c)] + scale * (dS @ kb[keys])
+            out[("dgc", c)] = np.sum(G[rows] * oc[c], axis=1)
+            out[("dgf", c)] = np.sum(G[rows] * of, axis=1)
+        for pos, j in enumerate(ids):
+            j = int(j)
+            if j in key_set:
+                sl = slice(64 * pos, 64 * pos + 64)
+                out[("dk", j)] = out[("dk", j)] + scale * (dS[:, sl].T @ qb[rows])
+                out[("dv", j)] = out[("dv", j)] + P[:, sl].T @ dOf
+    return out

@@ -1,0 +1,116 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point include/vsa.h declares, sizes its buffers, and rejects bad
+arguments with the documented status before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from trainable_block_sparse_cube_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vsa.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = (_lib.VSA_OK, _lib.VSA_ERR_INVALID_ARG,
+                                       _lib.VSA_ERR_UNSUPPORTED, _lib.VSA_ERR_WORKSPACE)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\**\s+\**([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libvsa.so not built")
+    return _lib.load()
+
+
+def test_header_declares_the_required_entry_points():
+    names = declared_functions()
+    for need in ("vsa_forward", "vsa_backward", "block_sparse_attn_varlen",
+                 "block_sparse_attn_varlen_backward", "vsa_forward_workspace_bytes",
+                 "vsa_backward_workspace_bytes", "vsa_saved_bytes", "vsa_status_string",
+                 "vsa_cube_permute_pool", "vsa_coarse_topk", "vsa_fine_forward"):
+        assert need in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, f"{name} missing from the Python binding"
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.vsa_status_string(s)
+    assert lib.vsa_status_string(99) == b"unknown status"
+
+
+def test_workspace_sizes(lib):
+    # forward: three bf16 tile copies + three fp32 means + coarse output/lse
+    B, nh, D, T, H, W = 1, 12, 128, 20, 48, 64
+    N, nc = T * H * W, T * H * W // 64
+    fw = lib.vsa_forward_workspace_bytes(B, nh, D, T, H, W, _lib.VSA_BF16)
+    assert fw >= 3 * B * nh * N * D * 2 + 4 * B * nh * nc * D * 4
+    sv = lib.vsa_saved_bytes(B, nh, D, T, H, W)
+    assert sv >= 4 * (B * nh * nc * D + B * nh * nc + B * nh * N + B * nh * N * D)
+    bw = lib.vsa_backward_workspace_bytes(B, nh, D, T, H, W, _lib.VSA_BF16, B * nh * nc * 32)
+    assert bw > fw
+    # invalid shapes size to 0
+    assert lib.vsa_forward_workspace_bytes(B, nh, D, 6, H, W, _lib.VSA_BF16) == 0
+    assert lib.vsa_forward_workspace_bytes(B, nh, 96, T, H, W, _lib.VSA_BF16) == 0
+    assert lib.vsa_backward_workspace_bytes(B, nh, D, T, H, W, _lib.VSA_BF16, -1) == 0
+
+
+FAKE = 0x1000  # a non-null pointer value; never dereferenced by failing calls
+
+
+def fwd(lib, T=8, H=8, W=8, D=64, topk=2, dtype=_lib.VSA_BF16, null_out=False, ws=FAKE, ws_bytes=1 << 40):
+    return lib.vsa_forward(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, D, T, H, W, topk, dtype,
+                           None if null_out else FAKE, FAKE, None, ws, ws_bytes, None)
+
+
+def test_forward_rejects_bad_arguments(lib):
+    assert fwd(lib, T=6) == INVALID          # grid not made of 4x4x4 cubes
+    assert fwd(lib, H=0) == INVALID
+    assert fwd(lib, topk=0) == INVALID
+    assert fwd(lib, topk=9) == INVALID       # 8 cubes
+    assert fwd(lib, D=96) == UNSUPPORTED
+    assert fwd(lib, dtype=7) == UNSUPPORTED
+    assert fwd(lib, null_out=True) == INVALID
+    assert fwd(lib, ws=None) == INVALID
+    assert fwd(lib, ws_bytes=16) == WORKSPACE
+
+
+def test_varlen_and_backward_reject_bad_arguments(lib):
+    st = lib.block_sparse_attn_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 64, 8, 8, 8,
+                                      None, FAKE, 4, _lib.VSA_BF16, FAKE, None, FAKE, 1 << 40, None)
+    assert st == INVALID  # no offsets
+    st = lib.block_sparse_attn_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 64, 8, 8, 8,
+                                      FAKE, FAKE, -1, _lib.VSA_BF16, FAKE, None, FAKE, 1 << 40, None)
+    assert st == INVALID  # negative entry count
+    st = lib.vsa_backward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 2, 64, 8, 8, 8, 2,
+                          _lib.VSA_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == INVALID  # no saved state
+    st = lib.vsa_backward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 64, 8, 8, 8, 2,
+                          _lib.VSA_F32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == UNSUPPORTED  # fp32 backward is not built
+    st = lib.vsa_backward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 64, 8, 8, 8, 2,
+                          _lib.VSA_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None)
+    assert st == WORKSPACE
+
+
+def test_stage_calls_reject_bad_arguments(lib):
+    assert lib.vsa_coarse_topk(FAKE, FAKE, FAKE, 1, 1, 64, 8, 9, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.vsa_coarse_topk(FAKE, FAKE, FAKE, 1, 1, 64, 8, 2, FAKE, FAKE, None, None) == INVALID
+    assert lib.vsa_coarse_topk(FAKE, FAKE, FAKE, 1, 1, 64, 100000, 2, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert lib.vsa_fine_forward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 8, 8, 8,
+                                None, FAKE, 2, _lib.VSA_BF16, FAKE, FAKE, None, None) == INVALID
+    assert lib.vsa_cube_permute_pool(FAKE, FAKE, FAKE, 1, 1, 64, 8, 8, 5, _lib.VSA_BF16,
+                                     FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID

@@ -326,3 +326,23 @@ def test_pages_sparsity_figure_at_16k_tokens():
     nc = T * H * W // 64
     kept = r["sel"].shape[-1] * 64 / (nc * 64)
     assert abs((1 - kept) - fig["sparsity"]) < 1e-12
+
+
+def test_backward_sampled_matches_full_backward():
+    grid = (4, 8, 12)
+    inp = make_inputs(2, 2, 8, grid, dtype="f32", seed=23, with_dout=True)
+    r = oracle.forward(inp["q"], inp["k"], inp["v"], inp["gc"], inp["gf"], grid, 3)
+    lists = oracle.lists_from_sel(r["sel"])
+    lists[1][0][2] = []  # an empty list
+    g = oracle.backward(inp["q"], inp["k"], inp["v"], inp["gc"], inp["gf"], inp["dout"], grid, lists)
+    members = vo.cube_members(*grid)
+    for b, h in [(0, 1), (1, 0)]:
+        out = oracle.backward_sampled(inp["q"], inp["k"], inp["v"], inp["gc"], inp["gf"], inp["dout"],
+                                      grid, lists[b][h], b, h, [0, 2, 5], [1, 2, 4])
+        for c in (0, 2, 5):
+            np.testing.assert_allclose(out[("dq", c)], g["dq"][b, members[c], h], rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(out[("dgc", c)], g["dgc"][b, members[c], h], rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(out[("dgf", c)], g["dgf"][b, members[c], h], rtol=1e-11, atol=1e-12)
+        for j in (1, 2, 4):
+            np.testing.assert_allclose(out[("dk", j)], g["dk"][b, members[j], h], rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(out[("dv", j)], g["dv"][b, members[j], h], rtol=1e-11, atol=1e-12)

@@ -28,6 +28,7 @@ __global__ __launch_bounds__(256) void permute_pool_kernel(PermutePoolPtrs p, in
 
   __shared__ __align__(16) T vt_lds[D * VT_PITCH];
   __shared__ float red[4][D];
+  __shared__ float mean_s[D];
 
   const int which = blockIdx.y;  // 0: q, 1: k, 2: v
   const T* __restrict__ src = (const T*)p.src[which];
@@ -82,17 +83,27 @@ __global__ __launch_bounds__(256) void permute_pool_kernel(PermutePoolPtrs p, in
     }
   }
   __syncthreads();
+  const bool center = tr && ((p.center_tr >> which) & 1);
   if (pooled) {
     for (int d = tid; d < D; d += 256) {
-      const float sum = (red[0][d] + red[1][d]) + (red[2][d] + red[3][d]);
-      pooled[((int64_t)(b * nh + h) * nc + c) * D + d] = sum * (1.0f / kCubeTokens);
+      const float mean = ((red[0][d] + red[1][d]) + (red[2][d] + red[3][d])) * (1.0f / kCubeTokens);
+      pooled[((int64_t)(b * nh + h) * nc + c) * D + d] = mean;
+      mean_s[d] = mean;
     }
   }
+  if (center) __syncthreads();
   if (tr) {
     constexpr int VCPR = kCubeTokens / EPC;  // chunks per transposed row
     for (int i = tid; i < D * VCPR; i += 256) {
       const int d = i / VCPR, cc = i % VCPR;
-      const u32x4 val = *reinterpret_cast<const u32x4*>(&vt_lds[d * VT_PITCH + cc * EPC]);
+      u32x4 val = *reinterpret_cast<const u32x4*>(&vt_lds[d * VT_PITCH + cc * EPC]);
+      if (center) {
+        T x[EPC];
+        __builtin_memcpy(x, &val, 16);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) x[e] = from_f32<T>(to_f32(x[e]) - mean_s[d]);
+        __builtin_memcpy(&val, x, 16);
+      }
       *reinterpret_cast<u32x4*>(tr + tile + (int64_t)d * kCubeTokens + cc * EPC) = val;
     }
   }

@@ -88,7 +88,7 @@ int forward_impl(const void* q, const void* k, const void* v, const void* gc, co
     oc = sv.oc; lse_c = sv.lse_c; lse_f = sv.lse_f; of = sv.of;
   }
   const bool bf = s.dtype == VSA_BF16;
-  PermutePoolArgs pa{{{q, k, v}, {w.qp, w.kp, nullptr}, {nullptr, nullptr, w.vt}, {w.qc, w.kc, w.vc}},
+  PermutePoolArgs pa{{{q, k, v}, {w.qp, w.kp, nullptr}, {nullptr, nullptr, w.vt}, {w.qc, w.kc, w.vc}, 0},
                      s.B, s.heads, s.D, s.T, s.H, s.W, bf};
   hipError_t e = launch_permute_pool(pa, st);
   if (e != hipSuccess) return VSA_ERR_HIP;
@@ -98,6 +98,66 @@ int forward_impl(const void* q, const void* k, const void* v, const void* gc, co
   FineArgs fa{w.qp, w.kp, w.vt, oc, gc, gf, s.B, s.heads, s.D, s.T, s.H, s.W,
               offs, offs ? ids : sel, topk, bf, out, lse_f, of};
   return hip_status(launch_fine_forward(fa, st));
+}
+
+struct BwdWorkspace {
+  void *qp, *kp, *vp, *qt, *kt, *dofp, *doft;
+  float *qc, *kc, *vc, *delta, *doc, *deltac, *S, *dP, *dqc, *dkc, *dvc;
+  int32_t *tr_offs, *tr_ids;
+};
+
+size_t bwd_ws_layout(const Shape& s, int64_t n_entries, char* base, BwdWorkspace* w) {
+  const size_t tile = align_up((size_t)s.B * s.heads * s.N * s.D * s.elt);
+  const size_t pooled = align_up((size_t)s.B * s.heads * s.nc * s.D * sizeof(float));
+  const size_t per_tok = align_up((size_t)s.B * s.heads * s.N * sizeof(float));
+  const size_t per_cube = align_up((size_t)s.B * s.heads * s.nc * sizeof(float));
+  const size_t sq = align_up((size_t)s.B * s.heads * s.nc * s.nc * sizeof(float));
+  size_t off = 0;
+  auto take = [&](size_t bytes) { char* p = base ? base + off : nullptr; off += bytes; return (void*)p; };
+  BwdWorkspace t;
+  t.qp = take(tile); t.kp = take(tile); t.vp = take(tile); t.qt = take(tile); t.kt = take(tile);
+  t.dofp = take(tile); t.doft = take(tile);
+  t.qc = (float*)take(pooled); t.kc = (float*)take(pooled); t.vc = (float*)take(pooled);
+  t.delta = (float*)take(per_tok);
+  t.doc = (float*)take(pooled); t.deltac = (float*)take(per_cube);
+  t.S = (float*)take(sq); t.dP = (float*)take(sq);
+  t.dqc = (float*)take(pooled); t.dkc = (float*)take(pooled); t.dvc = (float*)take(pooled);
+  t.tr_offs = (int32_t*)take(align_up(((size_t)s.B * s.heads * s.nc + 1) * sizeof(int32_t)));
+  t.tr_ids = (int32_t*)take(align_up((size_t)(n_entries > 0 ? n_entries : 1) * sizeof(int32_t)));
+  if (w) *w = t;
+  return off;
+}
+
+int backward_impl(const void* q, const void* k, const void* v, const void* gc, const void* gf,
+                  const void* dout, const int32_t* offs, const int32_t* ids, int topk,
+                  int64_t n_entries, const void* saved, const Shape& s,
+                  void* dq, void* dk, void* dv, void* dgc, void* dgf,
+                  void* ws, size_t ws_bytes, hipStream_t st) {
+  if (!q || !k || !v || !gc || !gf || !dout || !saved || !ws) return VSA_ERR_INVALID_ARG;
+  if (!dq || !dk || !dv || !dgc || !dgf) return VSA_ERR_INVALID_ARG;
+  if (s.dtype != VSA_BF16) return VSA_ERR_UNSUPPORTED;  // bf16 MFMA backward only
+  if (ws_bytes < bwd_ws_layout(s, n_entries, nullptr, nullptr)) return VSA_ERR_WORKSPACE;
+  BwdWorkspace w;
+  bwd_ws_layout(s, n_entries, (char*)ws, &w);
+  Saved sv;
+  saved_layout(s, (char*)const_cast<void*>(saved), &sv);
+  // K^T tiles are stored centred on their cube mean (see fine_bwd_dq).
+  PermutePoolArgs pa{{{q, k, v}, {w.qp, w.kp, w.vp}, {w.qt, w.kt, nullptr}, {w.qc, w.kc, w.vc}, 2},
+                     s.B, s.heads, s.D, s.T, s.H, s.W, true};
+  if (launch_permute_pool(pa, st) != hipSuccess) return VSA_ERR_HIP;
+  BackwardArgs ba;
+  ba.B = s.B; ba.heads = s.heads; ba.D = s.D; ba.T = s.T; ba.H = s.H; ba.W = s.W;
+  ba.dout = dout; ba.gc = gc; ba.gf = gf;
+  ba.qp = w.qp; ba.kp = w.kp; ba.vp = w.vp; ba.qt = w.qt; ba.kt = w.kt;
+  ba.qc = w.qc; ba.kc = w.kc; ba.vc = w.vc;
+  ba.oc = sv.oc; ba.lse_c = sv.lse_c; ba.lse_f = sv.lse_f; ba.of = sv.of;
+  ba.offs = offs; ba.ids = ids; ba.topk = topk;
+  ba.delta = w.delta; ba.dofp = w.dofp; ba.doft = w.doft;
+  ba.doc = w.doc; ba.deltac = w.deltac; ba.S = w.S; ba.dP = w.dP;
+  ba.dqc = w.dqc; ba.dkc = w.dkc; ba.dvc = w.dvc;
+  ba.tr_offs = w.tr_offs; ba.tr_ids = w.tr_ids;
+  ba.dq = dq; ba.dk = dk; ba.dv = dv; ba.dgc = dgc; ba.dgf = dgf;
+  return hip_status(launch_backward(ba, st));
 }
 
 }  // namespace
@@ -166,7 +226,7 @@ int vsa_cube_permute_pool(const void* q, const void* k, const void* v,
   int st = check_shape(B, heads, head_dim, T, H, W, dtype, &s);
   if (st != VSA_OK) return st;
   if (!q || !k || !v || !qp || !kp || !vt || !qc || !kc || !vc) return VSA_ERR_INVALID_ARG;
-  PermutePoolArgs pa{{{q, k, v}, {qp, kp, nullptr}, {nullptr, nullptr, vt}, {qc, kc, vc}},
+  PermutePoolArgs pa{{{q, k, v}, {qp, kp, nullptr}, {nullptr, nullptr, vt}, {qc, kc, vc}, 0},
                      B, heads, head_dim, T, H, W, dtype == VSA_BF16};
   return hip_status(launch_permute_pool(pa, stream));
 }
@@ -206,21 +266,42 @@ int vsa_fine_forward(const void* qp, const void* kp, const void* vt, const float
 
 size_t vsa_backward_workspace_bytes(int B, int heads, int head_dim, int T, int H, int W, int dtype,
                                     int64_t n_list_entries) {
-  (void)B; (void)heads; (void)head_dim; (void)T; (void)H; (void)W; (void)dtype; (void)n_list_entries;
-  return 0;
+  Shape s;
+  if (check_shape(B, heads, head_dim, T, H, W, dtype, &s) != VSA_OK || n_list_entries < 0) return 0;
+  return bwd_ws_layout(s, n_list_entries, nullptr, nullptr);
 }
 
-int vsa_backward(const void*, const void*, const void*, const void*, const void*, const void*,
-                 const int32_t*, const void*, int, int, int, int, int, int, int, int,
-                 void*, void*, void*, void*, void*, void*, size_t, hipStream_t) {
-  return VSA_ERR_UNSUPPORTED;
+int vsa_backward(const void* q, const void* k, const void* v, const void* gate_c, const void* gate_f,
+                 const void* dout, const int32_t* sel_idx, const void* saved,
+                 int B, int heads, int head_dim, int T, int H, int W, int topk, int dtype,
+                 void* dq, void* dk, void* dv, void* dgate_c, void* dgate_f,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Shape s;
+  int st = check_shape(B, heads, head_dim, T, H, W, dtype, &s);
+  if (st != VSA_OK) return st;
+  if (topk < 1 || topk > s.nc || !sel_idx) return VSA_ERR_INVALID_ARG;
+  if ((int64_t)B * heads * s.nc * topk > INT_MAX) return VSA_ERR_UNSUPPORTED;
+  return backward_impl(q, k, v, gate_c, gate_f, dout, nullptr, sel_idx, topk,
+                       (int64_t)B * heads * s.nc * topk, saved, s, dq, dk, dv, dgate_c, dgate_f,
+                       workspace, workspace_bytes, stream);
 }
 
-int block_sparse_attn_varlen_backward(const void*, const void*, const void*, const void*, const void*,
-                                      const void*, const int32_t*, const int32_t*, int64_t, const void*,
-                                      int, int, int, int, int, int, int,
-                                      void*, void*, void*, void*, void*, void*, size_t, hipStream_t) {
-  return VSA_ERR_UNSUPPORTED;
+int block_sparse_attn_varlen_backward(const void* q, const void* k, const void* v,
+                                      const void* gate_c, const void* gate_f, const void* dout,
+                                      const int32_t* kv_offsets, const int32_t* kv_ids,
+                                      int64_t n_list_entries, const void* saved,
+                                      int B, int heads, int head_dim, int T, int H, int W, int dtype,
+                                      void* dq, void* dk, void* dv, void* dgate_c, void* dgate_f,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Shape s;
+  int st = check_shape(B, heads, head_dim, T, H, W, dtype, &s);
+  if (st != VSA_OK) return st;
+  if (!kv_offsets) return VSA_ERR_INVALID_ARG;
+  if (n_list_entries < 0 || n_list_entries > (int64_t)B * heads * s.nc * s.nc) return VSA_ERR_INVALID_ARG;
+  if (n_list_entries > 0 && !kv_ids) return VSA_ERR_INVALID_ARG;
+  if (n_list_entries > INT_MAX) return VSA_ERR_UNSUPPORTED;
+  return backward_impl(q, k, v, gate_c, gate_f, dout, kv_offsets, kv_ids, 0, n_list_entries, saved, s,
+                       dq, dk, dv, dgate_c, dgate_f, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

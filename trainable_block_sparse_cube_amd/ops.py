@@ -99,14 +99,15 @@ def block_sparse_attn_varlen(q, k, v, gate_c, gate_f, grid, kv_offsets, kv_ids, 
 
 def vsa_backward(q, k, v, gate_c, gate_f, dout, sel, saved, grid):
     """Gradients of sum(dout * out) for a forward run with save=True.
-    Returns (dq, dk, dv, dgate_c, dgate_f)."""
+    Returns (dq, dk, dv, dgate_c, dgate_f); gate gradients are fp32."""
     lib = _lib.load()
     B, N, nh, D, T, H, W, dt = _check_inputs(q, k, v, gate_c, gate_f, grid)
     if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_contiguous():
         raise ValueError("dout must match q")
     topk = sel.shape[-1]
     grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
-             torch.empty_like(gate_c), torch.empty_like(gate_f)]
+             torch.empty(gate_c.shape, dtype=torch.float32, device=q.device),
+             torch.empty(gate_f.shape, dtype=torch.float32, device=q.device)]
     wsb = lib.vsa_backward_workspace_bytes(B, nh, D, T, H, W, dt, int(sel.numel()))
     ws = _workspace(wsb, q.device)
     st = lib.vsa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(gate_c), _ptr(gate_f), _ptr(dout),
@@ -121,7 +122,8 @@ def block_sparse_attn_varlen_backward(q, k, v, gate_c, gate_f, dout, kv_offsets,
     B, N, nh, D, T, H, W, dt = _check_inputs(q, k, v, gate_c, gate_f, grid)
     _check_lists(kv_offsets, kv_ids, B, nh, N // 64)
     grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
-             torch.empty_like(gate_c), torch.empty_like(gate_f)]
+             torch.empty(gate_c.shape, dtype=torch.float32, device=q.device),
+             torch.empty(gate_f.shape, dtype=torch.float32, device=q.device)]
     n = int(kv_ids.numel())
     wsb = lib.vsa_backward_workspace_bytes(B, nh, D, T, H, W, dt, n)
     ws = _workspace(wsb, q.device)
