@@ -9,10 +9,14 @@ and PV over the selected cubes plus the dense coarse stage).
 
 The fine kernel is also timed on its own (HIP events on the stream it is
 launched on) for the roofline entry; the fp64 CPU oracle is timed on a
-bounded sample of the same workload as the CPU baseline.
+bounded sample of the same workload as the CPU baseline.  HBM traffic of the
+fine kernel comes from the committed profiler-counter summary
+(profiles/fine_fwd_bf16_long61k_k32_pmc.txt) and is reported only while the
+kernel source still hashes to the value recorded there.
 Prints one JSON line.
 """
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -24,6 +28,26 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+FINE_SRC = os.path.join(ROOT, "trainable_block_sparse_cube_amd", "csrc", "fine_fwd.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "fine_fwd_bf16_long61k_k32_pmc.txt")
+
+
+def fine_source_hash():
+    with open(FINE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per fine-kernel launch from the committed counter summary
+    (its last line is JSON), or None if absent or taken on other source."""
+    try:
+        with open(PMC_SUMMARY) as f:
+            rec = json.loads(f.read().strip().splitlines()[-1])
+    except (OSError, ValueError, IndexError):
+        return None
+    if rec.get("fine_fwd_source_sha256_16") != fine_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def parse():
@@ -33,7 +57,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="long61k")
     p.add_argument("--topk", type=int, default=32)
-    p.add_argument("--cpu-heads", type=int, default=4,
+    p.add_argument("--cpu-heads", type=int, default=8,
                    help="heads of the workload the CPU oracle runs (bounded sample)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
@@ -112,7 +136,10 @@ def main():
     f_fine = fine_flops(w.B, w.heads, w.N, K, w.head_dim)
     f_coarse = coarse_flops(w.B, w.heads, w.n_cubes, w.head_dim)
     elt = 2
-    pp_bytes = 6 * w.B * w.N * w.heads * w.head_dim * elt + 3 * w.B * w.heads * w.n_cubes * w.head_dim * 4
+    tok_bytes = w.B * w.N * w.heads * w.head_dim * elt          # one of q, k, v
+    pooled_bytes = w.B * w.heads * w.n_cubes * w.head_dim * 4   # one fp32 mean tensor
+    pp_bytes = 3 * tok_bytes + 3 * tok_bytes + 3 * pooled_bytes  # read q,k,v; write 3 tiles + means
+    coarse_bytes = 4 * pooled_bytes + w.B * w.heads * w.n_cubes * (4 + 4 * K)
     fine_tflops = f_fine / (ms_fine * 1e-3) / 1e12
     res = {
         "metric": "VSA fwd effective TFLOP/s & % bf16 MFMA peak at 61440 tokens, K=32",
@@ -131,11 +158,13 @@ def main():
                    "tokens": w.N, "topk": K, "parallelism": "single GPU"},
         "frac_of_peak_whole_forward": (f_fine + f_coarse) / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "stages_ms": {"permute_pool": ms_pp, "coarse_topk": ms_coarse, "fine": ms_fine},
-        "permute_pool_GBs": pp_bytes / (ms_pp * 1e-3) / 1e9,
+        "stage_GBs": {"permute_pool": pp_bytes / (ms_pp * 1e-3) / 1e9,
+                      "coarse_topk": coarse_bytes / (ms_coarse * 1e-3) / 1e9},
+        "fine_TFLOPs": fine_tflops,
         "roofline": {"bound": "mfma", "kernel": "fine_fwd_bf16_kernel<128>",
                      "achieved": fine_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": fine_tflops / PEAK_BF16_TFLOPS, "traffic": None,
-                     "flops_per_launch": f_fine},
+                     "frac": fine_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
+                     "flops_per_launch": f_fine, "ms_per_launch": ms_fine},
     }
     if a.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -144,16 +173,55 @@ def main():
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = 1 << 30
     if a.extra:
-        res["extra"] = extra(a, vsa, torch, w, stream)
+        del qp, kp, vt, fout
+        res["extra"] = extra(a, vsa, torch, stream)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, w, K, min(a.cpu_heads, w.heads))
     print(json.dumps(res), flush=True)
 
 
-def extra(a, vsa, torch, w, stream):
+def extra(a, vsa, torch, stream):
+    """Other workloads, each timed the same way (HIP events, inputs resident)."""
     from workloads import WORKLOADS, coarse_flops, fine_flops, fine_flops_lists, workload_inputs
-    ext = {}
     dev = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda().contiguous()
+    ext = {}
+    steps, warm = max(3, a.steps // 2), 2
+
+    def fwd_case(name, K):
+        w = WORKLOADS[name]
+        inp = workload_inputs(w, with_varlen=False)
+        q, k, v, gc, gf = (dev(inp[n]) for n in ("q", "k", "v", "gc", "gf"))
+        ms = timed(lambda: vsa.vsa_forward(q, k, v, gc, gf, w.grid, K), steps, warm, stream)
+        fl = fine_flops(w.B, w.heads, w.N, K, w.head_dim) + coarse_flops(w.B, w.heads, w.n_cubes, w.head_dim)
+        return {"ms": ms, "TFLOPs": fl / (ms * 1e-3) / 1e12}
+
+    ext["long61k_k16_forward"] = fwd_case("long61k", 16)
+    ext["pretrain16k_k32_forward"] = fwd_case("pretrain16k", 32)
+    ext["large70k_k32_forward"] = fwd_case("large70k", 32)
+
+    w = WORKLOADS["large70k"]
+    inp = workload_inputs(w)
+    q, k, v, gc, gf = (dev(inp[n]) for n in ("q", "k", "v", "gc", "gf"))
+    offs = torch.from_numpy(inp["kv_offsets"]).cuda()
+    ids = torch.from_numpy(inp["kv_ids"]).cuda()
+    ms = timed(lambda: vsa.block_sparse_attn_varlen(q, k, v, gc, gf, w.grid, offs, ids), steps, warm, stream)
+    fl = fine_flops_lists(int(ids.numel()), w.head_dim) + coarse_flops(w.B, w.heads, w.n_cubes, w.head_dim)
+    ext["large70k_varlen_forward"] = {"ms": ms, "TFLOPs": fl / (ms * 1e-3) / 1e12,
+                                      "mean_list_len": int(ids.numel()) / (w.B * w.heads * w.n_cubes)}
+    del q, k, v, gc, gf, offs, ids, inp
+
+    w = WORKLOADS["train16k"]
+    inp = workload_inputs(w)
+    q, k, v, gc, gf, do = (dev(inp[n]) for n in ("q", "k", "v", "gc", "gf", "dout"))
+    out, sel, saved = vsa.vsa_forward(q, k, v, gc, gf, w.grid, 32, save=True)
+    ms_f = timed(lambda: vsa.vsa_forward(q, k, v, gc, gf, w.grid, 32, save=True), steps, warm, stream)
+    ms_b = timed(lambda: vsa.vsa_backward(q, k, v, gc, gf, do, sel, saved, w.grid), steps, warm, stream)
+    ff = fine_flops(w.B, w.heads, w.N, 32, w.head_dim)
+    fc = coarse_flops(w.B, w.heads, w.n_cubes, w.head_dim)
+    ext["train16k_k32"] = {"forward_ms": ms_f, "backward_ms": ms_b,
+                           "forward_TFLOPs": (ff + fc) / (ms_f * 1e-3) / 1e12,
+                           "backward_TFLOPs": (2.5 * ff + 2 * fc) / (ms_b * 1e-3) / 1e12,
+                           "backward_flop_model": "2.5 x fine forward + 2 x coarse forward"}
     return ext
 
 
