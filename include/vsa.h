@@ -148,8 +148,9 @@ int block_sparse_attn_varlen_backward(
 
 /* ------------------------------------------------------------ stage calls
  * The forward's steps one at a time, for per-stage checks and timing.
- * Internal layouts (all written by vsa_cube_permute_pool):
- *   qp, kp: [B, heads, Nc, 64, D], token slot-major inside each cube;
+ * Internal layouts (written by vsa_cube_permute_pool):
+ *   qp, kp: [B, heads, Nc, 64, D], token slot-major inside each cube
+ *           (qp is optional: pass NULL to skip it; the forward does);
  *   vt:     [B, heads, Nc, D, 64], V transposed per cube, with the 64 keys
  *           stored in MFMA order: inside every group of 16 keys, position
  *           p holds key (p & 3) + 8*((p >> 2) & 1) + 4*((p >> 3) & 1)
@@ -169,12 +170,15 @@ int vsa_coarse_topk(const float* qc, const float* kc, const float* vc,
                     float* oc, float* lse_c, int32_t* sel_idx,
                     hipStream_t stream);
 
-/* Fine stage + gated combine.  Key lists: when kv_offsets is NULL, list r
- * is kv_ids[r*topk .. r*topk + topk); otherwise the CSR lists as in
+/* Fine stage + gated combine.  q: the raster input [B,N,heads,D] (read in
+ * place); kp, vt: K and V^T tiles from vsa_cube_permute_pool; oc: coarse
+ * output.
+ * Key lists: when kv_offsets is NULL, list r is
+ * kv_ids[r*topk .. r*topk + topk); otherwise the CSR lists as in
  * block_sparse_attn_varlen (topk ignored).  lse_f [B,heads,N] and
  * o_fine [B,heads,N,D] (fp32, cube-major) are written only if non-NULL
  * (both or neither). */
-int vsa_fine_forward(const void* qp, const void* kp, const void* vt,
+int vsa_fine_forward(const void* q, const void* kp, const void* vt,
                      const float* oc, const void* gate_c, const void* gate_f,
                      int B, int heads, int head_dim, int T, int H, int W,
                      const int32_t* kv_offsets, const int32_t* kv_ids, int topk,

@@ -7,14 +7,14 @@
 // critical key cubes of each query cube.  [VSA-sum, Limitations]: this
 // selection is a separate step, not fused into the fine attention kernel.
 //
-// One workgroup (4 waves) owns 16 query cubes of one (batch, head):
+// One workgroup (8 waves) owns 16 query cubes of one (batch, head):
 //   1. logits S[r][j] = scale * <qc_r, kc_j> for every key cube j with fp32
 //      MFMA (operands straight from L2); the 16 x Nc block of logits stays
 //      in LDS;
-//   2. per row (one wave per row): top-K by (logit desc, index asc) found
-//      with a bitwise search for the K-th largest key plus a ballot-based
-//      ordered compaction, which also emits the ids ascending; then the
-//      softmax statistics, and S is overwritten by the probabilities;
+//   2. per row (one wave per row): top-K by (logit desc, index asc), ids
+//      emitted ascending (candidate pruning + direct ranks, see select_row);
+//      then the softmax statistics, and S is overwritten by the
+//      probabilities;
 //   3. Oc = P * vc with fp32 MFMA, vc operands read straight from L2.
 // Everything is fp32: the ranking must match an fp64 reference exactly
 // except at near-ties.
@@ -46,20 +46,25 @@ __device__ __forceinline__ uint32_t kth_largest_of_lanes(uint32_t x, int k) {
   return thr;
 }
 
-// Rank selection for one row held by one wave.  `keys` holds this lane's
-// order keys of entries lane + 64 j (0 past the end; real order keys are
-// never 0).  Writes the topk entries with the largest (key, -index) to
-// out[0..topk), ascending by index.  `cand` is per-wave LDS scratch of
-// 64 * MAXJ words.
+constexpr int kNW = 8;        // waves per workgroup
+constexpr int kCandCap = 256; // candidates ranked directly per row
+
+// Top-K of one row held by one wave.  `keys` holds this lane's order keys
+// of entries lane + 64 j (0 past the end; real order keys are never 0).
+// Writes the topk entries with the largest (key, -index) to out[0..topk),
+// ascending by index.  `ck`/`ci` are per-wave LDS scratch of kCandCap words.
 //
-// The K-th largest key is found by a bitwise search over a pruned candidate
-// set: for K <= 64 the K-th largest of the 64 per-lane maxima is a lower
-// bound on the row's K-th largest key (the lane maxima are row entries), so
-// only entries at or above it take part.
+// For K <= 64 the K-th largest of the 64 per-lane maxima is a lower bound
+// lo on the row's K-th largest key (the lane maxima are row entries), so
+// only entries with key >= lo can be chosen, and every entry that beats
+// such an entry is itself >= lo.  These candidates (typically a few dozen)
+// are compacted in index order and each one's rank among them, counted
+// directly, decides it: chosen iff fewer than K candidates beat it.  Larger
+// K or candidate sets use a bitwise search for the K-th largest key.
 template <int MAXJ>
 __device__ __forceinline__ void select_row(const uint32_t (&keys)[MAXJ], int nc, int topk,
-                                           int lane, uint32_t* __restrict__ cand,
-                                           int32_t* __restrict__ out) {
+                                           int lane, uint32_t* __restrict__ ck,
+                                           int32_t* __restrict__ ci, int32_t* __restrict__ out) {
   const uint64_t lt_mask = (1ull << lane) - 1ull;
   uint32_t lo = 0;
   if (topk <= 64) {
@@ -68,31 +73,47 @@ __device__ __forceinline__ void select_row(const uint32_t (&keys)[MAXJ], int nc,
     for (int j = 0; j < MAXJ; ++j) lane_max = max(lane_max, keys[j]);
     lo = kth_largest_of_lanes(lane_max, topk);
   }
-  // Compact the candidates (key >= lo) into LDS.
   int ncand = 0;
 #pragma unroll
   for (int j = 0; j < MAXJ; ++j) {
     if (64 * j < nc) {
       const bool in = keys[j] >= lo && keys[j] != 0u;
       const uint64_t m = __ballot(in);
-      if (in) cand[ncand + __popcll(m & lt_mask)] = keys[j];
+      const int pos = ncand + __popcll(m & lt_mask);
+      if (in && pos < kCandCap) { ck[pos] = keys[j]; ci[pos] = 64 * j + lane; }
       ncand += __popcll(m);
     }
   }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  // K-th largest key among the candidates.  The greedy search starts from
-  // 0: for probes c <= lo every candidate counts (>= K of them, as in the
-  // full row), for c > lo the candidates are all entries >= c, so every
-  // decision matches a search over the whole row.
+  if (ncand <= kCandCap) {
+    __builtin_amdgcn_wave_barrier();
+    int base = 0;
+    for (int i0 = 0; i0 < ncand; i0 += 64) {
+      const int i = i0 + lane;
+      bool take = false;
+      if (i < ncand) {
+        const uint32_t ki = ck[i];
+        int beaten = 0;
+        for (int c = 0; c < ncand; ++c) {
+          const uint32_t kc = ck[c];
+          beaten += (kc > ki) | ((kc == ki) & (c < i));
+        }
+        take = beaten < topk;
+      }
+      const uint64_t tm = __ballot(take);
+      const int pos = base + __popcll(tm & lt_mask);
+      if (take && pos < topk) out[pos] = ci[i];
+      base += __popcll(tm);
+    }
+    return;
+  }
+  // Fallback: K-th largest key by a greedy bitwise search over the row.
   uint32_t thr = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t c = thr | (1u << bit);
     int cnt = 0;
-    for (int i0 = 0; i0 < ncand; i0 += 64) {
-      const int i = i0 + lane;
-      cnt += __popcll(__ballot(i < ncand && cand[i] >= c));
-    }
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j)
+      if (64 * j < nc) cnt += __popcll(__ballot(keys[j] >= c));
     if (cnt >= topk) thr = c;
   }
   int n_gt = 0;
@@ -119,21 +140,22 @@ __device__ __forceinline__ void select_row(const uint32_t (&keys)[MAXJ], int nc,
   }
 }
 
-// One workgroup: R = 16 query rows of one (batch, head), 4 waves.
+// One workgroup: R = 16 query rows of one (batch, head), 8 waves.
 // Matrix products use v_mfma_f32_16x16x4f32 (fp32 in, fp32 accumulate).
 // Lane l of a 16x16x4 step supplies row/column l % 16 and k-slice l / 16.
 template <int D, int MAXJ>
-__global__ __launch_bounds__(256, 2) void coarse_topk_kernel(
+__global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
     const float* __restrict__ qc, const float* __restrict__ kc,
     const float* __restrict__ vc, int nc, int topk, float scale,
     float* __restrict__ oc, float* __restrict__ lse, int32_t* __restrict__ sel) {
   constexpr int R = 16;
   constexpr int DQ = D / 4;          // head_dim slice per lane group
-  constexpr int NB = D / 64;         // 16-column output blocks per wave
+  constexpr int NCW = D / 16;        // waves that own a 16-column output block
   extern __shared__ float lds[];
   const int s_pitch = (nc + 35) & ~3;  // room for a zero-padded last key block
   float* S = lds;                      // [R][s_pitch]
-  uint32_t* cand_all = reinterpret_cast<uint32_t*>(S + R * s_pitch);  // [4][64 * MAXJ]
+  uint32_t* cand_k = reinterpret_cast<uint32_t*>(S + R * s_pitch);  // [kNW][kCandCap]
+  int32_t* cand_i = reinterpret_cast<int32_t*>(cand_k + kNW * kCandCap);
 
   const int bh = blockIdx.y;
   const int row0 = blockIdx.x * R;
@@ -145,8 +167,9 @@ __global__ __launch_bounds__(256, 2) void coarse_topk_kernel(
   const float* vcb = vc + (int64_t)bh * nc * D;
 
   // ---- 1. logits.  Contraction over head_dim: lane group lg covers
-  // d in [lg*DQ, lg*DQ + DQ), one element per k-step.  The next 16-key
-  // block's operands are fetched while the current one is multiplied.
+  // d in [lg*DQ, lg*DQ + DQ), one element per k-step.  Wave w takes key
+  // blocks 16w, 16w + 16 kNW, ...; the next block's operands are fetched
+  // while the current one is multiplied.
   f32x4v qa[DQ / 4];
   {
     const int row = min(row0 + li, nc - 1);  // rows past the end are never stored
@@ -161,10 +184,10 @@ __global__ __launch_bounds__(256, 2) void coarse_topk_kernel(
   };
   f32x4v kb[DQ / 4], kn[DQ / 4];
   if (16 * wave < nc) load_k(16 * wave, kn);
-  for (int j0 = 16 * wave; j0 < nc; j0 += 64) {
+  for (int j0 = 16 * wave; j0 < nc; j0 += 16 * kNW) {
 #pragma unroll
     for (int i = 0; i < DQ / 4; ++i) kb[i] = kn[i];
-    if (j0 + 64 < nc) load_k(j0 + 64, kn);
+    if (j0 + 16 * kNW < nc) load_k(j0 + 16 * kNW, kn);
     f32x4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < DQ / 4; ++i)
@@ -180,7 +203,7 @@ __global__ __launch_bounds__(256, 2) void coarse_topk_kernel(
   __syncthreads();
 
   // ---- 2. per-row top-K and softmax, one wave per row
-  for (int rr = wave; rr < R; rr += 4) {
+  for (int rr = wave; rr < R; rr += kNW) {
     const int row = row0 + rr;
     float* Srow = S + rr * s_pitch;
     if (row >= nc) {  // keep padded rows finite for phase 3
@@ -194,7 +217,7 @@ __global__ __launch_bounds__(256, 2) void coarse_topk_kernel(
         const int idx = 64 * j + lane;
         keys[j] = idx < nc ? order_key(Srow[idx]) : 0u;
       }
-      select_row<MAXJ>(keys, nc, topk, lane, cand_all + wave * 64 * MAXJ,
+      select_row<MAXJ>(keys, nc, topk, lane, cand_k + wave * kCandCap, cand_i + wave * kCandCap,
                        sel + ((int64_t)bh * nc + row) * topk);
     }
     float m = -INFINITY;
@@ -212,55 +235,48 @@ __global__ __launch_bounds__(256, 2) void coarse_topk_kernel(
   }
   __syncthreads();
 
-  // ---- 3. Oc = P * vc.  Wave w owns output columns [D/4 * w, +D/4) in
-  // NB blocks of 16; contraction over keys, lane group lg taking key
-  // j0 + 4t + lg at k-step t.  B operands come straight from L2 (vc of one
-  // head is small), the next 32-key block prefetched during the current.
-  f32x4v oacc[NB];
+  // ---- 3. Oc = P * vc.  Wave w < D/16 owns output columns [16w, 16w + 16);
+  // contraction over keys, lane group lg taking key j0 + 4t + lg at k-step
+  // t.  B operands come straight from L2 (vc of one head is small), the
+  // next 32-key block prefetched during the current.
+  if (wave < NCW) {
+    f32x4v oacc = {0.f, 0.f, 0.f, 0.f};
+    const int col = 16 * wave + li;
+    auto load_v = [&](int j0, float (&vbuf)[8]) {
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x4v{0.f, 0.f, 0.f, 0.f};
-  const int col0 = (D / 4) * wave + li;
-  auto load_v = [&](int j0, float (&vbuf)[8][NB]) {
+      for (int t = 0; t < 8; ++t) {
+        const int key = min(j0 + 4 * t + lg, nc - 1);  // P is 0 past the end
+        vbuf[t] = vcb[(int64_t)key * D + col];
+      }
+    };
+    float vb[8], vn[8];
+    load_v(0, vn);
+    for (int j0 = 0; j0 < nc; j0 += 32) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int key = min(j0 + 4 * t + lg, nc - 1);  // P is 0 past the end
+      for (int t = 0; t < 8; ++t) vb[t] = vn[t];
+      if (j0 + 32 < nc) load_v(j0 + 32, vn);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) vbuf[t][nb] = vcb[(int64_t)key * D + col0 + 16 * nb];
+      for (int t = 0; t < 8; ++t) {
+        const float pa = S[li * s_pitch + j0 + 4 * t + lg];
+        oacc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vb[t], oacc, 0, 0, 0);
+      }
     }
-  };
-  float vb[8][NB], vn[8][NB];
-  load_v(0, vn);
-  for (int j0 = 0; j0 < nc; j0 += 32) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) vb[t][nb] = vn[t][nb];
-    if (j0 + 32 < nc) load_v(j0 + 32, vn);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const float pa = S[li * s_pitch + j0 + 4 * t + lg];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vb[t][nb], oacc[nb], 0, 0, 0);
-    }
-  }
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = row0 + 4 * lg + r;
-      if (row < nc) oc[((int64_t)bh * nc + row) * D + col0 + 16 * nb] = oacc[nb][r];
+      if (row < nc) oc[((int64_t)bh * nc + row) * D + col] = oacc[r];
     }
+  }
 }
 
-size_t coarse_lds_bytes(int nc, int maxj) {
+size_t coarse_lds_bytes(int nc) {
   const int s_pitch = (nc + 35) & ~3;
-  return sizeof(float) * ((size_t)16 * s_pitch + (size_t)4 * 64 * maxj);
+  return sizeof(float) * ((size_t)16 * s_pitch + (size_t)2 * kNW * kCandCap);
 }
 
 template <int D, int MAXJ>
 hipError_t launch_coarse_dj(const CoarseArgs& a, hipStream_t st) {
-  const size_t lds = coarse_lds_bytes(a.nc, MAXJ);
+  const size_t lds = coarse_lds_bytes(a.nc);
   auto kern = coarse_topk_kernel<D, MAXJ>;
   // Raise the dynamic LDS limit once per kernel instance (host-side call).
   static size_t lds_limit = 0;
@@ -270,7 +286,7 @@ hipError_t launch_coarse_dj(const CoarseArgs& a, hipStream_t st) {
     lds_limit = lds;
   }
   dim3 grid((unsigned)((a.nc + 15) / 16), (unsigned)(a.B * a.heads));
-  kern<<<grid, 256, lds, st>>>(a.qc, a.kc, a.vc, a.nc, a.topk, 1.0f / sqrtf((float)D),
+  kern<<<grid, 64 * kNW, lds, st>>>(a.qc, a.kc, a.vc, a.nc, a.topk, 1.0f / sqrtf((float)D),
                                 a.oc, a.lse, a.sel);
   return hipGetLastError();
 }
@@ -287,7 +303,7 @@ int coarse_max_cubes(int D) {
   (void)D;
   // 16 rows of logits plus candidate scratch in LDS, and at most 40 key
   // chunks of 64 per row.
-  const int by_lds = (int)((kLdsBudget / sizeof(float) - 4 * 64 * 40) / 16) - 35;
+  const int by_lds = (int)((kLdsBudget / sizeof(float) - 2 * kNW * kCandCap) / 16) - 35;
   return by_lds < 40 * 64 ? by_lds : 40 * 64;
 }
 

@@ -65,7 +65,7 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, void* lds_wave_base
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
-    const bf16* __restrict__ qp, const bf16* __restrict__ kp, const bf16* __restrict__ vt,
+    const bf16* __restrict__ q, const bf16* __restrict__ kp, const bf16* __restrict__ vt,
     const float* __restrict__ oc, const bf16* __restrict__ gc, const bf16* __restrict__ gf,
     int nh, int nc, int Hg, int Wg,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk,
@@ -103,9 +103,13 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
   else { start = blk * topk; n = topk; }
   const int32_t* list = ids + start;
   const int64_t bh_tiles = (int64_t)bh * nc;
+  const int b = bh / nh, h = bh - b * nh;
 
   // Copy K tile and V^T tile of key cube kc into buffer `buf`, XOR-swizzled:
   // the lane landing on LDS chunk P = (row, phys) fetches chunk phys ^ swz.
+  // Both come from contiguous cube-major tiles (each is re-read by about K
+  // query cubes, and one contiguous 16 KB block streams better than 64
+  // scattered token rows).
   auto copy_tile = [&](int kc, int buf) {
     const bf16* ksrc = kp + (bh_tiles + kc) * 64 * D;
     const bf16* vsrc = vt + (bh_tiles + kc) * 64 * D;
@@ -121,11 +125,12 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     }
   };
 
-  // Q^T operands: lane (query ql of this half, half-wave hf) holds
-  // d = (D/2)*hf + 8s .. +8.
+  // Q^T operands, read once in place from the raster q: lane (query ql of
+  // this half, half-wave hf) holds d = (D/2)*hf + 8s .. +8.
   bf16x8 qB[KS];
   {
-    const bf16* qrow = qp + ((bh_tiles + c) * 64 + 32 * qh + ql) * D + (D / 2) * hf;
+    const int qtok = raster_token(c, 32 * qh + ql, Hg, Wg);
+    const bf16* qrow = q + (((int64_t)b * N + qtok) * nh + h) * D + (D / 2) * hf;
 #pragma unroll
     for (int s = 0; s < KS; ++s) qB[s] = *reinterpret_cast<const bf16x8*>(qrow + 8 * s);
   }
@@ -229,7 +234,6 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
 
   // Epilogue: normalise, gate-combine with the coarse output, scatter.
   const int slot = 32 * qh + ql;
-  const int b = bh / nh, h = bh - b * nh;
   const int tok = raster_token(c, slot, Hg, Wg);
   const int64_t gidx = ((int64_t)b * N + tok) * nh + h;
   const float g_c = (float)gc[gidx], g_f = (float)gf[gidx];
@@ -260,7 +264,7 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
 
 template <int D>
 __global__ __launch_bounds__(64) void fine_fwd_f32_kernel(
-    const float* __restrict__ qp, const float* __restrict__ kp, const float* __restrict__ vt,
+    const float* __restrict__ q, const float* __restrict__ kp, const float* __restrict__ vt,
     const float* __restrict__ oc, const float* __restrict__ gc, const float* __restrict__ gf,
     int nh, int nc, int Hg, int Wg,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk, float scale,
@@ -277,7 +281,9 @@ __global__ __launch_bounds__(64) void fine_fwd_f32_kernel(
   else { start = blk * topk; n = topk; }
 
   float qv[D], acc[D];
-  const float* qrow = qp + (((int64_t)bh * nc + c) * 64 + slot) * D;
+  const int b = bh / nh, h = bh - b * nh;
+  const int64_t tok_stride = (int64_t)nh * D;
+  const float* qrow = q + ((int64_t)b * N + raster_token(c, slot, Hg, Wg)) * tok_stride + (int64_t)h * D;
 #pragma unroll
   for (int d = 0; d < D; ++d) { qv[d] = qrow[d]; acc[d] = 0.f; }
   float m_run = -INFINITY, l_run = 0.f;
@@ -311,7 +317,6 @@ __global__ __launch_bounds__(64) void fine_fwd_f32_kernel(
     }
   }
   const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-  const int b = bh / nh, h = bh - b * nh;
   const int tok = raster_token(c, slot, Hg, Wg);
   const int64_t gidx = ((int64_t)b * N + tok) * nh + h;
   const float g_c = gc[gidx], g_f = gf[gidx];
@@ -332,12 +337,12 @@ hipError_t launch_fine_d(const FineArgs& a, hipStream_t st) {
   const float scale = 1.0f / sqrtf((float)D);
   if (a.bf16) {
     fine_fwd_bf16_kernel<D><<<grid, 256, 0, st>>>(
-        (const bf16*)a.qp, (const bf16*)a.kp, (const bf16*)a.vt, a.oc,
+        (const bf16*)a.q, (const bf16*)a.kp, (const bf16*)a.vt, a.oc,
         (const bf16*)a.gc, (const bf16*)a.gf, a.heads, nc, a.H, a.W, a.offs, a.ids, a.topk,
         scale * kLog2e, (bf16*)a.out, a.lse_f, a.o_fine);
   } else {
     fine_fwd_f32_kernel<D><<<grid, 64, 0, st>>>(
-        (const float*)a.qp, (const float*)a.kp, (const float*)a.vt, a.oc,
+        (const float*)a.q, (const float*)a.kp, (const float*)a.vt, a.oc,
         (const float*)a.gc, (const float*)a.gf, a.heads, nc, a.H, a.W, a.offs, a.ids, a.topk,
         scale, (float*)a.out, a.lse_f, a.o_fine);
   }

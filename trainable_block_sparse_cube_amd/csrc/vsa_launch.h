@@ -37,7 +37,9 @@ int coarse_max_cubes(int D);
 hipError_t launch_coarse_topk(const CoarseArgs& a, hipStream_t st);
 
 struct FineArgs {
-  const void *qp, *kp, *vt;
+  const void* q;        // raster [B, N, heads, D]
+  const void* kp;       // natural K tiles
+  const void* vt;       // transposed V tiles
   const float* oc;
   const void *gc, *gf;  // [B, N, heads]
   int B, heads, D, T, H, W;

@@ -136,14 +136,15 @@ def block_sparse_attn_varlen_backward(q, k, v, gate_c, gate_f, dout, kv_offsets,
 
 
 # ------------------------------------------------------------ stage calls
-def vsa_cube_permute_pool(q, k, v, grid):
-    """Returns (qp, kp, vt, qc, kc, vc) in the library's cube-major layouts."""
+def vsa_cube_permute_pool(q, k, v, grid, with_q_tiles=True):
+    """Returns (qp, kp, vt, qc, kc, vc) in the library's cube-major layouts
+    (qp is None when with_q_tiles is False, as in the forward)."""
     lib = _lib.load()
     B, N, nh, D = q.shape
     dt = _DT[q.dtype]
     nc = N // 64
-    qp = torch.empty((B, nh, nc, 64, D), dtype=q.dtype, device=q.device)
-    kp = torch.empty_like(qp)
+    qp = torch.empty((B, nh, nc, 64, D), dtype=q.dtype, device=q.device) if with_q_tiles else None
+    kp = torch.empty((B, nh, nc, 64, D), dtype=q.dtype, device=q.device)
     vt = torch.empty((B, nh, nc, D, 64), dtype=q.dtype, device=q.device)
     pooled = [torch.empty((B, nh, nc, D), dtype=torch.float32, device=q.device) for _ in range(3)]
     st = lib.vsa_cube_permute_pool(_ptr(q), _ptr(k), _ptr(v), B, nh, D, *grid, dt,
@@ -165,20 +166,20 @@ def vsa_coarse_topk(qc, kc, vc, topk):
     return oc, lse, sel
 
 
-def vsa_fine_forward(qp, kp, vt, oc, gate_c, gate_f, grid, kv_ids, topk=0, kv_offsets=None,
+def vsa_fine_forward(q, kp, vt, oc, gate_c, gate_f, grid, kv_ids, topk=0, kv_offsets=None,
                      out=None, save=False):
-    """Fine stage + gated combine.  Returns (out, lse_f or None, o_fine or None)."""
+    """Fine stage + gated combine on raster q and K / V^T tiles.
+    Returns (out, lse_f or None, o_fine or None)."""
     lib = _lib.load()
-    B, nh, nc, _, D = qp.shape
-    N = nc * 64
+    B, N, nh, D = q.shape
     if out is None:
-        out = torch.empty((B, N, nh, D), dtype=qp.dtype, device=qp.device)
+        out = torch.empty_like(q)
     lse = of = None
     if save:
-        lse = torch.empty((B, nh, N), dtype=torch.float32, device=qp.device)
-        of = torch.empty((B, nh, N, D), dtype=torch.float32, device=qp.device)
-    st = lib.vsa_fine_forward(_ptr(qp), _ptr(kp), _ptr(vt), _ptr(oc), _ptr(gate_c), _ptr(gate_f),
+        lse = torch.empty((B, nh, N), dtype=torch.float32, device=q.device)
+        of = torch.empty((B, nh, N, D), dtype=torch.float32, device=q.device)
+    st = lib.vsa_fine_forward(_ptr(q), _ptr(kp), _ptr(vt), _ptr(oc), _ptr(gate_c), _ptr(gate_f),
                               B, nh, D, *grid, _ptr(kv_offsets), _ptr(kv_ids), topk,
-                              _DT[qp.dtype], _ptr(out), _ptr(lse), _ptr(of), _stream())
+                              _DT[q.dtype], _ptr(out), _ptr(lse), _ptr(of), _stream())
     _lib.check("vsa_fine_forward", st)
     return out, lse, of
