@@ -125,13 +125,13 @@ def main():
     ms_step = timed(step, a.steps, a.warmup, stream)
 
     # stages on their own, same stream
-    _, kp, vt, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, w.grid, with_q_tiles=False)
+    _, kp, vp, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, w.grid, with_q_tiles=False)
     oc, lse, sel2 = vsa.vsa_coarse_topk(qc, kc, vc, K)
     ms_pp = timed(lambda: vsa.vsa_cube_permute_pool(q, k, v, w.grid, with_q_tiles=False),
                   a.steps, a.warmup, stream)
     ms_coarse = timed(lambda: vsa.vsa_coarse_topk(qc, kc, vc, K), a.steps, a.warmup, stream)
     fout = torch.empty_like(q)
-    ms_fine = timed(lambda: vsa.vsa_fine_forward(q, kp, vt, oc, gc, gf, w.grid, sel2, topk=K, out=fout),
+    ms_fine = timed(lambda: vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, w.grid, sel2, topk=K, out=fout),
                     a.steps, a.warmup, stream)
 
     f_fine = fine_flops(w.B, w.heads, w.N, K, w.head_dim)
@@ -174,7 +174,7 @@ def main():
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = 1 << 30
     if a.extra:
-        del kp, vt, fout
+        del kp, vp, fout
         res["extra"] = extra(a, vsa, torch, stream)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, w, K, min(a.cpu_heads, w.heads))

@@ -149,18 +149,15 @@ int block_sparse_attn_varlen_backward(
 /* ------------------------------------------------------------ stage calls
  * The forward's steps one at a time, for per-stage checks and timing.
  * Internal layouts (written by vsa_cube_permute_pool):
- *   qp, kp: [B, heads, Nc, 64, D], token slot-major inside each cube
- *           (qp is optional: pass NULL to skip it; the forward does);
- *   vt:     [B, heads, Nc, D, 64], V transposed per cube, with the 64 keys
- *           stored in MFMA order: inside every group of 16 keys, position
- *           p holds key (p & 3) + 8*((p >> 2) & 1) + 4*((p >> 3) & 1)
- *           of that group;
+ *   qp, kp, vp: [B, heads, Nc, 64, D], token slot-major inside each cube
+ *           (qp is optional: pass NULL to skip it; the forward does, since
+ *           the fine stage reads Q in place);
  *   qc, kc, vc: fp32 [B, heads, Nc, D] cube means.
- * Element type of qp/kp/vt is `dtype`.
+ * Element type of qp/kp/vp is `dtype`.
  */
 int vsa_cube_permute_pool(const void* q, const void* k, const void* v,
                           int B, int heads, int head_dim, int T, int H, int W,
-                          int dtype, void* qp, void* kp, void* vt,
+                          int dtype, void* qp, void* kp, void* vp,
                           float* qc, float* kc, float* vc, hipStream_t stream);
 
 /* Coarse stage: Oc [B,heads,Nc,D] fp32, lse_c [B,heads,Nc] fp32 and, when
@@ -171,14 +168,14 @@ int vsa_coarse_topk(const float* qc, const float* kc, const float* vc,
                     hipStream_t stream);
 
 /* Fine stage + gated combine.  q: the raster input [B,N,heads,D] (read in
- * place); kp, vt: K and V^T tiles from vsa_cube_permute_pool; oc: coarse
+ * place); kp, vp: K and V tiles from vsa_cube_permute_pool; oc: coarse
  * output.
  * Key lists: when kv_offsets is NULL, list r is
  * kv_ids[r*topk .. r*topk + topk); otherwise the CSR lists as in
  * block_sparse_attn_varlen (topk ignored).  lse_f [B,heads,N] and
  * o_fine [B,heads,N,D] (fp32, cube-major) are written only if non-NULL
  * (both or neither). */
-int vsa_fine_forward(const void* q, const void* kp, const void* vt,
+int vsa_fine_forward(const void* q, const void* kp, const void* vp,
                      const float* oc, const void* gate_c, const void* gate_f,
                      int B, int heads, int head_dim, int T, int H, int W,
                      const int32_t* kv_offsets, const int32_t* kv_ids, int topk,

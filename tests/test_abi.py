@@ -53,7 +53,7 @@ def test_status_strings(lib):
 
 
 def test_workspace_sizes(lib):
-    # forward: K and V^T bf16 tile copies + three fp32 means + coarse output/lse
+    # forward: K and V bf16 tile copies + three fp32 means + coarse output/lse
     B, nh, D, T, H, W = 1, 12, 128, 20, 48, 64
     N, nc = T * H * W, T * H * W // 64
     fw = lib.vsa_forward_workspace_bytes(B, nh, D, T, H, W, _lib.VSA_BF16)

@@ -47,7 +47,28 @@ __device__ __forceinline__ int swz_k(int row) {
   if constexpr (D == 128) return row & 15;
   else return (row ^ (row >> 3)) & 7;
 }
-__device__ __forceinline__ int swz_v(int row) { return (row ^ (row >> 3)) & 7; }
+// V tiles stay in natural [key][D] order and are read transposed with
+// ds_read_b64_tr_b16.  One read instruction touches, per 16 lanes, 4 key
+// rows x 2 chunks and, per 32 lanes, 4 rows x 4 chunks; the swizzle gives
+// the 4 rows distinct values in chunk bits 1-2 and in bits 2-3, so both
+// groupings fall on distinct banks.
+template <int D>
+__device__ __forceinline__ int swz_vn(int row) {
+  const int r = row & 3;
+  if constexpr (D == 128) return (r << 2) ^ (((r ^ (r >> 1)) & 1) << 1);
+  else return 2 * r;
+}
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives
+// element i % 4 of the 8-byte loads of lanes 4e + i / 4, e = 0..3.  With
+// lane 4e + q pointing at row r0 + e, columns c0 + 4q .. +4 of a row-major
+// 16-bit tile, lane i gets column c0 + i of rows r0 .. r0 + 3.
+__device__ __forceinline__ bf16x4 read_tr16(const void* lds_byte_addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4*)((__attribute__((address_space(3))) char*)lds_byte_addr));
+}
 
 // vmcnt-only wait (expcnt and lgkmcnt left at their maxima), gfx9 encoding.
 template <int N>
@@ -65,7 +86,7 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, void* lds_wave_base
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ kp, const bf16* __restrict__ vt,
+    const bf16* __restrict__ q, const bf16* __restrict__ kp, const bf16* __restrict__ vp,
     const float* __restrict__ oc, const bf16* __restrict__ gc, const bf16* __restrict__ gf,
     int nh, int nc, int Hg, int Wg,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk,
@@ -112,7 +133,7 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
   // scattered token rows).
   auto copy_tile = [&](int kc, int buf) {
     const bf16* ksrc = kp + (bh_tiles + kc) * 64 * D;
-    const bf16* vsrc = vt + (bh_tiles + kc) * 64 * D;
+    const bf16* vsrc = vp + (bh_tiles + kc) * 64 * D;
     u32x4* kdst = buf ? k_lds1 : k_lds0;
     u32x4* vdst = buf ? v_lds1 : v_lds0;
 #pragma unroll
@@ -120,8 +141,7 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
       const int P = (4 * j + wave) * 64 + lane;
       const int krow = P / KCH, kphys = P % KCH;
       copy16_to_lds(ksrc + (krow * KCH + (kphys ^ swz_k<D>(krow))) * 8, kdst + (4 * j + wave) * 64);
-      const int vrow = P >> 3, vphys = P & 7;
-      copy16_to_lds(vsrc + (vrow * 8 + (vphys ^ swz_v(vrow))) * 8, vdst + (4 * j + wave) * 64);
+      copy16_to_lds(vsrc + (krow * KCH + (kphys ^ swz_vn<D>(krow))) * 8, vdst + (4 * j + wave) * 64);
     }
   };
 
@@ -158,13 +178,20 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       ka[s] = *reinterpret_cast<const bf16x8*>(&kb[krow * KCH + ((KS * hf + s) ^ swz_k<D>(krow))]);
+    // V^T operands from the natural V tile: lane (d, hf) needs keys
+    // 32kh + 16g + 4hf + {0..3} and the same + 8 (the order of pB).
     bf16x8 va[MD][2];
 #pragma unroll
     for (int m = 0; m < MD; ++m)
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const int row = 32 * m + ql;
-        va[m][g] = *reinterpret_cast<const bf16x8*>(&vb[row * 8 + ((4 * kh + 2 * g + hf) ^ swz_v(row))]);
+        const int d = 32 * m + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        const int r0 = 32 * kh + 16 * g + 4 * hf + ((lane & 15) >> 2);
+        const char* vbase = reinterpret_cast<const char*>(vb);
+        const int a0 = r0 * (KCH * 16) + (((d >> 3) ^ swz_vn<D>(r0)) << 4) + (d & 7) * 2;
+        const int a1 = (r0 + 8) * (KCH * 16) + (((d >> 3) ^ swz_vn<D>(r0 + 8)) << 4) + (d & 7) * 2;
+        const bf16x4 lo = read_tr16(vbase + a0), hi = read_tr16(vbase + a1);
+        va[m][g] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
     __builtin_amdgcn_sched_barrier(0);  // keep the reads batched ahead of their MFMAs
 
@@ -264,7 +291,7 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
 
 template <int D>
 __global__ __launch_bounds__(64) void fine_fwd_f32_kernel(
-    const float* __restrict__ q, const float* __restrict__ kp, const float* __restrict__ vt,
+    const float* __restrict__ q, const float* __restrict__ kp, const float* __restrict__ vp,
     const float* __restrict__ oc, const float* __restrict__ gc, const float* __restrict__ gf,
     int nh, int nc, int Hg, int Wg,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk, float scale,
@@ -290,7 +317,7 @@ __global__ __launch_bounds__(64) void fine_fwd_f32_kernel(
   for (int it = 0; it < n; ++it) {
     const int kc = ids[start + it];
     const float* ks = kp + ((int64_t)bh * nc + kc) * 64 * D;
-    const float* vs = vt + ((int64_t)bh * nc + kc) * 64 * D;
+    const float* vs = vp + ((int64_t)bh * nc + kc) * 64 * D;
     __syncthreads();
     for (int i = slot; i < 64 * D; i += 64) { k_lds[i] = ks[i]; v_lds[i] = vs[i]; }
     __syncthreads();
@@ -309,11 +336,11 @@ __global__ __launch_bounds__(64) void fine_fwd_f32_kernel(
     l_run *= alpha;
 #pragma unroll
     for (int d = 0; d < D; ++d) acc[d] *= alpha;
-    for (int p = 0; p < 64; ++p) {  // storage position p holds key vt_key_of_pos(p)
-      const float w = expf(sj[vt_key_of_pos(p)] - m_new);
+    for (int j = 0; j < 64; ++j) {
+      const float w = expf(sj[j] - m_new);
       l_run += w;
 #pragma unroll
-      for (int d = 0; d < D; ++d) acc[d] = fmaf(w, v_lds[d * 64 + p], acc[d]);
+      for (int d = 0; d < D; ++d) acc[d] = fmaf(w, v_lds[j * D + d], acc[d]);
     }
   }
   const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
@@ -337,12 +364,12 @@ hipError_t launch_fine_d(const FineArgs& a, hipStream_t st) {
   const float scale = 1.0f / sqrtf((float)D);
   if (a.bf16) {
     fine_fwd_bf16_kernel<D><<<grid, 256, 0, st>>>(
-        (const bf16*)a.q, (const bf16*)a.kp, (const bf16*)a.vt, a.oc,
+        (const bf16*)a.q, (const bf16*)a.kp, (const bf16*)a.vp, a.oc,
         (const bf16*)a.gc, (const bf16*)a.gf, a.heads, nc, a.H, a.W, a.offs, a.ids, a.topk,
         scale * kLog2e, (bf16*)a.out, a.lse_f, a.o_fine);
   } else {
     fine_fwd_f32_kernel<D><<<grid, 64, 0, st>>>(
-        (const float*)a.q, (const float*)a.kp, (const float*)a.vt, a.oc,
+        (const float*)a.q, (const float*)a.kp, (const float*)a.vp, a.oc,
         (const float*)a.gc, (const float*)a.gf, a.heads, nc, a.H, a.W, a.offs, a.ids, a.topk,
         scale, (float*)a.out, a.lse_f, a.o_fine);
   }

@@ -37,7 +37,7 @@ int check_shape(int B, int heads, int D, int T, int H, int W, int dtype, Shape* 
 }
 
 struct FwdWorkspace {
-  void *kp, *vt;
+  void *kp, *vp;
   float *qc, *kc, *vc, *oc, *lse_c;
 };
 
@@ -48,7 +48,7 @@ size_t fwd_ws_layout(const Shape& s, char* base, FwdWorkspace* w) {
   size_t off = 0;
   auto take = [&](size_t bytes) { char* p = base ? base + off : nullptr; off += bytes; return (void*)p; };
   FwdWorkspace t;
-  t.kp = take(tile_bytes); t.vt = take(tile_bytes);
+  t.kp = take(tile_bytes); t.vp = take(tile_bytes);
   t.qc = (float*)take(pooled); t.kc = (float*)take(pooled); t.vc = (float*)take(pooled);
   t.oc = (float*)take(pooled); t.lse_c = (float*)take(lse);
   if (w) *w = t;
@@ -88,15 +88,15 @@ int forward_impl(const void* q, const void* k, const void* v, const void* gc, co
     oc = sv.oc; lse_c = sv.lse_c; lse_f = sv.lse_f; of = sv.of;
   }
   const bool bf = s.dtype == VSA_BF16;
-  // The fine stage reads Q in place; K and V^T are copied into cube tiles.
-  PermutePoolArgs pa{{{q, k, v}, {nullptr, w.kp, nullptr}, {nullptr, nullptr, w.vt}, {w.qc, w.kc, w.vc}, 0},
+  // The fine stage reads Q in place; K and V are copied into cube tiles.
+  PermutePoolArgs pa{{{q, k, v}, {nullptr, w.kp, w.vp}, {nullptr, nullptr, nullptr}, {w.qc, w.kc, w.vc}, 0},
                      s.B, s.heads, s.D, s.T, s.H, s.W, bf};
   hipError_t e = launch_permute_pool(pa, st);
   if (e != hipSuccess) return VSA_ERR_HIP;
   CoarseArgs ca{w.qc, w.kc, w.vc, s.B, s.heads, s.D, (int)s.nc, offs ? 0 : topk, oc, lse_c, sel};
   e = launch_coarse_topk(ca, st);
   if (e != hipSuccess) return VSA_ERR_HIP;
-  FineArgs fa{q, w.kp, w.vt, oc, gc, gf, s.B, s.heads, s.D, s.T, s.H, s.W,
+  FineArgs fa{q, w.kp, w.vp, oc, gc, gf, s.B, s.heads, s.D, s.T, s.H, s.W,
               offs, offs ? ids : sel, topk, bf, out, lse_f, of};
   return hip_status(launch_fine_forward(fa, st));
 }
@@ -221,13 +221,13 @@ int block_sparse_attn_varlen(const void* q, const void* k, const void* v,
 
 int vsa_cube_permute_pool(const void* q, const void* k, const void* v,
                           int B, int heads, int head_dim, int T, int H, int W, int dtype,
-                          void* qp, void* kp, void* vt, float* qc, float* kc, float* vc,
+                          void* qp, void* kp, void* vp, float* qc, float* kc, float* vc,
                           hipStream_t stream) {
   Shape s;
   int st = check_shape(B, heads, head_dim, T, H, W, dtype, &s);
   if (st != VSA_OK) return st;
-  if (!q || !k || !v || !kp || !vt || !qc || !kc || !vc) return VSA_ERR_INVALID_ARG;
-  PermutePoolArgs pa{{{q, k, v}, {qp, kp, nullptr}, {nullptr, nullptr, vt}, {qc, kc, vc}, 0},
+  if (!q || !k || !v || !kp || !vp || !qc || !kc || !vc) return VSA_ERR_INVALID_ARG;
+  PermutePoolArgs pa{{{q, k, v}, {qp, kp, vp}, {nullptr, nullptr, nullptr}, {qc, kc, vc}, 0},
                      B, heads, head_dim, T, H, W, dtype == VSA_BF16};
   return hip_status(launch_permute_pool(pa, stream));
 }
@@ -246,7 +246,7 @@ int vsa_coarse_topk(const float* qc, const float* kc, const float* vc,
   return hip_status(launch_coarse_topk(ca, stream));
 }
 
-int vsa_fine_forward(const void* q, const void* kp, const void* vt, const float* oc,
+int vsa_fine_forward(const void* q, const void* kp, const void* vp, const float* oc,
                      const void* gate_c, const void* gate_f,
                      int B, int heads, int head_dim, int T, int H, int W,
                      const int32_t* kv_offsets, const int32_t* kv_ids, int topk, int dtype,
@@ -254,13 +254,13 @@ int vsa_fine_forward(const void* q, const void* kp, const void* vt, const float*
   Shape s;
   int st = check_shape(B, heads, head_dim, T, H, W, dtype, &s);
   if (st != VSA_OK) return st;
-  if (!q || !kp || !vt || !oc || !gate_c || !gate_f || !out) return VSA_ERR_INVALID_ARG;
+  if (!q || !kp || !vp || !oc || !gate_c || !gate_f || !out) return VSA_ERR_INVALID_ARG;
   if ((lse_f == nullptr) != (o_fine == nullptr)) return VSA_ERR_INVALID_ARG;
   if (!kv_offsets) {
     if (topk < 1 || topk > s.nc || !kv_ids) return VSA_ERR_INVALID_ARG;
     if ((int64_t)B * heads * s.nc * topk > INT_MAX) return VSA_ERR_UNSUPPORTED;
   }
-  FineArgs fa{q, kp, vt, oc, gate_c, gate_f, B, heads, head_dim, T, H, W,
+  FineArgs fa{q, kp, vp, oc, gate_c, gate_f, B, heads, head_dim, T, H, W,
               kv_offsets, kv_ids, topk, dtype == VSA_BF16, out, lse_f, o_fine};
   return hip_status(launch_fine_forward(fa, stream));
 }

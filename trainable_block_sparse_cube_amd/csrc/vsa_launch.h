@@ -39,7 +39,7 @@ hipError_t launch_coarse_topk(const CoarseArgs& a, hipStream_t st);
 struct FineArgs {
   const void* q;        // raster [B, N, heads, D]
   const void* kp;       // natural K tiles
-  const void* vt;       // transposed V tiles
+  const void* vp;       // natural V tiles
   const float* oc;
   const void *gc, *gf;  // [B, N, heads]
   int B, heads, D, T, H, W;

@@ -137,7 +137,7 @@ def block_sparse_attn_varlen_backward(q, k, v, gate_c, gate_f, dout, kv_offsets,
 
 # ------------------------------------------------------------ stage calls
 def vsa_cube_permute_pool(q, k, v, grid, with_q_tiles=True):
-    """Returns (qp, kp, vt, qc, kc, vc) in the library's cube-major layouts
+    """Returns (qp, kp, vp, qc, kc, vc) in the library's cube-major layouts
     (qp is None when with_q_tiles is False, as in the forward)."""
     lib = _lib.load()
     B, N, nh, D = q.shape
@@ -145,12 +145,12 @@ def vsa_cube_permute_pool(q, k, v, grid, with_q_tiles=True):
     nc = N // 64
     qp = torch.empty((B, nh, nc, 64, D), dtype=q.dtype, device=q.device) if with_q_tiles else None
     kp = torch.empty((B, nh, nc, 64, D), dtype=q.dtype, device=q.device)
-    vt = torch.empty((B, nh, nc, D, 64), dtype=q.dtype, device=q.device)
+    vp = torch.empty((B, nh, nc, 64, D), dtype=q.dtype, device=q.device)
     pooled = [torch.empty((B, nh, nc, D), dtype=torch.float32, device=q.device) for _ in range(3)]
     st = lib.vsa_cube_permute_pool(_ptr(q), _ptr(k), _ptr(v), B, nh, D, *grid, dt,
-                                   _ptr(qp), _ptr(kp), _ptr(vt), *[_ptr(p) for p in pooled], _stream())
+                                   _ptr(qp), _ptr(kp), _ptr(vp), *[_ptr(p) for p in pooled], _stream())
     _lib.check("vsa_cube_permute_pool", st)
-    return (qp, kp, vt, *pooled)
+    return (qp, kp, vp, *pooled)
 
 
 def vsa_coarse_topk(qc, kc, vc, topk):
@@ -166,9 +166,9 @@ def vsa_coarse_topk(qc, kc, vc, topk):
     return oc, lse, sel
 
 
-def vsa_fine_forward(q, kp, vt, oc, gate_c, gate_f, grid, kv_ids, topk=0, kv_offsets=None,
+def vsa_fine_forward(q, kp, vp, oc, gate_c, gate_f, grid, kv_ids, topk=0, kv_offsets=None,
                      out=None, save=False):
-    """Fine stage + gated combine on raster q and K / V^T tiles.
+    """Fine stage + gated combine on raster q and K / V tiles.
     Returns (out, lse_f or None, o_fine or None)."""
     lib = _lib.load()
     B, N, nh, D = q.shape
@@ -178,7 +178,7 @@ def vsa_fine_forward(q, kp, vt, oc, gate_c, gate_f, grid, kv_ids, topk=0, kv_off
     if save:
         lse = torch.empty((B, nh, N), dtype=torch.float32, device=q.device)
         of = torch.empty((B, nh, N, D), dtype=torch.float32, device=q.device)
-    st = lib.vsa_fine_forward(_ptr(q), _ptr(kp), _ptr(vt), _ptr(oc), _ptr(gate_c), _ptr(gate_f),
+    st = lib.vsa_fine_forward(_ptr(q), _ptr(kp), _ptr(vp), _ptr(oc), _ptr(gate_c), _ptr(gate_f),
                               B, nh, D, *grid, _ptr(kv_offsets), _ptr(kv_ids), topk,
                               _DT[q.dtype], _ptr(out), _ptr(lse), _ptr(of), _stream())
     _lib.check("vsa_fine_forward", st)
