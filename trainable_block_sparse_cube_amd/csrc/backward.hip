@@ -11,20 +11,25 @@
 //
 // Kernels, in launch order (all deterministic, no atomics on floats):
 //   bwd_prep        per (cube, head): dg_c = dO.Oc, dg_f = dO.O_fine (fp32),
-//                   Delta = dOf.O_fine, dOf = g_f dO (bf16, natural and
-//                   transposed tiles), dOc = sum over the cube of g_c dO and
-//                   Delta_c = dOc.Oc
+//                   Delta = dOf.O_fine, dOf = g_f dO (bf16 cube tile),
+//                   dOc = sum over the cube of g_c dO and Delta_c = dOc.Oc
 //   gemm_f32 / coarse_softmax_grad
 //                   coarse backward on the means: S, dP by fp32 MFMA GEMMs,
 //                   P = exp(S - lse_c), dS = P (dP - Delta_c), then
 //                   dQc = s dS Kc, dKc = s dS^T Qc, dVc = P^T dOc
 //   transpose_lists for every key cube, the ascending list of query cubes
-//                   that selected it (counting sort + per-list sort)
+//                   that selected it (counting sort, then a rank sort of
+//                   each list)
 //   fine_bwd_dkdv   key-stationary: one workgroup per key cube accumulates
 //                   dK and dV over the query cubes that selected it
 //   fine_bwd_dq     query-stationary: one workgroup per query cube
 //                   accumulates dQ over its selected key cubes
 // The last two write raster-order gradients with the coarse share added.
+// Both stream their per-pair tiles (Q and dOf, resp. K and V; 16 KB each
+// at D = 128, natural [token][D] layout) with global->LDS copies, double
+// buffered, and take every transposed operand from transposing LDS reads.
+#include <climits>
+
 #include "vsa_device.h"
 #include "vsa_launch.h"
 
@@ -44,14 +49,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
     const bf16* __restrict__ dout, const bf16* __restrict__ gc, const bf16* __restrict__ gf,
     const float* __restrict__ of, const float* __restrict__ oc, int nh, int Tg, int Hg, int Wg,
     float* __restrict__ dgc, float* __restrict__ dgf, float* __restrict__ delta,
-    bf16* __restrict__ dofp, bf16* __restrict__ doft, float* __restrict__ doc,
-    float* __restrict__ deltac) {
+    bf16* __restrict__ dofp, float* __restrict__ doc, float* __restrict__ deltac) {
   constexpr int EPC = 8;
   constexpr int CPR = D / EPC;
   constexpr int RPP = 256 / CPR;
   constexpr int PASSES = kCubeTokens / RPP;
-  constexpr int PITCH = kCubeTokens + EPC;
-  __shared__ __align__(16) bf16 t_lds[D * PITCH];
   __shared__ float red[4][D];
   __shared__ float dsum[D];
 
@@ -118,9 +120,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
     u32x4 packed;
     __builtin_memcpy(&packed, dv, 16);
     *reinterpret_cast<u32x4*>(dofp + tile + (int64_t)s * D + ch * EPC) = packed;
-    const int pos = vt_key_of_pos(s);
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) t_lds[(ch * EPC + e) * PITCH + pos] = dv[e];
   }
 #pragma unroll
   for (int o = CPR; o < 64; o <<= 1)
@@ -136,12 +135,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
     const float v = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
     doc[((int64_t)bh * nc + c) * D + tid] = v;
     dsum[tid] = v * oc[((int64_t)bh * nc + c) * D + tid];
-  }
-  constexpr int VCPR = kCubeTokens / EPC;
-  for (int i = tid; i < D * VCPR; i += 256) {
-    const int d = i / VCPR, cc = i % VCPR;
-    *reinterpret_cast<u32x4*>(doft + tile + (int64_t)d * kCubeTokens + cc * EPC) =
-        *reinterpret_cast<const u32x4*>(&t_lds[d * PITCH + cc * EPC]);
   }
   __syncthreads();
   if (tid == 0) {
@@ -237,14 +230,19 @@ __global__ __launch_bounds__(256) void coarse_softmax_grad_kernel(
 // For every (b, h) and key cube j: tr_ids[tr_offs[r] .. tr_offs[r+1]) are
 // the query cubes whose list contains j, ascending (r = (b*nh + h)*nc + j).
 // Lists: CSR (offs) or fixed length topk (offs == null).  The output of
-// (b, h) occupies the same index range as its input lists.
+// (b, h) occupies the same index range as its input lists.  One workgroup
+// per (b, h): counts (LDS atomics), an exclusive scan, a scatter into `tmp`
+// in arbitrary order, then each list is sorted by rank (a query cube occurs
+// at most once per list, so ranks are distinct): one wave per list, every
+// lane counting the list's smaller entries through readlane broadcasts.
 __global__ __launch_bounds__(256) void transpose_lists_kernel(
     const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk, int nc,
-    int32_t* __restrict__ tr_offs, int32_t* __restrict__ tr_ids) {
-  extern __shared__ int32_t cnt[];  // [nc] counts, then [nc + 1] starts
+    int32_t* __restrict__ tr_offs, int32_t* __restrict__ tr_ids, int32_t* __restrict__ tmp) {
+  extern __shared__ int32_t cnt[];  // [nc] counts / cursors, then [nc + 1] starts
+  __shared__ int32_t wsum[4];
   int32_t* start = cnt + nc;
   const int bh = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t r0 = (int64_t)bh * nc;
   const int base = offs ? offs[r0] : (int)(r0 * topk);
   const int total = (offs ? offs[r0 + nc] : (int)((r0 + nc) * topk)) - base;
@@ -255,11 +253,23 @@ __global__ __launch_bounds__(256) void transpose_lists_kernel(
     if (j >= 0 && j < nc) atomicAdd(&cnt[j], 1);
   }
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int j = 0; j < nc; ++j) { start[j] = run; run += cnt[j]; }
-    start[nc] = run;
+  // exclusive scan: thread t owns counts [t L, t L + L)
+  const int L = (nc + 255) / 256;
+  const int lo = min(tid * L, nc), hi = min(lo + L, nc);
+  int own = 0;
+  for (int j = lo; j < hi; ++j) own += cnt[j];
+  int incl = own;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
   }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int run = incl - own;
+  for (int w = 0; w < wave; ++w) run += wsum[w];
+  for (int j = lo; j < hi; ++j) { start[j] = run; run += cnt[j]; }
+  if (tid == 255) start[nc] = run;
   __syncthreads();
   for (int j = tid; j <= nc; j += 256) tr_offs[r0 + j] = base + start[j];
   for (int j = tid; j < nc; j += 256) cnt[j] = start[j];  // fill cursors
@@ -269,73 +279,60 @@ __global__ __launch_bounds__(256) void transpose_lists_kernel(
     const int e1 = offs ? offs[r0 + c + 1] : e0 + topk;
     for (int e = e0; e < e1; ++e) {
       const int j = ids[e];
-      if (j >= 0 && j < nc) tr_ids[base + atomicAdd(&cnt[j], 1)] = c;
+      if (j >= 0 && j < nc) tmp[base + atomicAdd(&cnt[j], 1)] = c;
     }
   }
   __syncthreads();
-  for (int j = tid; j < nc; j += 256) {  // insertion sort of each list
-    int32_t* l = tr_ids + base + start[j];
-    const int n = start[j + 1] - start[j];
-    for (int i = 1; i < n; ++i) {
-      const int32_t x = l[i];
-      int k = i - 1;
-      while (k >= 0 && l[k] > x) { l[k + 1] = l[k]; --k; }
-      l[k + 1] = x;
+  for (int j = wave; j < nc; j += 4) {
+    const int s0 = start[j], n = start[j + 1] - s0;
+    const int32_t* lst = tmp + base + s0;
+    for (int c0 = 0; c0 < n; c0 += 64) {
+      const int idx = c0 + lane;
+      const int v = idx < n ? lst[idx] : INT_MAX;
+      int rank = 0;
+      for (int k0 = 0; k0 < n; k0 += 64) {
+        const int u = k0 + lane < n ? lst[k0 + lane] : INT_MAX;
+        const int m = min(64, n - k0);
+        for (int i = 0; i < m; ++i) rank += __builtin_amdgcn_readlane(u, i) < v;
+      }
+      if (idx < n) tr_ids[base + s0 + rank] = v;
     }
   }
 }
 
 // ---------------------------------------------------------------- fine
-template <int D>
-__device__ __forceinline__ int swz_row(int row) {
-  if constexpr (D == 128) return row & 15;
-  else return (row ^ (row >> 3)) & 7;
-}
-__device__ __forceinline__ int swz_t(int row) { return (row ^ (row >> 3)) & 7; }
-
-// Stage one natural tile [64][D] (swizzled chunks) and one transposed tile
-// [D][64] (MFMA token order, swizzled chunks) into LDS with plain loads.
-template <int D, int NT>
-__device__ __forceinline__ void stage_nat(const bf16* __restrict__ src, u32x4* dst, int tid) {
-  constexpr int KCH = D / 8;
-  const u32x4* s = reinterpret_cast<const u32x4*>(src);
-  for (int i = tid; i < 64 * KCH; i += NT) {
-    const int row = i / KCH, chk = i % KCH;
-    dst[row * KCH + (chk ^ swz_row<D>(row))] = s[i];
-  }
-}
-template <int D, int NT>
-__device__ __forceinline__ void stage_tr(const bf16* __restrict__ src, u32x4* dst, int tid) {
-  const u32x4* s = reinterpret_cast<const u32x4*>(src);
-  for (int i = tid; i < D * 8; i += NT) {
-    const int row = i >> 3, chk = i & 7;
-    dst[row * 8 + (chk ^ swz_t(row))] = s[i];
-  }
-}
-
-// dK, dV of one key cube.  2 waves; wave w owns keys 32w .. 32w + 31 and all
-// 64 queries of each query tile that selected this key cube:
-//   S  = Q K^T,  dP = dOf V^T      (m = queries, n = keys, k = d)
+// dK, dV of one key cube.  4 waves; wave w: key half kh = w & 1 (keys
+// 32kh .. +32), query half qh = w >> 1 of every query tile that selected
+// this key cube.  Per query tile:
+//   S  = Q K^T,  dP = dOf V^T        (m = 32 queries, n = 32 keys, k = d)
 //   P = exp(s S - lse), dS = P (dP - Delta)
-//   dV^T += dOf^T P,  dK^T += Q^T dS  (m = d, n = keys, k = queries)
+// then the two waves of a key half swap half of their results through LDS
+// (the qh = 0 wave hands over dS, the qh = 1 wave P), and over all 64
+// queries (m = d, n = keys, k = queries)
+//   qh = 0:  dV^T += dOf^T P          qh = 1:  dK^T += Q^T dS
+// with dOf^T and Q^T read transposed from the natural tiles.
 template <int D>
-__global__ __launch_bounds__(128, 1) void fine_bwd_dkdv_kernel(
+__global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(
     const bf16* __restrict__ qp, const bf16* __restrict__ kp, const bf16* __restrict__ vp,
-    const bf16* __restrict__ qt, const bf16* __restrict__ dofp, const bf16* __restrict__ doft,
-    const float* __restrict__ lse_f, const float* __restrict__ delta,
+    const bf16* __restrict__ dofp, const float* __restrict__ lse_f, const float* __restrict__ delta,
     const int32_t* __restrict__ tr_offs, const int32_t* __restrict__ tr_ids,
     const float* __restrict__ dkc, const float* __restrict__ dvc,
     int nh, int nc, int Hg, int Wg, float scale,
     bf16* __restrict__ dk, bf16* __restrict__ dv) {
-  constexpr int KS = D / 16, KCH = D / 8, MD = D / 32;
-  __shared__ __align__(16) u32x4 q_lds[64 * KCH];
-  __shared__ __align__(16) u32x4 do_lds[64 * KCH];
-  __shared__ __align__(16) u32x4 qt_lds[D * 8];
-  __shared__ __align__(16) u32x4 dot_lds[D * 8];
-  __shared__ float lse_s[64], del_s[64];
+  constexpr int KS = D / 16, MD = D / 32, TILE_CH = 64 * D / 8;
+  // Tile parity buffers: separate arrays picked at run time, so that the
+  // compiler adds no waits of its own for the global->LDS copies.
+  __shared__ __align__(256) u32x4 q_lds0[TILE_CH];
+  __shared__ __align__(256) u32x4 q_lds1[TILE_CH];
+  __shared__ __align__(256) u32x4 o_lds0[TILE_CH];
+  __shared__ __align__(256) u32x4 o_lds1[TILE_CH];
+  __shared__ __align__(16) float ld_s0[128];  // lse (64 queries), then Delta (64)
+  __shared__ __align__(16) float ld_s1[128];
+  __shared__ __align__(16) bf16x8 xch[4][2][64];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ql = lane & 31, hf = lane >> 5;
+  const int kh = wave & 1, qh = wave >> 1;
   const int blk = blockIdx.x;  // (b*nh + h)*nc + key cube
   const int bh = blk / nc, j = blk - bh * nc;
   const int64_t N = (int64_t)nc * 64;
@@ -346,128 +343,147 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dkdv_kernel(
   // d = (D/2) hf + 8 s .. +8.
   bf16x8 kB[KS], vB[KS];
   {
-    const int64_t row = (bh_tiles + j) * 64 + 32 * wave + ql;
+    const int64_t row = (bh_tiles + j) * 64 + 32 * kh + ql;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       kB[s] = *reinterpret_cast<const bf16x8*>(kp + row * D + (D / 2) * hf + 8 * s);
       vB[s] = *reinterpret_cast<const bf16x8*>(vp + row * D + (D / 2) * hf + 8 * s);
     }
   }
-  f32x16 dka[MD], dva[MD];
+  f32x16 acc[MD];
 #pragma unroll
   for (int m = 0; m < MD; ++m)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { dka[m][r] = 0.f; dva[m][r] = 0.f; }
+    for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
 
-  const int e0 = tr_offs[blk], e1 = tr_offs[blk + 1];
-  for (int e = e0; e < e1; ++e) {
-    const int c = tr_ids[e];
+  const uint32_t tr_lo = tr_offset<D>(lane, 0), tr_hi = tr_offset<D>(lane, 1);
+  const int e0 = tr_offs[blk], n = tr_offs[blk + 1] - e0;
+  auto copy_tile = [&](int c, int buf) {
     const int64_t t = (bh_tiles + c) * 64;
-    __syncthreads();
-    stage_nat<D, 128>(qp + t * D, q_lds, tid);
-    stage_nat<D, 128>(dofp + t * D, do_lds, tid);
-    stage_tr<D, 128>(qt + t * D, qt_lds, tid);
-    stage_tr<D, 128>(doft + t * D, dot_lds, tid);
-    if (tid < 64) lse_s[tid] = lse_f[(int64_t)bh * N + (int64_t)c * 64 + tid] * kLog2e;
-    else del_s[tid - 64] = delta[(int64_t)bh * N + (int64_t)c * 64 + tid - 64];
-    __syncthreads();
-
-    bf16x8 pB[2][2], dsB[2][2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      f32x16 sa, da;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { sa[r] = 0.f; da[r] = 0.f; }
-      const int qrow = 32 * mb + ql;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int chk = (KS * hf + s) ^ swz_row<D>(qrow);
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&q_lds[qrow * KCH + chk]);
-        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&do_lds[qrow * KCH + chk]);
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kB[s], sa, 0, 0, 0);
-        da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vB[s], da, 0, 0, 0);
-      }
-      // this lane: key column ql, query rows 32mb + 8(r/4) + 4hf + r%4
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int e8 = 0; e8 < 8; ++e8) {
-          const int r = 8 * g + e8;
-          const int q = 32 * mb + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const float p = __builtin_amdgcn_exp2f(fmaf(sa[r], scale_log2, -lse_s[q]));
-          pB[mb][g][e8] = (bf16)p;
-          dsB[mb][g][e8] = (bf16)(p * (da[r] - del_s[q]));
-        }
+    dma_tile<D>(qp + t * D, buf ? q_lds1 : q_lds0, wave, lane);
+    dma_tile<D>(dofp + t * D, buf ? o_lds1 : o_lds0, wave, lane);
+    if (wave == 0 && lane < 32) {  // 16 lanes of lse, 16 of Delta
+      const int64_t tok = (int64_t)bh * N + (int64_t)c * 64 + 4 * (lane & 15);
+      copy16_to_lds(lane < 16 ? lse_f + tok : delta + tok, buf ? ld_s1 : ld_s0);
     }
-    // dV^T += dOf^T P,  dK^T += Q^T dS : k-steps (mb, g) over 64 queries
+  };
+  if (n > 0) copy_tile(tr_ids[e0], 0);
+
+  for (int it = 0; it < n; ++it) {
+    const int buf = it & 1;
+    wait_vmcnt<0>();   // this wave's copies of tile `it` have landed
+    __syncthreads();   // all copies visible; buffer buf^1 and xch free
+    if (it + 1 < n) copy_tile(tr_ids[e0 + it + 1], buf ^ 1);
+    const u32x4* qb = buf ? q_lds1 : q_lds0;
+    const u32x4* ob = buf ? o_lds1 : o_lds0;
+    const float* ls = buf ? ld_s1 : ld_s0;
+
+    bf16x8 qa[KS], oa[KS];
+    const int qrow = 32 * qh + ql;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qa[s] = tile_row8<D>(qb, qrow, KS * hf + s);
+      oa[s] = tile_row8<D>(ob, qrow, KS * hf + s);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 sa, da;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { sa[r] = 0.f; da[r] = 0.f; }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kB[s], sa, 0, 0, 0);
+      da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[s], vB[s], da, 0, 0, 0);
+    }
+    // Q^T (dK wave) or dOf^T (dV wave) operands of column block 0, read
+    // while the MFMAs above run; blocks m > 0 follow the MFMAs of m - 1.
+    const uint32_t xbase = lds_addr(qh ? qb : ob);
+    bf16x8 xa[4];
+    tile_tr8_asm<D, 4>(xa, xbase + tr_lo, xbase + tr_hi);
+    // this lane: key column ql, query rows 32qh + 8(r/4) + 4hf + r%4
+    bf16x8 pB[2], dsB[2];
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int q0 = 32 * qh + 8 * rg + 4 * hf;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + q0);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(ls + 64 + q0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * rg + i;
+        const float p = __builtin_amdgcn_exp2f(fmaf(sa[r], scale_log2, -l4[i] * kLog2e));
+        pB[r >> 3][r & 7] = (bf16)p;
+        dsB[r >> 3][r & 7] = (bf16)(p * (da[r] - d4[i]));
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) xch[wave][g][lane] = qh ? pB[g] : dsB[g];
+    lds_barrier();
+    bf16x8 bq0[2], bq1[2];  // B operands for queries 0..31 and 32..63
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const bf16x8 other = xch[wave ^ 2][g][lane];
+      bq0[g] = qh ? other : pB[g];
+      bq1[g] = qh ? dsB[g] : other;
+    }
 #pragma unroll
     for (int m = 0; m < MD; ++m) {
-      const int row = 32 * m + ql;
+      if (m > 0) tile_tr8_asm<D, 4>(xa, (xbase + tr_lo) ^ (m << 6), (xbase + tr_hi) ^ (m << 6));
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const int chk = (2 * (2 * mb + g) + hf) ^ swz_t(row);
-          const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&dot_lds[row * 8 + chk]);
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&qt_lds[row * 8 + chk]);
-          dva[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pB[mb][g], dva[m], 0, 0, 0);
-          dka[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dsB[mb][g], dka[m], 0, 0, 0);
-        }
+      for (int t = 0; t < 4; ++t)
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[t], t < 2 ? bq0[t] : bq1[t - 2], acc[m], 0, 0, 0);
     }
   }
 
   // raster rows of this wave's keys, coarse share (mean adjoint) added
-  const int slot = 32 * wave + ql;
+  const int slot = 32 * kh + ql;
   const int b = bh / nh, h = bh - b * nh;
   const int tok = raster_tok(j, slot, Hg, Wg);
   const int64_t gidx = ((int64_t)b * N + tok) * nh + h;
-  const float* kcr = dkc + (bh_tiles + j) * D;
-  const float* vcr = dvc + (bh_tiles + j) * D;
+  const float* crow = (qh ? dkc : dvc) + (bh_tiles + j) * D;
+  bf16* orow = (qh ? dk : dv) + gidx * D;
+  const float mul = qh ? scale : 1.0f;
 #pragma unroll
   for (int m = 0; m < MD; ++m)
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
       const int d0 = 32 * m + 8 * rg + 4 * hf;
-      const f32x4 ck = *reinterpret_cast<const f32x4*>(kcr + d0);
-      const f32x4 cv = *reinterpret_cast<const f32x4*>(vcr + d0);
-      bf16x4 ok, ov;
+      const f32x4 cv = *reinterpret_cast<const f32x4*>(crow + d0);
+      bf16x4 o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ok[i] = (bf16)fmaf(scale, dka[m][4 * rg + i], ck[i] * (1.0f / kCubeTokens));
-        ov[i] = (bf16)(dva[m][4 * rg + i] + cv[i] * (1.0f / kCubeTokens));
-      }
-      *reinterpret_cast<bf16x4*>(dk + gidx * D + d0) = ok;
-      *reinterpret_cast<bf16x4*>(dv + gidx * D + d0) = ov;
+      for (int i = 0; i < 4; ++i) o[i] = (bf16)fmaf(mul, acc[m][4 * rg + i], cv[i] * (1.0f / kCubeTokens));
+      *reinterpret_cast<bf16x4*>(orow + d0) = o;
     }
 }
 
-// dQ of one query cube.  2 waves; wave w owns queries 32w .. 32w + 31:
-//   S^T = K Q^T, dP^T = V dOf^T    (m = keys, n = queries, k = d)
+// dQ of one query cube.  4 waves; wave w: key half kh = w & 1 of every
+// selected key tile, query half qh = w >> 1 (queries 32qh .. +32):
+//   S^T = K Q^T, dP^T = V dOf^T    (m = 32 keys, n = 32 queries, k = d)
 //   dS^T = P^T (dP^T - Delta)
-//   dQ = sum over tiles t of  dS_t (K_t - kc_t)  +  s_t kc_t,
-//        s_t = sum of dS over the keys of tile t (fp32)
-// The first term runs on MFMA with K^T tiles centred on their cube mean
-// kc_t (kt holds K - kc); the second is an fp32 vector update.  Because the
-// exact dS sums to zero over a row, sum_t s_t c adds nothing for any fixed
-// vector c; taking c = kc of the row's first tile removes the rounding
-// residue of sum_t s_t along the keys' large shared component, which would
-// otherwise dominate dQ when the selected cubes share a mean.
+//   dQ^T += K^T dS^T               (m = d, n = queries, k = 32 keys)
+// K^T is read transposed from the natural K tile.  The exact dS sums to
+// zero over each query's keys, so sum_j dS_j c adds nothing for any fixed
+// vector c; the computed dS does not quite (Delta comes from the forward's
+// output, whose weights were rounded to bf16), and that residue times the
+// keys' large shared component (cubes with a common mean) would dominate
+// dQ.  So dQ = sum_j dS_j K_j - (sum_j dS_j) c0, with c0 the mean of the
+// first listed key cube and both sums in fp32; dS enters the product as a
+// bf16 pair (hi + lo, both MFMA operands) so that its own rounding leaves no
+// such residue.  The two key halves are summed at the end.
 template <int D>
-__global__ __launch_bounds__(128, 1) void fine_bwd_dq_kernel(
+__global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(
     const bf16* __restrict__ qp, const bf16* __restrict__ kp, const bf16* __restrict__ vp,
-    const bf16* __restrict__ kt, const bf16* __restrict__ dofp,
-    const float* __restrict__ lse_f, const float* __restrict__ delta,
+    const bf16* __restrict__ dofp, const float* __restrict__ lse_f, const float* __restrict__ delta,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk,
     const float* __restrict__ dqc, const float* __restrict__ kc_mean,
     int nh, int nc, int Hg, int Wg, float scale, bf16* __restrict__ dq) {
-  constexpr int KS = D / 16, KCH = D / 8, MD = D / 32;
-  __shared__ __align__(16) u32x4 k_lds[64 * KCH];
-  __shared__ __align__(16) u32x4 v_lds[64 * KCH];
-  __shared__ __align__(16) u32x4 kt_lds[D * 8];
-  __shared__ __align__(16) float kc_s[D];
+  constexpr int KS = D / 16, MD = D / 32, TILE_CH = 64 * D / 8;
+  __shared__ __align__(256) u32x4 k_lds0[TILE_CH];
+  __shared__ __align__(256) u32x4 k_lds1[TILE_CH];
+  __shared__ __align__(16) u32x4 v_lds0[TILE_CH];
+  __shared__ __align__(16) u32x4 v_lds1[TILE_CH];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ql = lane & 31, hf = lane >> 5;
+  const int kh = wave & 1, qh = wave >> 1;
   const int blk = blockIdx.x;  // (b*nh + h)*nc + query cube
   const int bh = blk / nc, c = blk - bh * nc;
   const int64_t N = (int64_t)nc * 64;
@@ -476,8 +492,9 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dq_kernel(
   int start, n;
   if (offs) { start = offs[blk]; n = offs[blk + 1] - start; }
   else { start = blk * topk; n = topk; }
+  const int32_t* list = ids + start;
 
-  const int slot = 32 * wave + ql;
+  const int slot = 32 * qh + ql;
   bf16x8 qB[KS], oB[KS];
   {
     const int64_t row = (bh_tiles + c) * 64 + slot;
@@ -489,78 +506,93 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dq_kernel(
   }
   const float lse2 = lse_f[(int64_t)bh * N + (int64_t)c * 64 + slot] * kLog2e;
   const float del = delta[(int64_t)bh * N + (int64_t)c * 64 + slot];
-  f32x16 dqa[MD], cor[MD];
+  f32x16 acc[MD];
 #pragma unroll
   for (int m = 0; m < MD; ++m)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { dqa[m][r] = 0.f; cor[m][r] = 0.f; }
-  float ssum = 0.f;
+    for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
+  float ssum = 0.f;  // this lane's share of sum_j dS_j
+
+  auto copy_tile = [&](int kc, int buf) {
+    dma_tile<D>(kp + (bh_tiles + kc) * 64 * D, buf ? k_lds1 : k_lds0, wave, lane);
+    dma_tile<D>(vp + (bh_tiles + kc) * 64 * D, buf ? v_lds1 : v_lds0, wave, lane);
+  };
+  if (n > 0) copy_tile(list[0], 0);
+  const int krow = 32 * kh + ql;
+  // transposed reads of K rows 32kh .. 32kh + 31
+  const uint32_t tr_lo = tr_offset<D>(lane, 0) + 32 * kh * D * 2;
+  const uint32_t tr_hi = tr_offset<D>(lane, 1) + 32 * kh * D * 2;
 
   for (int it = 0; it < n; ++it) {
-    const int kc = ids[start + it];
-    const int64_t t = (bh_tiles + kc) * 64;
+    const int buf = it & 1;
+    wait_vmcnt<0>();
     __syncthreads();
-    stage_nat<D, 128>(kp + t * D, k_lds, tid);
-    stage_nat<D, 128>(vp + t * D, v_lds, tid);
-    stage_tr<D, 128>(kt + t * D, kt_lds, tid);
-    if (tid < D) kc_s[tid] = kc_mean[(bh_tiles + kc) * D + tid];
-    __syncthreads();
-    bf16x8 dsB[2][2];
-    float st = 0.f;  // sum of this lane's dS over its keys of the tile
+    if (it + 1 < n) copy_tile(list[it + 1], buf ^ 1);
+    const u32x4* kb = buf ? k_lds1 : k_lds0;
+    const u32x4* vb = buf ? v_lds1 : v_lds0;
+
+    bf16x8 ka[KS], va[KS];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      f32x16 sa, da;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { sa[r] = 0.f; da[r] = 0.f; }
-      const int krow = 32 * mb + ql;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int chk = (KS * hf + s) ^ swz_row<D>(krow);
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&k_lds[krow * KCH + chk]);
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&v_lds[krow * KCH + chk]);
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qB[s], sa, 0, 0, 0);
-        da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, oB[s], da, 0, 0, 0);
-      }
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int e8 = 0; e8 < 8; ++e8) {
-          const int r = 8 * g + e8;
-          const float p = __builtin_amdgcn_exp2f(fmaf(sa[r], scale_log2, -lse2));
-          const float ds = p * (da[r] - del);
-          st += ds;
-          dsB[mb][g][e8] = (bf16)ds;
-        }
+    for (int s = 0; s < KS; ++s) {
+      ka[s] = tile_row8<D>(kb, krow, KS * hf + s);
+      va[s] = tile_row8<D>(vb, krow, KS * hf + s);
     }
-    st += swap_halves(st);
-    ssum += st;
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 sa, da;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { sa[r] = 0.f; da[r] = 0.f; }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qB[s], sa, 0, 0, 0);
+      da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s], oB[s], da, 0, 0, 0);
+    }
+    // K^T operands (m = d, k = keys), read while the MFMAs above run
+    const uint32_t kbase = lds_addr(kb);
+    bf16x8 ta[MD][2];
+#pragma unroll
+    for (int m = 0; m < MD; ++m) tile_tr8_asm<D, 2>(ta[m], (kbase + tr_lo) ^ (m << 6), (kbase + tr_hi) ^ (m << 6));
+    // this lane: query column ql, key rows 32kh + 8(r/4) + 4hf + r%4
+    bf16x8 hiB[2], loB[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sa[r], scale_log2, -lse2));
+      const float ds = p * (da[r] - del);
+      ssum += ds;
+      const bf16 hi = (bf16)ds;
+      hiB[r >> 3][r & 7] = hi;
+      loB[r >> 3][r & 7] = (bf16)(ds - (float)hi);
+    }
 #pragma unroll
     for (int m = 0; m < MD; ++m)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const f32x4 kv = *reinterpret_cast<const f32x4*>(&kc_s[32 * m + 8 * rg + 4 * hf]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cor[m][4 * rg + i] = fmaf(st, kv[i], cor[m][4 * rg + i]);
+      for (int g = 0; g < 2; ++g) {
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[m][g], hiB[g], acc[m], 0, 0, 0);
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[m][g], loB[g], acc[m], 0, 0, 0);
       }
-#pragma unroll
-    for (int m = 0; m < MD; ++m) {
-      const int row = 32 * m + ql;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const int chk = (2 * (2 * mb + g) + hf) ^ swz_t(row);
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kt_lds[row * 8 + chk]);
-          dqa[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, dsB[mb][g], dqa[m], 0, 0, 0);
-        }
-    }
   }
+
+  ssum += swap_halves(ssum);  // over this wave's 32 keys of every tile
+  // Sum the key halves: the kh = 1 wave hands its dQ^T and dS sum to the
+  // kh = 0 wave of the same query half through LDS.
+  __syncthreads();  // all tile reads done; the buffers are free
+  float* xo = reinterpret_cast<float*>(qh ? k_lds1 : k_lds0);  // 32 q x D floats
+  float* xs = reinterpret_cast<float*>(qh ? v_lds1 : v_lds0);  // 32 q
+  if (kh == 1) {
+#pragma unroll
+    for (int m = 0; m < MD; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[(m * 16 + r) * 64 + lane] = acc[m][r];
+    if (hf == 0) xs[ql] = ssum;
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  ssum += xs[ql];
+  const float* c0 = kc_mean + (bh_tiles + (n > 0 ? list[0] : 0)) * D;
 
   const int b = bh / nh, h = bh - b * nh;
   const int tok = raster_tok(c, slot, Hg, Wg);
   const int64_t gidx = ((int64_t)b * N + tok) * nh + h;
   const float* qcr = dqc + (bh_tiles + c) * D;
-  const float* c0 = kc_mean + (bh_tiles + (n > 0 ? ids[start] : 0)) * D;
 #pragma unroll
   for (int m = 0; m < MD; ++m)
 #pragma unroll
@@ -572,7 +604,7 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dq_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * rg + i;
-        const float fine = dqa[m][r] + (cor[m][r] - ssum * cc[i]);
+        const float fine = (acc[m][r] + xo[(m * 16 + r) * 64 + lane]) - ssum * cc[i];
         o[i] = (bf16)fmaf(scale, fine, cq[i] * (1.0f / kCubeTokens));
       }
       *reinterpret_cast<bf16x4*>(dq + gidx * D + d0) = o;
@@ -597,7 +629,7 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t st) {
 #define VSA_TRY(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
   bwd_prep_kernel<D><<<(unsigned)(a.B * nc * a.heads), 256, 0, st>>>(
       (const bf16*)a.dout, (const bf16*)a.gc, (const bf16*)a.gf, a.of, a.oc, a.heads, a.T, a.H, a.W,
-      (float*)a.dgc, (float*)a.dgf, a.delta, (bf16*)a.dofp, (bf16*)a.doft, a.doc, a.deltac);
+      (float*)a.dgc, (float*)a.dgf, a.delta, (bf16*)a.dofp, a.doc, a.deltac);
   VSA_TRY(hipGetLastError());
   // coarse backward on the cube means
   const int64_t sq = (int64_t)nc * D, ss = (int64_t)nc * nc;
@@ -611,18 +643,18 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t st) {
   VSA_TRY((gemm<true, false>(a.S, nc, ss, a.doc, D, sq, a.dvc, D, sq, nc, D, nc, 1.0f, BH, st)));
   // transposed selection
   transpose_lists_kernel<<<(unsigned)BH, 256, sizeof(int32_t) * (2 * nc + 1), st>>>(
-      a.offs, a.ids, a.topk, nc, a.tr_offs, a.tr_ids);
+      a.offs, a.ids, a.topk, nc, a.tr_offs, a.tr_ids, a.tr_tmp);
   VSA_TRY(hipGetLastError());
   const unsigned grid = (unsigned)(BH * nc);
-  fine_bwd_dkdv_kernel<D><<<grid, 128, 0, st>>>(
-      (const bf16*)a.qp, (const bf16*)a.kp, (const bf16*)a.vp, (const bf16*)a.qt,
-      (const bf16*)a.dofp, (const bf16*)a.doft, a.lse_f, a.delta, a.tr_offs, a.tr_ids,
-      a.dkc, a.dvc, a.heads, nc, a.H, a.W, scale, (bf16*)a.dk, (bf16*)a.dv);
+  fine_bwd_dkdv_kernel<D><<<grid, 256, 0, st>>>(
+      (const bf16*)a.qp, (const bf16*)a.kp, (const bf16*)a.vp, (const bf16*)a.dofp,
+      a.lse_f, a.delta, a.tr_offs, a.tr_ids, a.dkc, a.dvc, a.heads, nc, a.H, a.W, scale,
+      (bf16*)a.dk, (bf16*)a.dv);
   VSA_TRY(hipGetLastError());
-  fine_bwd_dq_kernel<D><<<grid, 128, 0, st>>>(
-      (const bf16*)a.qp, (const bf16*)a.kp, (const bf16*)a.vp, (const bf16*)a.kt,
-      (const bf16*)a.dofp, a.lse_f, a.delta, a.offs, a.ids, a.topk, a.dqc, a.kc,
-      a.heads, nc, a.H, a.W, scale, (bf16*)a.dq);
+  fine_bwd_dq_kernel<D><<<grid, 256, 0, st>>>(
+      (const bf16*)a.qp, (const bf16*)a.kp, (const bf16*)a.vp, (const bf16*)a.dofp,
+      a.lse_f, a.delta, a.offs, a.ids, a.topk, a.dqc, a.kc, a.heads, nc, a.H, a.W, scale,
+      (bf16*)a.dq);
   VSA_TRY(hipGetLastError());
 #undef VSA_TRY
   return hipSuccess;

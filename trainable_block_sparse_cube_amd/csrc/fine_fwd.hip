@@ -17,11 +17,12 @@
 //   half-waves (v_permlane32_swap)
 //   O^T (D x 32) += V^T * P^T                      D/16 x mfma 32x32x16
 // Each wave keeps its own softmax state over its key half; the two halves
-// are merged once at the end (split softmax).  K and V^T tiles (16 KB each
-// at D = 128) are copied straight from global memory into LDS
-// (global_load_lds, no register staging) with an XOR chunk swizzle, double
-// buffered: tile t+1 streams in while tile t is computed, one barrier per
-// tile.  The epilogue divides by the row sum, mixes in the coarse output
+// are merged once at the end (split softmax).  K and V tiles (16 KB each
+// at D = 128, both in natural [key][D] order) are copied straight from
+// global memory into LDS (global_load_lds, no register staging) with an XOR
+// chunk swizzle, double buffered: tile t+1 streams in while tile t is
+// computed, one barrier per tile.  V^T operands come from transposing LDS
+// reads (ds_read_b64_tr_b16).  The epilogue divides by the row sum, mixes in the coarse output
 // with the two gates, rounds once to bf16 and scatters rows back to raster
 // token order.
 //
@@ -40,50 +41,6 @@ __device__ __forceinline__ int raster_token(int c, int s, int Hg, int Wg) {
   return ((4 * ct + (s >> 4)) * Hg + 4 * cy + ((s >> 2) & 3)) * Wg + 4 * cx + (s & 3);
 }
 
-// XOR swizzles of 16-byte chunk columns in LDS tiles (bank-conflict-free
-// MFMA operand reads).  K tile rows are D*2 bytes; V^T rows are 128 bytes.
-template <int D>
-__device__ __forceinline__ int swz_k(int row) {
-  if constexpr (D == 128) return row & 15;
-  else return (row ^ (row >> 3)) & 7;
-}
-// V tiles stay in natural [key][D] order and are read transposed with
-// ds_read_b64_tr_b16.  One read instruction touches, per 16 lanes, 4 key
-// rows x 2 chunks and, per 32 lanes, 4 rows x 4 chunks; the swizzle gives
-// the 4 rows distinct values in chunk bits 1-2 and in bits 2-3, so both
-// groupings fall on distinct banks.
-template <int D>
-__device__ __forceinline__ int swz_vn(int row) {
-  const int r = row & 3;
-  if constexpr (D == 128) return (r << 2) ^ (((r ^ (r >> 1)) & 1) << 1);
-  else return 2 * r;
-}
-
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-
-// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives
-// element i % 4 of the 8-byte loads of lanes 4e + i / 4, e = 0..3.  With
-// lane 4e + q pointing at row r0 + e, columns c0 + 4q .. +4 of a row-major
-// 16-bit tile, lane i gets column c0 + i of rows r0 .. r0 + 3.
-__device__ __forceinline__ bf16x4 read_tr16(const void* lds_byte_addr) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (lds_bf16x4*)((__attribute__((address_space(3))) char*)lds_byte_addr));
-}
-
-// vmcnt-only wait (expcnt and lgkmcnt left at their maxima), gfx9 encoding.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// One 16-byte global -> LDS copy per lane; lane l of the wave writes LDS
-// bytes [16 l, 16 l + 16) past `lds_wave_base` (wave-uniform).
-__device__ __forceinline__ void copy16_to_lds(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
-}
-
 template <int D>
 __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kp, const bf16* __restrict__ vp,
@@ -93,15 +50,13 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     float scale_log2,
     bf16* __restrict__ out, float* __restrict__ lse_f, float* __restrict__ o_fine) {
   constexpr int KS = D / 16;          // k-steps of S^T over head_dim
-  constexpr int KCH = D / 8;          // 16-byte chunks per K row
-  constexpr int TILE_CH = 64 * KCH;   // chunks per K (and per V^T) tile
-  constexpr int LD = TILE_CH / 256;   // copy instructions per wave per tile and tensor
+  constexpr int TILE_CH = 64 * D / 8; // 16-byte chunks per K (and per V) tile
   constexpr int MD = D / 32;          // m-blocks of O^T
   // Lazy rescaling: the running max moves only when a tile's max exceeds
   // it by more than this many powers of two (exact; bounds p by 2^8).
   constexpr float kRescale = 8.f;
 
-  // Two buffers (tile parity) of K and V^T.  Separate arrays, picked at run
+  // Two buffers (tile parity) of K and V.  Separate arrays, picked at run
   // time, so that the compiler adds no waits of its own for the copies; the
   // waits below (vmcnt + barrier) order every copy before its reads.
   __shared__ __align__(16) u32x4 k_lds0[TILE_CH];
@@ -126,23 +81,13 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
   const int64_t bh_tiles = (int64_t)bh * nc;
   const int b = bh / nh, h = bh - b * nh;
 
-  // Copy K tile and V^T tile of key cube kc into buffer `buf`, XOR-swizzled:
-  // the lane landing on LDS chunk P = (row, phys) fetches chunk phys ^ swz.
-  // Both come from contiguous cube-major tiles (each is re-read by about K
-  // query cubes, and one contiguous 16 KB block streams better than 64
-  // scattered token rows).
+  // Copy the K and V tiles of key cube kc into buffer `buf`.  Both come
+  // from contiguous cube-major tiles (each is re-read by about K query
+  // cubes, and one contiguous 16 KB block streams better than 64 scattered
+  // token rows).
   auto copy_tile = [&](int kc, int buf) {
-    const bf16* ksrc = kp + (bh_tiles + kc) * 64 * D;
-    const bf16* vsrc = vp + (bh_tiles + kc) * 64 * D;
-    u32x4* kdst = buf ? k_lds1 : k_lds0;
-    u32x4* vdst = buf ? v_lds1 : v_lds0;
-#pragma unroll
-    for (int j = 0; j < LD; ++j) {
-      const int P = (4 * j + wave) * 64 + lane;
-      const int krow = P / KCH, kphys = P % KCH;
-      copy16_to_lds(ksrc + (krow * KCH + (kphys ^ swz_k<D>(krow))) * 8, kdst + (4 * j + wave) * 64);
-      copy16_to_lds(vsrc + (krow * KCH + (kphys ^ swz_vn<D>(krow))) * 8, vdst + (4 * j + wave) * 64);
-    }
+    dma_tile<D>(kp + (bh_tiles + kc) * 64 * D, buf ? k_lds1 : k_lds0, wave, lane);
+    dma_tile<D>(vp + (bh_tiles + kc) * 64 * D, buf ? v_lds1 : v_lds0, wave, lane);
   };
 
   // Q^T operands, read once in place from the raster q: lane (query ql of
@@ -168,7 +113,6 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     const int buf = it & 1;
     wait_vmcnt<0>();   // this wave's copies of tile `it` have landed
     __syncthreads();   // all copies of tile `it` visible; buffer buf^1 free
-    if (it + 1 < n) copy_tile(list[it + 1], buf ^ 1);
     const u32x4* kb = buf ? k_lds1 : k_lds0;
     const u32x4* vb = buf ? v_lds1 : v_lds0;
 
@@ -176,24 +120,21 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     // latency overlaps the MFMA chain instead of stalling each step.
     bf16x8 ka[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      ka[s] = *reinterpret_cast<const bf16x8*>(&kb[krow * KCH + ((KS * hf + s) ^ swz_k<D>(krow))]);
-    // V^T operands from the natural V tile: lane (d, hf) needs keys
-    // 32kh + 16g + 4hf + {0..3} and the same + 8 (the order of pB).
+    for (int s = 0; s < KS; ++s) ka[s] = tile_row8<D>(kb, krow, KS * hf + s);
+    // V^T operands, read transposed from the natural V tile: keys
+    // 32kh + 16g .. +16 in the order of pB.
     bf16x8 va[MD][2];
 #pragma unroll
     for (int m = 0; m < MD; ++m)
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int d = 32 * m + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        const int r0 = 32 * kh + 16 * g + 4 * hf + ((lane & 15) >> 2);
-        const char* vbase = reinterpret_cast<const char*>(vb);
-        const int a0 = r0 * (KCH * 16) + (((d >> 3) ^ swz_vn<D>(r0)) << 4) + (d & 7) * 2;
-        const int a1 = (r0 + 8) * (KCH * 16) + (((d >> 3) ^ swz_vn<D>(r0 + 8)) << 4) + (d & 7) * 2;
-        const bf16x4 lo = read_tr16(vbase + a0), hi = read_tr16(vbase + a1);
-        va[m][g] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
+      for (int g = 0; g < 2; ++g) va[m][g] = tile_tr8<D>(vb, 32 * kh + 16 * g, 32 * m, lane);
     __builtin_amdgcn_sched_barrier(0);  // keep the reads batched ahead of their MFMAs
+    // The next tile's copy is queued only now: the compiler makes each
+    // transposing read wait for every global->LDS copy in flight, so the
+    // copy must not be in flight while they issue.  It still overlaps all
+    // of this tile's arithmetic.
+    if (it + 1 < n) copy_tile(list[it + 1], buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
 
     // S^T (32 keys x 32 queries) = K[32kh..] * Q[32qh..]^T
     f32x16 sacc;

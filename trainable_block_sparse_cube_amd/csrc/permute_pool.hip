@@ -7,11 +7,8 @@
 // it gathers the cube's 64 token rows (each row D contiguous elements in the
 // raster layout), writes them as one contiguous cube-major tile, and reduces
 // the 64 rows to their fp32 mean with wavefront shuffles plus a 4-way LDS
-// combine.  Each tensor can be written in natural order ([64 tokens][D]),
-// transposed ([D][64 tokens], tokens in MFMA order, so that MFMA steps
-// contracting over tokens read 16-byte vectors), or both.  The forward uses
-// natural Q, K and transposed V; the backward natural Q, K, V and
-// transposed Q, K.
+// combine.  The forward writes the K and V tiles (the fine stage reads Q in
+// place); the backward writes Q, K and V tiles.
 #include "vsa_device.h"
 #include "vsa_launch.h"
 
@@ -23,17 +20,13 @@ __global__ __launch_bounds__(256) void permute_pool_kernel(PermutePoolPtrs p, in
   constexpr int CPR = D / EPC;            // chunks per token row
   constexpr int ROWS_PER_PASS = 256 / CPR;
   constexpr int PASSES = kCubeTokens / ROWS_PER_PASS;
-  constexpr int VT_PITCH = kCubeTokens + EPC;  // padded LDS row of a transposed tile
   static_assert(256 % CPR == 0 && kCubeTokens % ROWS_PER_PASS == 0, "tiling");
 
-  __shared__ __align__(16) T vt_lds[D * VT_PITCH];
   __shared__ float red[4][D];
-  __shared__ float mean_s[D];
 
   const int which = blockIdx.y;  // 0: q, 1: k, 2: v
   const T* __restrict__ src = (const T*)p.src[which];
   T* __restrict__ nat = (T*)p.nat[which];
-  T* __restrict__ tr = (T*)p.tr[which];
   float* __restrict__ pooled = p.pooled[which];
 
   const int nc = (Tg / 4) * (Hg / 4) * (Wg / 4);
@@ -63,11 +56,6 @@ __global__ __launch_bounds__(256) void permute_pool_kernel(PermutePoolPtrs p, in
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] += to_f32(vals[e]);
     if (nat) *reinterpret_cast<u32x4*>(nat + tile + (int64_t)s * D + ch * EPC) = raw;
-    if (tr) {
-      const int pos = vt_key_of_pos(s);  // storage position of token s
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) vt_lds[(ch * EPC + e) * VT_PITCH + pos] = vals[e];
-    }
   }
 
   if (pooled) {
@@ -83,28 +71,10 @@ __global__ __launch_bounds__(256) void permute_pool_kernel(PermutePoolPtrs p, in
     }
   }
   __syncthreads();
-  const bool center = tr && ((p.center_tr >> which) & 1);
   if (pooled) {
     for (int d = tid; d < D; d += 256) {
       const float mean = ((red[0][d] + red[1][d]) + (red[2][d] + red[3][d])) * (1.0f / kCubeTokens);
       pooled[((int64_t)(b * nh + h) * nc + c) * D + d] = mean;
-      mean_s[d] = mean;
-    }
-  }
-  if (center) __syncthreads();
-  if (tr) {
-    constexpr int VCPR = kCubeTokens / EPC;  // chunks per transposed row
-    for (int i = tid; i < D * VCPR; i += 256) {
-      const int d = i / VCPR, cc = i % VCPR;
-      u32x4 val = *reinterpret_cast<const u32x4*>(&vt_lds[d * VT_PITCH + cc * EPC]);
-      if (center) {
-        T x[EPC];
-        __builtin_memcpy(x, &val, 16);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) x[e] = from_f32<T>(to_f32(x[e]) - mean_s[d]);
-        __builtin_memcpy(&val, x, 16);
-      }
-      *reinterpret_cast<u32x4*>(tr + tile + (int64_t)d * kCubeTokens + cc * EPC) = val;
     }
   }
 }

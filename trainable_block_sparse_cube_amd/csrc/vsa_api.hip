@@ -89,7 +89,7 @@ int forward_impl(const void* q, const void* k, const void* v, const void* gc, co
   }
   const bool bf = s.dtype == VSA_BF16;
   // The fine stage reads Q in place; K and V are copied into cube tiles.
-  PermutePoolArgs pa{{{q, k, v}, {nullptr, w.kp, w.vp}, {nullptr, nullptr, nullptr}, {w.qc, w.kc, w.vc}, 0},
+  PermutePoolArgs pa{{{q, k, v}, {nullptr, w.kp, w.vp}, {w.qc, w.kc, w.vc}},
                      s.B, s.heads, s.D, s.T, s.H, s.W, bf};
   hipError_t e = launch_permute_pool(pa, st);
   if (e != hipSuccess) return VSA_ERR_HIP;
@@ -102,9 +102,9 @@ int forward_impl(const void* q, const void* k, const void* v, const void* gc, co
 }
 
 struct BwdWorkspace {
-  void *qp, *kp, *vp, *qt, *kt, *dofp, *doft;
+  void *qp, *kp, *vp, *dofp;
   float *qc, *kc, *vc, *delta, *doc, *deltac, *S, *dP, *dqc, *dkc, *dvc;
-  int32_t *tr_offs, *tr_ids;
+  int32_t *tr_offs, *tr_ids, *tr_tmp;
 };
 
 size_t bwd_ws_layout(const Shape& s, int64_t n_entries, char* base, BwdWorkspace* w) {
@@ -116,8 +116,7 @@ size_t bwd_ws_layout(const Shape& s, int64_t n_entries, char* base, BwdWorkspace
   size_t off = 0;
   auto take = [&](size_t bytes) { char* p = base ? base + off : nullptr; off += bytes; return (void*)p; };
   BwdWorkspace t;
-  t.qp = take(tile); t.kp = take(tile); t.vp = take(tile); t.qt = take(tile); t.kt = take(tile);
-  t.dofp = take(tile); t.doft = take(tile);
+  t.qp = take(tile); t.kp = take(tile); t.vp = take(tile); t.dofp = take(tile);
   t.qc = (float*)take(pooled); t.kc = (float*)take(pooled); t.vc = (float*)take(pooled);
   t.delta = (float*)take(per_tok);
   t.doc = (float*)take(pooled); t.deltac = (float*)take(per_cube);
@@ -125,6 +124,7 @@ size_t bwd_ws_layout(const Shape& s, int64_t n_entries, char* base, BwdWorkspace
   t.dqc = (float*)take(pooled); t.dkc = (float*)take(pooled); t.dvc = (float*)take(pooled);
   t.tr_offs = (int32_t*)take(align_up(((size_t)s.B * s.heads * s.nc + 1) * sizeof(int32_t)));
   t.tr_ids = (int32_t*)take(align_up((size_t)(n_entries > 0 ? n_entries : 1) * sizeof(int32_t)));
+  t.tr_tmp = (int32_t*)take(align_up((size_t)(n_entries > 0 ? n_entries : 1) * sizeof(int32_t)));
   if (w) *w = t;
   return off;
 }
@@ -142,21 +142,20 @@ int backward_impl(const void* q, const void* k, const void* v, const void* gc, c
   bwd_ws_layout(s, n_entries, (char*)ws, &w);
   Saved sv;
   saved_layout(s, (char*)const_cast<void*>(saved), &sv);
-  // K^T tiles are stored centred on their cube mean (see fine_bwd_dq).
-  PermutePoolArgs pa{{{q, k, v}, {w.qp, w.kp, w.vp}, {w.qt, w.kt, nullptr}, {w.qc, w.kc, w.vc}, 2},
+  PermutePoolArgs pa{{{q, k, v}, {w.qp, w.kp, w.vp}, {w.qc, w.kc, w.vc}},
                      s.B, s.heads, s.D, s.T, s.H, s.W, true};
   if (launch_permute_pool(pa, st) != hipSuccess) return VSA_ERR_HIP;
   BackwardArgs ba;
   ba.B = s.B; ba.heads = s.heads; ba.D = s.D; ba.T = s.T; ba.H = s.H; ba.W = s.W;
   ba.dout = dout; ba.gc = gc; ba.gf = gf;
-  ba.qp = w.qp; ba.kp = w.kp; ba.vp = w.vp; ba.qt = w.qt; ba.kt = w.kt;
+  ba.qp = w.qp; ba.kp = w.kp; ba.vp = w.vp;
   ba.qc = w.qc; ba.kc = w.kc; ba.vc = w.vc;
   ba.oc = sv.oc; ba.lse_c = sv.lse_c; ba.lse_f = sv.lse_f; ba.of = sv.of;
   ba.offs = offs; ba.ids = ids; ba.topk = topk;
-  ba.delta = w.delta; ba.dofp = w.dofp; ba.doft = w.doft;
+  ba.delta = w.delta; ba.dofp = w.dofp;
   ba.doc = w.doc; ba.deltac = w.deltac; ba.S = w.S; ba.dP = w.dP;
   ba.dqc = w.dqc; ba.dkc = w.dkc; ba.dvc = w.dvc;
-  ba.tr_offs = w.tr_offs; ba.tr_ids = w.tr_ids;
+  ba.tr_offs = w.tr_offs; ba.tr_ids = w.tr_ids; ba.tr_tmp = w.tr_tmp;
   ba.dq = dq; ba.dk = dk; ba.dv = dv; ba.dgc = dgc; ba.dgf = dgf;
   return hip_status(launch_backward(ba, st));
 }
@@ -227,7 +226,7 @@ int vsa_cube_permute_pool(const void* q, const void* k, const void* v,
   int st = check_shape(B, heads, head_dim, T, H, W, dtype, &s);
   if (st != VSA_OK) return st;
   if (!q || !k || !v || !kp || !vp || !qc || !kc || !vc) return VSA_ERR_INVALID_ARG;
-  PermutePoolArgs pa{{{q, k, v}, {qp, kp, vp}, {nullptr, nullptr, nullptr}, {qc, kc, vc}, 0},
+  PermutePoolArgs pa{{{q, k, v}, {qp, kp, vp}, {qc, kc, vc}},
                      B, heads, head_dim, T, H, W, dtype == VSA_BF16};
   return hip_status(launch_permute_pool(pa, stream));
 }

@@ -8,16 +8,11 @@
 namespace vsa {
 
 // Per tensor (q, k, v): raster source [B, N, heads, D]; optional outputs
-// natural cube-major tiles [B, heads, Nc, 64, D], transposed tiles
-// [B, heads, Nc, D, 64] (tokens in MFMA order) and fp32 means [B, heads, Nc, D].
-// center_tr bit i: tensor i's transposed tile holds x - mean(cube) instead
-// of x (mean subtracted in fp32, then rounded once).
+// cube-major tiles [B, heads, Nc, 64, D] and fp32 means [B, heads, Nc, D].
 struct PermutePoolPtrs {
   const void* src[3];
   void* nat[3];
-  void* tr[3];
   float* pooled[3];
-  int center_tr;
 };
 struct PermutePoolArgs {
   PermutePoolPtrs p;
@@ -53,24 +48,25 @@ struct FineArgs {
 };
 hipError_t launch_fine_forward(const FineArgs& a, hipStream_t st);
 
-// Backward (bf16).  Inputs: raster dout, gates; cube-major tiles from the
-// backward permute (qp, kp, vp natural; qt, kt transposed); fp32 means;
-// forward state (oc, lse_c, lse_f, of); key lists (offs null: fixed topk).
-// Scratch: delta [BH,N], dofp/doft tiles, doc [BH,Nc,D], deltac [BH,Nc],
-// S and dP [BH,Nc,Nc], dqc/dkc/dvc [BH,Nc,D], tr_offs [BH*Nc+1], tr_ids.
+// Backward (bf16).  Inputs: raster dout, gates; cube-major tiles qp, kp,
+// vp from the backward permute; fp32 means; forward state (oc, lse_c,
+// lse_f, of); key lists (offs null: fixed topk).  Scratch: delta [BH,N],
+// dofp tiles, doc [BH,Nc,D], deltac [BH,Nc], S and dP [BH,Nc,Nc],
+// dqc/dkc/dvc [BH,Nc,D], tr_offs [BH*Nc+1], tr_ids and tr_tmp (one int
+// per list entry).
 struct BackwardArgs {
   int B, heads, D, T, H, W;
   const void *dout, *gc, *gf;
-  const void *qp, *kp, *vp, *qt, *kt;
+  const void *qp, *kp, *vp;
   const float *qc, *kc, *vc;
   const float *oc, *lse_c, *lse_f, *of;
   const int32_t* offs;
   const int32_t* ids;
   int topk;
   float* delta;
-  void *dofp, *doft;
+  void* dofp;
   float *doc, *deltac, *S, *dP, *dqc, *dkc, *dvc;
-  int32_t *tr_offs, *tr_ids;
+  int32_t *tr_offs, *tr_ids, *tr_tmp;
   void *dq, *dk, *dv, *dgc, *dgf;
 };
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t st);
