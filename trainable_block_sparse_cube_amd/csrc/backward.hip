@@ -17,9 +17,10 @@
 //                   coarse backward on the means: S, dP by fp32 MFMA GEMMs,
 //                   P = exp(S - lse_c), dS = P (dP - Delta_c), then
 //                   dQc = s dS Kc, dKc = s dS^T Qc, dVc = P^T dOc
-//   transpose_lists for every key cube, the ascending list of query cubes
-//                   that selected it (counting sort, then a rank sort of
-//                   each list)
+//   transpose_scatter / transpose_rank
+//                   for every key cube, the ascending list of query cubes
+//                   that selected it (counting sort per (b, h), then a rank
+//                   sort of each list, one wave per list)
 //   fine_bwd_dkdv   key-stationary: one workgroup per key cube accumulates
 //                   dK and dV over the query cubes that selected it
 //   fine_bwd_dq     query-stationary: one workgroup per query cube
@@ -137,10 +138,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
     dsum[tid] = v * oc[((int64_t)bh * nc + c) * D + tid];
   }
   __syncthreads();
-  if (tid == 0) {
+  if (tid < 64) {  // Delta_c = dOc . Oc: one wave folds the D products
     float t = 0.f;
-    for (int d = 0; d < D; ++d) t += dsum[d];
-    deltac[(int64_t)bh * nc + c] = t;
+#pragma unroll
+    for (int d = tid; d < D; d += 64) t += dsum[d];
+    t = wave_sum(t);
+    if (tid == 0) deltac[(int64_t)bh * nc + c] = t;
   }
 }
 
@@ -230,14 +233,14 @@ __global__ __launch_bounds__(256) void coarse_softmax_grad_kernel(
 // For every (b, h) and key cube j: tr_ids[tr_offs[r] .. tr_offs[r+1]) are
 // the query cubes whose list contains j, ascending (r = (b*nh + h)*nc + j).
 // Lists: CSR (offs) or fixed length topk (offs == null).  The output of
-// (b, h) occupies the same index range as its input lists.  One workgroup
-// per (b, h): counts (LDS atomics), an exclusive scan, a scatter into `tmp`
-// in arbitrary order, then each list is sorted by rank (a query cube occurs
-// at most once per list, so ranks are distinct): one wave per list, every
-// lane counting the list's smaller entries through readlane broadcasts.
-__global__ __launch_bounds__(256) void transpose_lists_kernel(
+// (b, h) occupies the same index range as its input lists.
+//
+// transpose_scatter: one workgroup per (b, h): counts (LDS atomics), an
+// exclusive scan into tr_offs, then a scatter of the query cube ids into
+// `tmp`, each list in arbitrary order.
+__global__ __launch_bounds__(256) void transpose_scatter_kernel(
     const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk, int nc,
-    int32_t* __restrict__ tr_offs, int32_t* __restrict__ tr_ids, int32_t* __restrict__ tmp) {
+    int32_t* __restrict__ tr_offs, int32_t* __restrict__ tmp) {
   extern __shared__ int32_t cnt[];  // [nc] counts / cursors, then [nc + 1] starts
   __shared__ int32_t wsum[4];
   int32_t* start = cnt + nc;
@@ -282,21 +285,29 @@ __global__ __launch_bounds__(256) void transpose_lists_kernel(
       if (j >= 0 && j < nc) tmp[base + atomicAdd(&cnt[j], 1)] = c;
     }
   }
-  __syncthreads();
-  for (int j = wave; j < nc; j += 4) {
-    const int s0 = start[j], n = start[j + 1] - s0;
-    const int32_t* lst = tmp + base + s0;
-    for (int c0 = 0; c0 < n; c0 += 64) {
-      const int idx = c0 + lane;
-      const int v = idx < n ? lst[idx] : INT_MAX;
-      int rank = 0;
-      for (int k0 = 0; k0 < n; k0 += 64) {
-        const int u = k0 + lane < n ? lst[k0 + lane] : INT_MAX;
-        const int m = min(64, n - k0);
-        for (int i = 0; i < m; ++i) rank += __builtin_amdgcn_readlane(u, i) < v;
-      }
-      if (idx < n) tr_ids[base + s0 + rank] = v;
+}
+
+// transpose_rank: one wave per list r < n_lists, sorting it by rank (a
+// query cube occurs at most once per list, so ranks are distinct): every
+// lane counts the list's smaller entries through readlane broadcasts.
+__global__ __launch_bounds__(256) void transpose_rank_kernel(
+    const int32_t* __restrict__ tr_offs, const int32_t* __restrict__ tmp, int64_t n_lists,
+    int32_t* __restrict__ tr_ids) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= n_lists) return;
+  const int s0 = tr_offs[r], n = tr_offs[r + 1] - s0;
+  const int32_t* lst = tmp + s0;
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    const int idx = c0 + lane;
+    const int v = idx < n ? lst[idx] : INT_MAX;
+    int rank = 0;
+    for (int k0 = 0; k0 < n; k0 += 64) {
+      const int u = k0 + lane < n ? lst[k0 + lane] : INT_MAX;
+      const int m = min(64, n - k0);
+      for (int i = 0; i < m; ++i) rank += __builtin_amdgcn_readlane(u, i) < v;
     }
+    if (idx < n) tr_ids[s0 + rank] = v;
   }
 }
 
@@ -642,8 +653,11 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t st) {
   VSA_TRY((gemm<true, false>(a.dP, nc, ss, a.qc, D, sq, a.dkc, D, sq, nc, D, nc, scale, BH, st)));
   VSA_TRY((gemm<true, false>(a.S, nc, ss, a.doc, D, sq, a.dvc, D, sq, nc, D, nc, 1.0f, BH, st)));
   // transposed selection
-  transpose_lists_kernel<<<(unsigned)BH, 256, sizeof(int32_t) * (2 * nc + 1), st>>>(
-      a.offs, a.ids, a.topk, nc, a.tr_offs, a.tr_ids, a.tr_tmp);
+  transpose_scatter_kernel<<<(unsigned)BH, 256, sizeof(int32_t) * (2 * nc + 1), st>>>(
+      a.offs, a.ids, a.topk, nc, a.tr_offs, a.tr_tmp);
+  VSA_TRY(hipGetLastError());
+  const int64_t n_lists = (int64_t)BH * nc;
+  transpose_rank_kernel<<<(unsigned)((n_lists + 3) / 4), 256, 0, st>>>(a.tr_offs, a.tr_tmp, n_lists, a.tr_ids);
   VSA_TRY(hipGetLastError());
   const unsigned grid = (unsigned)(BH * nc);
   fine_bwd_dkdv_kernel<D><<<grid, 256, 0, st>>>(
