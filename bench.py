@@ -8,8 +8,12 @@ whole forward, counting the sparse FLOPs the method needs (fine stage QK^T
 and PV over the selected cubes plus the dense coarse stage).
 
 The fine kernel is also timed on its own (HIP events on the stream it is
-launched on) for the roofline entry; the fp64 CPU oracle is timed on a
-bounded sample of the same workload as the CPU baseline.  HBM traffic of the
+launched on) for the roofline entry, next to its two floors on the same
+data: the library's tile-gather helper (the fine kernel's K/V reads for the
+same selection, no arithmetic) and the fine kernel on a shared selection
+(every query cube picks the same key cubes, so every tile is an L2 hit).
+The fp64 CPU oracle is timed on a bounded sample of the same workload as the
+CPU baseline.  HBM traffic of the
 fine kernel comes from the committed profiler-counter summary
 (profiles/fine_fwd_bf16_long61k_k32_pmc.txt) and is reported only while the
 kernel source still hashes to the value recorded there.
@@ -63,7 +67,7 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain 1 GiB device copy (for scaling profiler byte counters)")
     p.add_argument("--extra", action="store_true",
-                   help="also time top-K 16, the 70400-token workload, varlen and backward")
+                   help="also time a dense reference, top-K 16, the 16K and 70400-token workloads, varlen and backward")
     return p.parse_args()
 
 
@@ -139,9 +143,18 @@ def main():
     elt = 2
     tok_bytes = w.B * w.N * w.heads * w.head_dim * elt          # one of q, k, v
     pooled_bytes = w.B * w.heads * w.n_cubes * w.head_dim * 4   # one fp32 mean tensor
-    pp_bytes = 3 * tok_bytes + 2 * tok_bytes + 3 * pooled_bytes  # read q,k,v; write K, V^T tiles + means
+    pp_bytes = 3 * tok_bytes + 2 * tok_bytes + 3 * pooled_bytes  # read q,k,v; write K, V tiles + means
     coarse_bytes = 4 * pooled_bytes + w.B * w.heads * w.n_cubes * (4 + 4 * K)
     fine_tflops = f_fine / (ms_fine * 1e-3) / 1e12
+
+    # floors of the fine kernel on the same data
+    tile_bytes = w.B * w.heads * w.n_cubes * K * 2 * 64 * w.head_dim * elt  # K and V tiles read
+    gather_ms = {d: timed(lambda: vsa.probe_tile_gather(kp, vp, sel2, K, d), a.steps, a.warmup, stream)
+                 for d in (1, 8)}
+    shared = torch.arange(K, dtype=torch.int32, device="cuda").expand(w.B, w.heads, w.n_cubes, K).contiguous()
+    ms_shared = timed(lambda: vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, w.grid, shared, topk=K, out=fout),
+                      a.steps, a.warmup, stream)
+    del shared
     res = {
         "metric": "VSA fwd effective TFLOP/s & % bf16 MFMA peak at 61440 tokens, K=32",
         "value": (f_fine + f_coarse) / (ms_step * 1e-3) / 1e12,
@@ -166,6 +179,14 @@ def main():
                      "achieved": fine_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": fine_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
                      "flops_per_launch": f_fine, "ms_per_launch": ms_fine},
+        "fine_floors": {
+            "tile_bytes_per_launch": tile_bytes,
+            "tile_delivery_TBps": tile_bytes / (ms_fine * 1e-3) / 1e12,
+            "gather_only_ms": {f"depth{d}": t for d, t in gather_ms.items()},
+            "fine_over_best_gather": ms_fine / min(gather_ms.values()),
+            "shared_selection_ms": ms_shared,
+            "shared_selection_TFLOPs": f_fine / (ms_shared * 1e-3) / 1e12,
+        },
     }
     if a.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -195,6 +216,25 @@ def extra(a, vsa, torch, stream):
         ms = timed(lambda: vsa.vsa_forward(q, k, v, gc, gf, w.grid, K), steps, warm, stream)
         fl = fine_flops(w.B, w.heads, w.N, K, w.head_dim) + coarse_flops(w.B, w.heads, w.n_cubes, w.head_dim)
         return {"ms": ms, "TFLOPs": fl / (ms * 1e-3) / 1e12}
+
+    # dense reference through the same fine kernel: every query cube lists
+    # all Nc key cubes (plain block attention over the whole clip)
+    w = WORKLOADS["long61k"]
+    inp = workload_inputs(w, with_varlen=False)
+    q, k, v, gc, gf = (dev(inp[n]) for n in ("q", "k", "v", "gc", "gf"))
+    _, kp, vp, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, w.grid, with_q_tiles=False)
+    oc, _, _ = vsa.vsa_coarse_topk(qc, kc, vc, 0)
+    nc = w.n_cubes
+    full = torch.arange(nc, dtype=torch.int32, device="cuda").expand(w.B, w.heads, nc, nc).contiguous()
+    fout = torch.empty_like(q)
+    ms_dense = timed(lambda: vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, w.grid, full, topk=nc, out=fout),
+                     2, 1, stream)
+    f_dense = fine_flops(w.B, w.heads, w.N, nc, w.head_dim)
+    ms_sparse = timed(lambda: vsa.vsa_forward(q, k, v, gc, gf, w.grid, 32), steps, warm, stream)
+    ext["long61k_dense_fine"] = {"ms": ms_dense, "TFLOPs": f_dense / (ms_dense * 1e-3) / 1e12,
+                                 "vsa_k32_forward_ms": ms_sparse,
+                                 "speedup_vsa_k32_over_dense": ms_dense / ms_sparse}
+    del full, fout, kp, vp, q, k, v, gc, gf, inp
 
     ext["long61k_k16_forward"] = fwd_case("long61k", 16)
     ext["pretrain16k_k32_forward"] = fwd_case("pretrain16k", 32)

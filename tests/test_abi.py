@@ -11,13 +11,14 @@ from trainable_block_sparse_cube_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "vsa.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "vsa_probe.h")
 
 OK, INVALID, UNSUPPORTED, WORKSPACE = (_lib.VSA_OK, _lib.VSA_ERR_INVALID_ARG,
                                        _lib.VSA_ERR_UNSUPPORTED, _lib.VSA_ERR_WORKSPACE)
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\**\s+\**([A-Za-z_][A-Za-z0-9_]*)\s*\(",
                        text, flags=re.M)
@@ -41,7 +42,9 @@ def test_header_declares_the_required_entry_points():
 
 
 def test_library_exports_every_declared_symbol(lib):
-    for name in declared_functions():
+    names = declared_functions() + declared_functions(PROBE_HEADER)
+    assert "vsa_probe_tile_gather" in names
+    for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, f"{name} missing from the Python binding"
 
@@ -114,3 +117,7 @@ def test_stage_calls_reject_bad_arguments(lib):
                                 None, FAKE, 2, _lib.VSA_BF16, FAKE, FAKE, None, None) == INVALID
     assert lib.vsa_cube_permute_pool(FAKE, FAKE, FAKE, 1, 1, 64, 8, 8, 5, _lib.VSA_BF16,
                                      FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    # measurement helper: bad depth, head_dim, topk
+    assert lib.vsa_probe_tile_gather(FAKE, FAKE, 1, 8, 128, FAKE, 2, 3, FAKE, None) == 1
+    assert lib.vsa_probe_tile_gather(FAKE, FAKE, 1, 8, 96, FAKE, 2, 1, FAKE, None) == 1
+    assert lib.vsa_probe_tile_gather(FAKE, FAKE, 1, 8, 128, FAKE, 9, 1, FAKE, None) == 1

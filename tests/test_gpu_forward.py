@@ -212,6 +212,24 @@ def test_forward_is_deterministic():
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
+def test_probe_tile_gather_runs_on_every_depth():
+    """The measurement helper (no arithmetic) accepts the forward's tiles and
+    selection at every depth and leaves the tiles untouched."""
+    vsa = _vsa()
+    grid = (8, 16, 16)
+    inp = make_inputs(1, 2, 128, grid, dtype="bf16", seed=12)
+    q, k, v = (dev(inp[n], BF16) for n in "qkv")
+    _, kp, vp, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, grid, with_q_tiles=False)
+    _, _, sel = vsa.vsa_coarse_topk(qc, kc, vc, 5)
+    kp0, vp0 = kp.clone(), vp.clone()
+    for depth in (1, 2, 4, 8):
+        vsa.probe_tile_gather(kp, vp, sel, 5, depth)
+    torch.cuda.synchronize()
+    assert torch.equal(kp, kp0) and torch.equal(vp, vp0)
+    with pytest.raises(RuntimeError):
+        vsa.probe_tile_gather(kp, vp, sel, 5, 3)
+
+
 # --------------------------------------------------------------- full sizes
 def _sampled_check(w, inp, out, sel_np, K, n_samples, rng, lists=None):
     B, nh, D = w.B, w.heads, w.head_dim

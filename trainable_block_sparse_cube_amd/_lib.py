@@ -1,5 +1,6 @@
 """ctypes view of libvsa.so: one Python callable per C entry point of
-include/vsa.h, with the same names and argument order.  Nothing here
+include/vsa.h (and the measurement helper of include/vsa_probe.h), with the
+same names and argument order.  Nothing here
 computes; it only loads the library and declares the C signatures."""
 from __future__ import annotations
 
@@ -30,6 +31,8 @@ SIGNATURES = {
     "vsa_cube_permute_pool": (_i, [_p] * 3 + [_i] * 7 + [_p] * 6 + [_p]),
     "vsa_coarse_topk": (_i, [_p] * 3 + [_i] * 5 + [_p] * 3 + [_p]),
     "vsa_fine_forward": (_i, [_p] * 6 + [_i] * 6 + [_p, _p, _i, _i, _p, _p, _p, _p]),
+    # include/vsa_probe.h
+    "vsa_probe_tile_gather": (_i, [_p, _p, _i, _i, _i, _p, _i, _i, _p, _p]),
 }
 
 _lib = None

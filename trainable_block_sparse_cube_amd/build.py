@@ -22,6 +22,7 @@ SOURCES = [
     "coarse_topk.hip",
     "fine_fwd.hip",
     "backward.hip",
+    "probe_gather.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -183,3 +183,17 @@ def vsa_fine_forward(q, kp, vp, oc, gate_c, gate_f, grid, kv_ids, topk=0, kv_off
                               _DT[q.dtype], _ptr(out), _ptr(lse), _ptr(of), _stream())
     _lib.check("vsa_fine_forward", st)
     return out, lse, of
+
+
+# ------------------------------------------------------- measurement helper
+def probe_tile_gather(kp, vp, kv_ids, topk, depth=8):
+    """include/vsa_probe.h: stream the K and V tiles the fine stage reads for
+    the fixed-length lists kv_ids [B, heads, Nc, topk], with no arithmetic
+    (the fine stage's data-movement floor).  Queued on the current stream."""
+    lib = _lib.load()
+    B, nh, nc, _, D = kp.shape
+    sink = torch.empty(4096, dtype=torch.uint8, device=kp.device)
+    st = lib.vsa_probe_tile_gather(_ptr(kp), _ptr(vp), B * nh, nc, D, _ptr(kv_ids), topk, depth,
+                                   _ptr(sink), _stream())
+    if st != 0:
+        raise RuntimeError(f"vsa_probe_tile_gather failed with status {st}")
