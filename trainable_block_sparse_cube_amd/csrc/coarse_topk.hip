@@ -210,27 +210,40 @@ __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
       for (int j = lane; j < s_pitch; j += 64) Srow[j] = 0.f;
       continue;
     }
+    // The row stays in registers: entry 64 j + lane in sv[j].
+    float sv[MAXJ];
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+      const int idx = 64 * j + lane;
+      sv[j] = (64 * j < nc && idx < nc) ? Srow[idx] : -INFINITY;
+    }
     if (topk > 0) {
       uint32_t keys[MAXJ];
 #pragma unroll
-      for (int j = 0; j < MAXJ; ++j) {
-        const int idx = 64 * j + lane;
-        keys[j] = idx < nc ? order_key(Srow[idx]) : 0u;
-      }
+      for (int j = 0; j < MAXJ; ++j) keys[j] = sv[j] == -INFINITY ? 0u : order_key(sv[j]);
       select_row<MAXJ>(keys, nc, topk, lane, cand_k + wave * kCandCap, cand_i + wave * kCandCap,
                        sel + ((int64_t)bh * nc + row) * topk);
     }
     float m = -INFINITY;
-    for (int j = lane; j < nc; j += 64) m = fmaxf(m, Srow[j]);
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) m = fmaxf(m, sv[j]);
     m = wave_max(m);
-    // exp(x) as 2^(x log2 e): one v_exp_f32 per entry.
+    // exp(x) as 2^(x log2 e): one v_exp_f32 per entry (2^-inf = 0 past the end).
     const float m2 = m * kLog2e;
     float z = 0.f;
-    for (int j = lane; j < nc; j += 64) z += __builtin_amdgcn_exp2f(fmaf(Srow[j], kLog2e, -m2));
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+      sv[j] = __builtin_amdgcn_exp2f(fmaf(sv[j], kLog2e, -m2));
+      z += sv[j];
+    }
     z = wave_sum(z);
     const float inv = 1.0f / z;
-    for (int j = lane; j < s_pitch; j += 64)
-      Srow[j] = j < nc ? __builtin_amdgcn_exp2f(fmaf(Srow[j], kLog2e, -m2)) * inv : 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+      const int idx = 64 * j + lane;
+      if (64 * j < nc && idx < nc) Srow[idx] = sv[j] * inv;
+    }
+    for (int j = nc + lane; j < s_pitch; j += 64) Srow[j] = 0.f;  // padded key block
     if (lane == 0) lse[(int64_t)bh * nc + row] = m + logf(z);
   }
   __syncthreads();
