@@ -89,16 +89,20 @@ __device__ __forceinline__ void select_row(const uint32_t (&keys)[MAXJ], int nc,
     int base = 0;
     for (int i0 = 0; i0 < ncand; i0 += 64) {
       const int i = i0 + lane;
-      bool take = false;
-      if (i < ncand) {
-        const uint32_t ki = ck[i];
-        int beaten = 0;
-        for (int c = 0; c < ncand; ++c) {
-          const uint32_t kc = ck[c];
-          beaten += (kc > ki) | ((kc == ki) & (c < i));
+      const uint32_t ki = i < ncand ? ck[i] : 0u;
+      // Count the candidates that beat candidate i: 64 at a time held one
+      // per lane, broadcast to the wave with readlane (no LDS round trip
+      // per comparison).
+      int beaten = 0;
+      for (int c0 = 0; c0 < ncand; c0 += 64) {
+        const uint32_t kl = c0 + lane < ncand ? ck[c0 + lane] : 0u;
+        const int m = min(64, ncand - c0);
+        for (int c = 0; c < m; ++c) {
+          const uint32_t kc = __builtin_amdgcn_readlane(kl, c);
+          beaten += (kc > ki) | ((kc == ki) & (c0 + c < i));
         }
-        take = beaten < topk;
       }
+      const bool take = i < ncand && beaten < topk;
       const uint64_t tm = __ballot(take);
       const int pos = base + __popcll(tm & lt_mask);
       if (take && pos < topk) out[pos] = ci[i];
