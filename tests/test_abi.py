@@ -65,6 +65,9 @@ def test_workspace_sizes(lib):
     assert sv >= 4 * (B * nh * nc * D + B * nh * nc + B * nh * N + B * nh * N * D)
     bw = lib.vsa_backward_workspace_bytes(B, nh, D, T, H, W, _lib.VSA_BF16, B * nh * nc * 32)
     assert bw > fw
+    # the coarse stage holds at most 2269 cubes (16 rows of logits in LDS)
+    assert lib.vsa_forward_workspace_bytes(1, 1, 128, 4, 4, 4 * 2269, _lib.VSA_BF16) > 0
+    assert lib.vsa_forward_workspace_bytes(1, 1, 128, 4, 8, 4 * 1135, _lib.VSA_BF16) == 0
     # invalid shapes size to 0
     assert lib.vsa_forward_workspace_bytes(B, nh, D, 6, H, W, _lib.VSA_BF16) == 0
     assert lib.vsa_forward_workspace_bytes(B, nh, 96, T, H, W, _lib.VSA_BF16) == 0
@@ -89,6 +92,9 @@ def test_forward_rejects_bad_arguments(lib):
     assert fwd(lib, null_out=True) == INVALID
     assert fwd(lib, ws=None) == INVALID
     assert fwd(lib, ws_bytes=16) == WORKSPACE
+    # B * heads is a grid dimension: at most 65535 (batch, head) pairs
+    assert lib.vsa_forward(FAKE, FAKE, FAKE, FAKE, FAKE, 256, 256, 64, 8, 8, 8, 2, _lib.VSA_BF16,
+                           FAKE, FAKE, None, FAKE, 1 << 40, None) == UNSUPPORTED
 
 
 def test_varlen_and_backward_reject_bad_arguments(lib):

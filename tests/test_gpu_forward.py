@@ -131,6 +131,28 @@ def test_coarse_stage_and_exact_ties():
     assert straddled > 0
 
 
+def test_coarse_stage_at_the_largest_cube_count():
+    """2268 cubes (grid 4x108x336), the most the coarse kernel holds (16
+    rows of logits in LDS, 40 key chunks per row): top-K 32 (pruned
+    candidates), 100 (bitwise-search fallback) and Nc, with Oc and lse."""
+    vsa = _vsa()
+    grid = (4, 108, 336)
+    log("coarse stage at 2268 cubes")
+    inp = make_inputs(1, 1, 128, grid, dtype="bf16", seed=41)
+    q, k, v = (dev(inp[n], BF16) for n in "qkv")
+    _, _, _, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, grid, with_q_tiles=False)
+    nc = qc.shape[2]
+    assert nc == 2268
+    pooled = [vo.pool(inp[n][0, :, 0].astype(np.float64), *grid) for n in "qkv"]
+    oc_ref, S, lse_ref = vo.coarse_attention(*pooled, 1.0 / np.sqrt(128))
+    for K in (32, 100, nc):
+        oc, lse, sel = vsa.vsa_coarse_topk(qc, kc, vc, K)
+        torch.cuda.synchronize()
+        check_selection(sel.cpu().numpy(), S[None, None], K)
+    assert_close(host64(oc)[0, 0], oc_ref, F32, "oc")
+    np.testing.assert_allclose(host64(lse)[0, 0], lse_ref, atol=1e-5)
+
+
 def test_coarse_topk_zero_skips_selection():
     vsa = _vsa()
     inp = make_inputs(1, 1, 64, (4, 8, 8), dtype="f32", seed=2)
