@@ -235,32 +235,15 @@ __global__ __launch_bounds__(256) void coarse_softmax_grad_kernel(
 // Lists: CSR (offs) or fixed length topk (offs == null).  The output of
 // (b, h) occupies the same index range as its input lists.
 //
-// transpose_scatter: one workgroup per (b, h): counts (LDS atomics), an
-// exclusive scan into tr_offs, then a scatter of the query cube ids into
-// `tmp`, each list in arbitrary order.
-__global__ __launch_bounds__(256) void transpose_scatter_kernel(
-    const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk, int nc,
-    int32_t* __restrict__ tr_offs, int32_t* __restrict__ tmp) {
-  extern __shared__ int32_t cnt[];  // [nc] counts / cursors, then [nc + 1] starts
-  __shared__ int32_t wsum[4];
-  int32_t* start = cnt + nc;
-  const int bh = blockIdx.x;
+// Exclusive prefix sum of in[0..n) into out[0..n] (out[n] = total) by the
+// 256 threads of a workgroup: thread t owns in[t L .. t L + L).  Ends with
+// a barrier.
+__device__ void block_exclusive_scan(const int32_t* in, int n, int32_t* out, int32_t* wsum) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int64_t r0 = (int64_t)bh * nc;
-  const int base = offs ? offs[r0] : (int)(r0 * topk);
-  const int total = (offs ? offs[r0 + nc] : (int)((r0 + nc) * topk)) - base;
-  for (int j = tid; j < nc; j += 256) cnt[j] = 0;
-  __syncthreads();
-  for (int e = tid; e < total; e += 256) {
-    const int j = ids[base + e];
-    if (j >= 0 && j < nc) atomicAdd(&cnt[j], 1);
-  }
-  __syncthreads();
-  // exclusive scan: thread t owns counts [t L, t L + L)
-  const int L = (nc + 255) / 256;
-  const int lo = min(tid * L, nc), hi = min(lo + L, nc);
+  const int L = (n + 255) / 256;
+  const int lo = min(tid * L, n), hi = min(lo + L, n);
   int own = 0;
-  for (int j = lo; j < hi; ++j) own += cnt[j];
+  for (int j = lo; j < hi; ++j) own += in[j];
   int incl = own;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -271,10 +254,56 @@ __global__ __launch_bounds__(256) void transpose_scatter_kernel(
   __syncthreads();
   int run = incl - own;
   for (int w = 0; w < wave; ++w) run += wsum[w];
-  for (int j = lo; j < hi; ++j) { start[j] = run; run += cnt[j]; }
-  if (tid == 255) start[nc] = run;
+  for (int j = lo; j < hi; ++j) { out[j] = run; run += in[j]; }
+  if (tid == 255) out[n] = run;
   __syncthreads();
+}
+
+// transpose_scatter: one workgroup per (b, h): counts (LDS atomics), an
+// exclusive scan into tr_offs, then a scatter of the query cube ids into
+// `tmp`, each list in arbitrary order.  It also writes tr_order, the key
+// cubes of (b, h) by list length, longest first: the dK/dV kernel takes
+// them in that order, so that the longest lists start first and the
+// workgroups running together have lists of similar length (their sweeps
+// over the query cubes stay in step, which helps L2 reuse).  The order
+// among equal lengths is arbitrary; results do not depend on it.
+__global__ __launch_bounds__(256) void transpose_scatter_kernel(
+    const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk, int nc,
+    int32_t* __restrict__ tr_offs, int32_t* __restrict__ tr_order, int32_t* __restrict__ tmp) {
+  // LDS: cnt [nc] (counts, then cursors), start [nc + 1], hist [nc + 1],
+  // hpos [nc + 2]
+  extern __shared__ int32_t cnt[];
+  __shared__ int32_t wsum[4];
+  int32_t* start = cnt + nc;
+  int32_t* hist = start + nc + 1;
+  int32_t* hpos = hist + nc + 1;
+  const int bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t r0 = (int64_t)bh * nc;
+  const int base = offs ? offs[r0] : (int)(r0 * topk);
+  const int total = (offs ? offs[r0 + nc] : (int)((r0 + nc) * topk)) - base;
+  for (int j = tid; j < nc; j += 256) cnt[j] = 0;
+  for (int v = tid; v <= nc; v += 256) hist[v] = 0;
+  __syncthreads();
+  for (int e = tid; e < total; e += 256) {
+    const int j = ids[base + e];
+    if (j >= 0 && j < nc) atomicAdd(&cnt[j], 1);
+  }
+  __syncthreads();
+  block_exclusive_scan(cnt, nc, start, wsum);
   for (int j = tid; j <= nc; j += 256) tr_offs[r0 + j] = base + start[j];
+  // key cubes by list length, longest first (a query cube picks a key cube
+  // at most once, so lengths are at most nc)
+  for (int j = tid; j < nc; j += 256) atomicAdd(&hist[min(cnt[j], nc)], 1);
+  __syncthreads();
+  block_exclusive_scan(hist, nc + 1, hpos, wsum);
+  for (int v = tid; v <= nc; v += 256) hist[v] = 0;  // cursors per length
+  __syncthreads();
+  for (int j = tid; j < nc; j += 256) {
+    const int v = min(cnt[j], nc);
+    tr_order[r0 + (nc - hpos[v + 1]) + atomicAdd(&hist[v], 1)] = j;
+  }
+  __syncthreads();
   for (int j = tid; j < nc; j += 256) cnt[j] = start[j];  // fill cursors
   __syncthreads();
   for (int c = tid; c < nc; c += 256) {
@@ -326,8 +355,8 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(
     const bf16* __restrict__ qp, const bf16* __restrict__ kp, const bf16* __restrict__ vp,
     const bf16* __restrict__ dofp, const float* __restrict__ lse_f, const float* __restrict__ delta,
-    const int32_t* __restrict__ tr_offs, const int32_t* __restrict__ tr_ids,
-    const float* __restrict__ dkc, const float* __restrict__ dvc,
+    const int32_t* __restrict__ tr_offs, const int32_t* __restrict__ tr_order,
+    const int32_t* __restrict__ tr_ids, const float* __restrict__ dkc, const float* __restrict__ dvc,
     int nh, int nc, int Hg, int Wg, float scale,
     bf16* __restrict__ dk, bf16* __restrict__ dv) {
   constexpr int KS = D / 16, MD = D / 32, TILE_CH = 64 * D / 8;
@@ -344,10 +373,11 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ql = lane & 31, hf = lane >> 5;
   const int kh = wave & 1, qh = wave >> 1;
-  const int blk = blockIdx.x;  // (b*nh + h)*nc + key cube
-  const int bh = blk / nc, j = blk - bh * nc;
+  const int blk = blockIdx.x;  // (b*nh + h)*nc + rank of the key cube by list length
+  const int bh = blk / nc;
   const int64_t N = (int64_t)nc * 64;
   const int64_t bh_tiles = (int64_t)bh * nc;
+  const int j = tr_order[blk];
   const float scale_log2 = scale * kLog2e;
 
   // K and V rows of this wave's keys as B operands: lane (key, hf) holds
@@ -368,7 +398,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(
     for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
 
   const uint32_t tr_lo = tr_offset<D>(lane, 0), tr_hi = tr_offset<D>(lane, 1);
-  const int e0 = tr_offs[blk], n = tr_offs[blk + 1] - e0;
+  const int e0 = tr_offs[bh_tiles + j], n = tr_offs[bh_tiles + j + 1] - e0;
   auto copy_tile = [&](int c, int buf) {
     const int64_t t = (bh_tiles + c) * 64;
     dma_tile<D>(qp + t * D, buf ? q_lds1 : q_lds0, wave, lane);
@@ -653,8 +683,8 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t st) {
   VSA_TRY((gemm<true, false>(a.dP, nc, ss, a.qc, D, sq, a.dkc, D, sq, nc, D, nc, scale, BH, st)));
   VSA_TRY((gemm<true, false>(a.S, nc, ss, a.doc, D, sq, a.dvc, D, sq, nc, D, nc, 1.0f, BH, st)));
   // transposed selection
-  transpose_scatter_kernel<<<(unsigned)BH, 256, sizeof(int32_t) * (2 * nc + 1), st>>>(
-      a.offs, a.ids, a.topk, nc, a.tr_offs, a.tr_tmp);
+  transpose_scatter_kernel<<<(unsigned)BH, 256, sizeof(int32_t) * (4 * nc + 4), st>>>(
+      a.offs, a.ids, a.topk, nc, a.tr_offs, a.tr_order, a.tr_tmp);
   VSA_TRY(hipGetLastError());
   const int64_t n_lists = (int64_t)BH * nc;
   transpose_rank_kernel<<<(unsigned)((n_lists + 3) / 4), 256, 0, st>>>(a.tr_offs, a.tr_tmp, n_lists, a.tr_ids);
@@ -662,8 +692,8 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)(BH * nc);
   fine_bwd_dkdv_kernel<D><<<grid, 256, 0, st>>>(
       (const bf16*)a.qp, (const bf16*)a.kp, (const bf16*)a.vp, (const bf16*)a.dofp,
-      a.lse_f, a.delta, a.tr_offs, a.tr_ids, a.dkc, a.dvc, a.heads, nc, a.H, a.W, scale,
-      (bf16*)a.dk, (bf16*)a.dv);
+      a.lse_f, a.delta, a.tr_offs, a.tr_order, a.tr_ids, a.dkc, a.dvc, a.heads, nc, a.H, a.W,
+      scale, (bf16*)a.dk, (bf16*)a.dv);
   VSA_TRY(hipGetLastError());
   fine_bwd_dq_kernel<D><<<grid, 256, 0, st>>>(
       (const bf16*)a.qp, (const bf16*)a.kp, (const bf16*)a.vp, (const bf16*)a.dofp,

@@ -104,7 +104,7 @@ int forward_impl(const void* q, const void* k, const void* v, const void* gc, co
 struct BwdWorkspace {
   void *qp, *kp, *vp, *dofp;
   float *qc, *kc, *vc, *delta, *doc, *deltac, *S, *dP, *dqc, *dkc, *dvc;
-  int32_t *tr_offs, *tr_ids, *tr_tmp;
+  int32_t *tr_offs, *tr_order, *tr_ids, *tr_tmp;
 };
 
 size_t bwd_ws_layout(const Shape& s, int64_t n_entries, char* base, BwdWorkspace* w) {
@@ -123,6 +123,7 @@ size_t bwd_ws_layout(const Shape& s, int64_t n_entries, char* base, BwdWorkspace
   t.S = (float*)take(sq); t.dP = (float*)take(sq);
   t.dqc = (float*)take(pooled); t.dkc = (float*)take(pooled); t.dvc = (float*)take(pooled);
   t.tr_offs = (int32_t*)take(align_up(((size_t)s.B * s.heads * s.nc + 1) * sizeof(int32_t)));
+  t.tr_order = (int32_t*)take(align_up((size_t)s.B * s.heads * s.nc * sizeof(int32_t)));
   t.tr_ids = (int32_t*)take(align_up((size_t)(n_entries > 0 ? n_entries : 1) * sizeof(int32_t)));
   t.tr_tmp = (int32_t*)take(align_up((size_t)(n_entries > 0 ? n_entries : 1) * sizeof(int32_t)));
   if (w) *w = t;
@@ -155,7 +156,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* gc, c
   ba.delta = w.delta; ba.dofp = w.dofp;
   ba.doc = w.doc; ba.deltac = w.deltac; ba.S = w.S; ba.dP = w.dP;
   ba.dqc = w.dqc; ba.dkc = w.dkc; ba.dvc = w.dvc;
-  ba.tr_offs = w.tr_offs; ba.tr_ids = w.tr_ids; ba.tr_tmp = w.tr_tmp;
+  ba.tr_offs = w.tr_offs; ba.tr_order = w.tr_order; ba.tr_ids = w.tr_ids; ba.tr_tmp = w.tr_tmp;
   ba.dq = dq; ba.dk = dk; ba.dv = dv; ba.dgc = dgc; ba.dgf = dgf;
   return hip_status(launch_backward(ba, st));
 }

@@ -52,8 +52,8 @@ hipError_t launch_fine_forward(const FineArgs& a, hipStream_t st);
 // vp from the backward permute; fp32 means; forward state (oc, lse_c,
 // lse_f, of); key lists (offs null: fixed topk).  Scratch: delta [BH,N],
 // dofp tiles, doc [BH,Nc,D], deltac [BH,Nc], S and dP [BH,Nc,Nc],
-// dqc/dkc/dvc [BH,Nc,D], tr_offs [BH*Nc+1], tr_ids and tr_tmp (one int
-// per list entry).
+// dqc/dkc/dvc [BH,Nc,D], tr_offs [BH*Nc+1], tr_order [BH*Nc], tr_ids and
+// tr_tmp (one int per list entry).
 struct BackwardArgs {
   int B, heads, D, T, H, W;
   const void *dout, *gc, *gf;
@@ -66,7 +66,7 @@ struct BackwardArgs {
   float* delta;
   void* dofp;
   float *doc, *deltac, *S, *dP, *dqc, *dkc, *dvc;
-  int32_t *tr_offs, *tr_ids, *tr_tmp;
+  int32_t *tr_offs, *tr_order, *tr_ids, *tr_tmp;
   void *dq, *dk, *dv, *dgc, *dgf;
 };
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t st);
