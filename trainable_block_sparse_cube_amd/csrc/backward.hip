@@ -152,14 +152,18 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 // C[z] = alpha * op(A[z]) * op(B[z]) for z < batch, fp32, row-major.
 // op(A) is M x K (TA: A stored K x M); op(B) is K x N (TB: B stored N x K).
-// 64 x 64 output tile per workgroup, 16-deep K chunks staged in LDS,
-// v_mfma_f32_16x16x4f32; each wave owns a 32 x 32 quarter.
+// 64 x 64 output tile per workgroup, v_mfma_f32_16x16x4f32, each wave owns a
+// 32 x 32 quarter.  K runs in 32-deep chunks staged through LDS; the next
+// chunk's loads (8 + 8 floats per thread, consecutive threads on the
+// contiguous dimension of each operand) are issued before the current chunk
+// is multiplied, so their latency overlaps the MFMAs.
 template <bool TA, bool TB>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(
     const float* __restrict__ A, int lda, int64_t sA, const float* __restrict__ B, int ldb, int64_t sB,
     float* __restrict__ C, int ldc, int64_t sC, int M, int N, int K, float alpha) {
-  __shared__ float As[16][64 + 4];
-  __shared__ float Bs[16][64 + 4];
+  constexpr int KC = 32;
+  __shared__ float As[KC][64 + 4];
+  __shared__ float Bs[KC][64 + 4];
   const int z = blockIdx.z;
   A += z * sA; B += z * sB; C += z * sC;
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
@@ -171,21 +175,44 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4v{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    __syncthreads();
-    for (int i = tid; i < 16 * 64; i += 256) {
-      int kk, mm;
-      if (TA) { kk = i / 64; mm = i % 64; } else { mm = i / 16; kk = i % 16; }
+
+  // element e of this thread's share of a chunk: (k, m) of A and (k, n) of B
+  auto a_km = [&](int e, int& kk, int& mm) {
+    const int i = tid + 256 * e;
+    if (TA) { kk = i / 64; mm = i % 64; } else { mm = i / KC; kk = i % KC; }
+  };
+  auto b_kn = [&](int e, int& kk, int& nn) {
+    const int i = tid + 256 * e;
+    if (TB) { nn = i / KC; kk = i % KC; } else { kk = i / 64; nn = i % 64; }
+  };
+  float ra[8], rb[8];
+  auto load_chunk = [&](int k0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int kk, mm, nn, kb;
+      a_km(e, kk, mm);
       const int gm = m0 + mm, gk = k0 + kk;
-      As[kk][mm] = (gm < M && gk < K) ? (TA ? A[(int64_t)gk * lda + gm] : A[(int64_t)gm * lda + gk]) : 0.f;
-      int nn;
-      if (TB) { nn = i / 16; kk = i % 16; } else { kk = i / 64; nn = i % 64; }
-      const int gn = n0 + nn; const int gk2 = k0 + kk;
-      Bs[kk][nn] = (gn < N && gk2 < K) ? (TB ? B[(int64_t)gn * ldb + gk2] : B[(int64_t)gk2 * ldb + gn]) : 0.f;
+      ra[e] = (gm < M && gk < K) ? (TA ? A[(int64_t)gk * lda + gm] : A[(int64_t)gm * lda + gk]) : 0.f;
+      b_kn(e, kb, nn);
+      const int gn = n0 + nn, gk2 = k0 + kb;
+      rb[e] = (gn < N && gk2 < K) ? (TB ? B[(int64_t)gn * ldb + gk2] : B[(int64_t)gk2 * ldb + gn]) : 0.f;
+    }
+  };
+  load_chunk(0);
+  for (int k0 = 0; k0 < K; k0 += KC) {
+    __syncthreads();  // the previous chunk's reads are done
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int kk, mm, nn, kb;
+      a_km(e, kk, mm);
+      As[kk][mm] = ra[e];
+      b_kn(e, kb, nn);
+      Bs[kb][nn] = rb[e];
     }
     __syncthreads();
+    if (k0 + KC < K) load_chunk(k0 + KC);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < KC / 4; ++t) {
       const int kk = 4 * t + lg;
       float a[2], bb[2];
 #pragma unroll
