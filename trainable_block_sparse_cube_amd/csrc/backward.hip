@@ -617,8 +617,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(
     // K^T operands (m = d, k = keys), read while the MFMAs above run
     const uint32_t kbase = lds_addr(kb);
     bf16x8 ta[MD][2];
-#pragma unroll
-    for (int m = 0; m < MD; ++m) tile_tr8_asm<D, 2>(ta[m], (kbase + tr_lo) ^ (m << 6), (kbase + tr_hi) ^ (m << 6));
+    tile_tr8_asm_cols<D, MD>(ta, kbase + tr_lo, kbase + tr_hi);
     // this lane: query column ql, key rows 32kh + 8(r/4) + 4hf + r%4
     bf16x8 hiB[2], loB[2];
 #pragma unroll

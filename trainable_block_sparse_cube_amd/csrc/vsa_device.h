@@ -200,4 +200,66 @@ __device__ __forceinline__ void tile_tr8_asm(bf16x8 (&o)[NS], uint32_t lo, uint3
   for (int s = 0; s < NS; ++s) o[s] = join_tr(r[2 * s], r[2 * s + 1]);
 }
 
+// Two 16-row groups for NM column blocks (block m at address ^ (m << 6)),
+// all reads in one asm statement with one wait.
+template <int D, int NM>
+__device__ __forceinline__ void tile_tr8_asm_cols(bf16x8 (&o)[NM][2], uint32_t lo, uint32_t hi) {
+  constexpr int G = 16 * D * 2;
+  if constexpr (NM == 2) {
+    u32x2 r[8];
+    const uint32_t lo1 = lo ^ 64u, hi1 = hi ^ 64u;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %4, %10\n\t"
+        "ds_read_b64_tr_b16 %5, %11\n\t"
+        "ds_read_b64_tr_b16 %6, %10 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:%12\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]),
+          "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(lo), "v"(hi), "v"(lo1), "v"(hi1), "i"(G)
+        : "memory");
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) o[m][s] = join_tr(r[4 * m + 2 * s], r[4 * m + 2 * s + 1]);
+  } else {
+    static_assert(NM == 4, "2 or 4 column blocks");
+    u32x2 r[16];
+    const uint32_t lo1 = lo ^ 64u, hi1 = hi ^ 64u, lo2 = lo ^ 128u, hi2 = hi ^ 128u;
+    const uint32_t lo3 = lo ^ 192u, hi3 = hi ^ 192u;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16\n\t"
+        "ds_read_b64_tr_b16 %1, %17\n\t"
+        "ds_read_b64_tr_b16 %2, %16 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %3, %17 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %4, %18\n\t"
+        "ds_read_b64_tr_b16 %5, %19\n\t"
+        "ds_read_b64_tr_b16 %6, %18 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %7, %19 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %8, %20\n\t"
+        "ds_read_b64_tr_b16 %9, %21\n\t"
+        "ds_read_b64_tr_b16 %10, %20 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %11, %21 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %12, %22\n\t"
+        "ds_read_b64_tr_b16 %13, %23\n\t"
+        "ds_read_b64_tr_b16 %14, %22 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %15, %23 offset:%24\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]),
+          "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+          "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
+          "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+        : "v"(lo), "v"(hi), "v"(lo1), "v"(hi1), "v"(lo2), "v"(hi2), "v"(lo3), "v"(hi3), "i"(G)
+        : "memory");
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) o[m][s] = join_tr(r[4 * m + 2 * s], r[4 * m + 2 * s + 1]);
+  }
+}
+
 }  // namespace vsa
