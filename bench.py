@@ -236,6 +236,27 @@ def extra(a, vsa, torch, stream):
                                  "speedup_vsa_k32_over_dense": ms_dense / ms_sparse}
     del full, fout, kp, vp, q, k, v, gc, gf, inp
 
+    # the headline shape with spatially smooth cube means (neighbouring query
+    # cubes select overlapping key cubes, as in video); context, not the metric
+    w = WORKLOADS["long61k_smooth"]
+    inp = workload_inputs(w, with_varlen=False)
+    q, k, v, gc, gf = (dev(inp[n]) for n in ("q", "k", "v", "gc", "gf"))
+    _, kp, vp, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, w.grid, with_q_tiles=False)
+    oc, _, sel = vsa.vsa_coarse_topk(qc, kc, vc, 32)
+    fout = torch.empty_like(q)
+    ms_fine_s = timed(lambda: vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, w.grid, sel, topk=32, out=fout),
+                      steps, warm, stream)
+    ms_fwd_s = timed(lambda: vsa.vsa_forward(q, k, v, gc, gf, w.grid, 32), steps, warm, stream)
+    s_np = sel[0, 0].cpu().numpy()
+    f_s = fine_flops(w.B, w.heads, w.N, 32, w.head_dim)
+    ext["long61k_smooth_k32"] = {
+        "forward_ms": ms_fwd_s,
+        "forward_TFLOPs": (f_s + coarse_flops(w.B, w.heads, w.n_cubes, w.head_dim)) / (ms_fwd_s * 1e-3) / 1e12,
+        "fine_ms": ms_fine_s, "fine_TFLOPs": f_s / (ms_fine_s * 1e-3) / 1e12,
+        "mean_shared_ids_with_next_cube": float(sum(len(set(s_np[c]) & set(s_np[c + 1]))
+                                                   for c in range(len(s_np) - 1)) / (len(s_np) - 1))}
+    del q, k, v, gc, gf, kp, vp, fout, inp
+
     ext["long61k_k16_forward"] = fwd_case("long61k", 16)
     ext["pretrain16k_k32_forward"] = fwd_case("pretrain16k", 32)
     ext["large70k_k32_forward"] = fwd_case("large70k", 32)

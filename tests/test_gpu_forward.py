@@ -272,7 +272,7 @@ def _sampled_check(w, inp, out, sel_np, K, n_samples, rng, lists=None):
 
 
 @pytest.mark.parametrize("name,K", [("pretrain16k", 32), ("long61k", 16), ("long61k", 32),
-                                    ("large70k", 32), ("train16k", 32)])
+                                    ("large70k", 32), ("train16k", 32), ("long61k_smooth", 32)])
 def test_forward_full_size_sampled(name, K):
     vsa = _vsa()
     w = WORKLOADS[name]

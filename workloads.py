@@ -18,6 +18,14 @@ Distribution (one recipe for every workload):
   * bf16 workloads round the fp32 draws once, round-to-nearest-even; both the
     GPU path and the oracle consume those exact rounded values.
 
+A second structure ("smooth", used only by the long61k_smooth extra): the
+per-cube means vary smoothly over the cube grid instead of independently, a
+stand-in for video, where neighbouring cubes look alike and so select
+overlapping key cubes.  Per (batch, head, tensor) an N(0, 1) field over the
+(T/4, H/4, W/4) cube grid and head_dim is box-filtered (3 taps, periodic)
+SMOOTH_PASSES times along each grid axis and rescaled to unit standard
+deviation over the whole draw; tokens add N(0, 0.5^2) noise as before.
+
 Token order is raster: token (t, y, x) of a T x H x W grid sits at flat index
 (t*H + y)*W + x, and tensors are [B, N, heads, head_dim] / [B, N, heads].
 """
@@ -41,6 +49,7 @@ class Workload:
     seed: int
     varlen: Optional[tuple] = None  # (lo, hi) for per-query-cube list lengths
     backward: bool = False
+    structure: str = "blocks"  # "blocks" (independent cube means) or "smooth"
 
     @property
     def N(self) -> int:
@@ -61,7 +70,12 @@ WORKLOADS = {
                          varlen=(8, 64)),
     "train16k": Workload("train16k", 2, 12, 128, (16, 32, 32), (32,), "bf16", 1004,
                          backward=True),
+    # not one of the five: the headline shape with spatially smooth cube means
+    "long61k_smooth": Workload("long61k_smooth", 1, 12, 128, (20, 48, 64), (32,), "bf16", 1005,
+                               structure="smooth"),
 }
+
+SMOOTH_PASSES = 4
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
@@ -89,12 +103,27 @@ def _blockwise_mean_plus_noise(rng, B, T, H, W, heads, D, noise_std):
     return (full + np.float32(noise_std) * noise).astype(np.float32)
 
 
+def _smooth_mean_plus_noise(rng, B, T, H, W, heads, D, noise_std):
+    """[B, T*H*W, heads, D]: a smooth field of cube means + token noise."""
+    f = rng.standard_normal((B, T // 4, H // 4, W // 4, heads, D), dtype=np.float32)
+    for axis in (1, 2, 3):
+        for _ in range(SMOOTH_PASSES):
+            f = (f + np.roll(f, 1, axis=axis) + np.roll(f, -1, axis=axis)) / np.float32(3.0)
+    f = (f / f.std()).astype(np.float32)
+    full = np.broadcast_to(
+        f[:, :, None, :, None, :, None, :, :],
+        (B, T // 4, 4, H // 4, 4, W // 4, 4, heads, D),
+    ).reshape(B, T * H * W, heads, D)
+    noise = rng.standard_normal((B, T * H * W, heads, D), dtype=np.float32)
+    return (full + np.float32(noise_std) * noise).astype(np.float32)
+
+
 def _sigmoid(x):
     return (1.0 / (1.0 + np.exp(-x.astype(np.float64)))).astype(np.float32)
 
 
 def make_inputs(B, heads, D, grid, dtype="bf16", seed=0, with_dout=False,
-                varlen=None):
+                varlen=None, structure="blocks"):
     """Draw one seeded input set.
 
     Returns a dict of fp32 numpy arrays (bf16-exact when dtype == "bf16"):
@@ -107,8 +136,9 @@ def make_inputs(B, heads, D, grid, dtype="bf16", seed=0, with_dout=False,
         raise ValueError("grid dimensions must be multiples of 4")
     rng = np.random.default_rng(seed)
     out = {}
+    draw = {"blocks": _blockwise_mean_plus_noise, "smooth": _smooth_mean_plus_noise}[structure]
     for name in ("q", "k", "v"):
-        out[name] = _blockwise_mean_plus_noise(rng, B, T, H, W, heads, D, 0.5)
+        out[name] = draw(rng, B, T, H, W, heads, D, 0.5)
     N = T * H * W
     out["gc"] = _sigmoid(rng.standard_normal((B, N, heads), dtype=np.float32))
     out["gf"] = _sigmoid(rng.standard_normal((B, N, heads), dtype=np.float32))
@@ -139,7 +169,8 @@ def workload_inputs(w: Workload, seed=None, with_varlen=True):
     return make_inputs(w.B, w.heads, w.head_dim, w.grid, w.dtype,
                        w.seed if seed is None else seed,
                        with_dout=w.backward,
-                       varlen=w.varlen if with_varlen else None)
+                       varlen=w.varlen if with_varlen else None,
+                       structure=w.structure)
 
 
 def fine_flops(B, heads, N, topk, D):
