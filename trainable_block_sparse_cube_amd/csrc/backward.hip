@@ -542,7 +542,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(
     const bf16* __restrict__ dofp, const float* __restrict__ lse_f, const float* __restrict__ delta,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk,
     const float* __restrict__ dqc, const float* __restrict__ kc_mean,
-    int nh, int nc, int Hg, int Wg, float scale, bf16* __restrict__ dq) {
+    int nh, int nc, int Hg, int Wg, float scale, int n_logical, bf16* __restrict__ dq) {
   constexpr int KS = D / 16, MD = D / 32, TILE_CH = 64 * D / 8;
   __shared__ __align__(256) u32x4 k_lds0[TILE_CH];
   __shared__ __align__(256) u32x4 k_lds1[TILE_CH];
@@ -552,7 +552,12 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ql = lane & 31, hf = lane >> 5;
   const int kh = wave & 1, qh = wave >> 1;
-  const int blk = blockIdx.x;  // (b*nh + h)*nc + query cube
+  // Logical block (b*nh + h)*nc + query cube, XCD-contiguous as in the
+  // forward fine kernel (hardware block i runs on XCD i % 8); the grid is
+  // padded to a multiple of 8.
+  const int per = (n_logical + 7) >> 3;
+  const int blk = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  if (blk >= n_logical) return;
   const int bh = blk / nc, c = blk - bh * nc;
   const int64_t N = (int64_t)nc * 64;
   const int64_t bh_tiles = (int64_t)bh * nc;
@@ -721,10 +726,10 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t st) {
       a.lse_f, a.delta, a.tr_offs, a.tr_order, a.tr_ids, a.dkc, a.dvc, a.heads, nc, a.H, a.W,
       scale, (bf16*)a.dk, (bf16*)a.dv);
   VSA_TRY(hipGetLastError());
-  fine_bwd_dq_kernel<D><<<grid, 256, 0, st>>>(
+  fine_bwd_dq_kernel<D><<<((grid + 7u) / 8u) * 8u, 256, 0, st>>>(
       (const bf16*)a.qp, (const bf16*)a.kp, (const bf16*)a.vp, (const bf16*)a.dofp,
       a.lse_f, a.delta, a.offs, a.ids, a.topk, a.dqc, a.kc, a.heads, nc, a.H, a.W, scale,
-      (bf16*)a.dq);
+      (int)grid, (bf16*)a.dq);
   VSA_TRY(hipGetLastError());
 #undef VSA_TRY
   return hipSuccess;
