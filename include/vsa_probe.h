@@ -8,8 +8,10 @@
  * K and V operands, and does nothing else: one workgroup per (b, h, query
  * cube) streams the K and V tiles (64 x head_dim bf16 each, cube-major, as
  * written by vsa_cube_permute_pool) of the cube's `topk` selected key cubes
- * and folds them with XOR.  `depth` tiles are in flight per workgroup.  Its
- * time is the data-movement floor of the fine stage for that selection.
+ * and folds them with XOR.  `depth` tiles are in flight per workgroup, and
+ * workgroups are numbered as in the fine kernel (block i on XCD i % 8 takes
+ * a contiguous range of query cubes).  Its time is the data-movement floor
+ * of the fine stage for that selection.
  *
  * kp, vp: [BH, Nc, 64, head_dim] bf16 (device); ids: [BH, Nc, topk] int32
  * (device, each in [0, Nc), not checked on the GPU); sink: device buffer of

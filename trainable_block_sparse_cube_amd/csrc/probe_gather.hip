@@ -13,9 +13,12 @@ namespace {
 template <int CPT, int DEPTH>
 __global__ __launch_bounds__(256) void tile_gather_kernel(
     const u32x4* __restrict__ kp, const u32x4* __restrict__ vp, int nc,
-    const int32_t* __restrict__ ids, int topk, u32x4* __restrict__ sink) {
+    const int32_t* __restrict__ ids, int topk, int n_logical, u32x4* __restrict__ sink) {
   constexpr int TILE = 256 * CPT;
-  const int64_t blk = blockIdx.x;  // bh * nc + query cube
+  // bh * nc + query cube, numbered XCD-contiguously as in the fine kernel
+  const int per = (n_logical + 7) >> 3;
+  const int64_t blk = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (blk >= n_logical) return;
   const int64_t bh_tiles = (blk / nc) * nc;
   const int32_t* list = ids + blk * topk;
   u32x4 acc = {0u, 0u, 0u, 0u};
@@ -46,15 +49,16 @@ __global__ __launch_bounds__(256) void tile_gather_kernel(
 template <int CPT>
 hipError_t launch(const void* kp, const void* vp, int BH, int nc, const int32_t* ids, int topk,
                   int depth, void* sink, hipStream_t st) {
-  const unsigned grid = (unsigned)((int64_t)BH * nc);
+  const int n_logical = (int)((int64_t)BH * nc);
+  const unsigned grid = ((unsigned)n_logical + 7u) / 8u * 8u;
   const u32x4* k = (const u32x4*)kp;
   const u32x4* v = (const u32x4*)vp;
   u32x4* s = (u32x4*)sink;
   switch (depth) {
-    case 1: tile_gather_kernel<CPT, 1><<<grid, 256, 0, st>>>(k, v, nc, ids, topk, s); break;
-    case 2: tile_gather_kernel<CPT, 2><<<grid, 256, 0, st>>>(k, v, nc, ids, topk, s); break;
-    case 4: tile_gather_kernel<CPT, 4><<<grid, 256, 0, st>>>(k, v, nc, ids, topk, s); break;
-    default: tile_gather_kernel<CPT, 8><<<grid, 256, 0, st>>>(k, v, nc, ids, topk, s); break;
+    case 1: tile_gather_kernel<CPT, 1><<<grid, 256, 0, st>>>(k, v, nc, ids, topk, n_logical, s); break;
+    case 2: tile_gather_kernel<CPT, 2><<<grid, 256, 0, st>>>(k, v, nc, ids, topk, n_logical, s); break;
+    case 4: tile_gather_kernel<CPT, 4><<<grid, 256, 0, st>>>(k, v, nc, ids, topk, n_logical, s); break;
+    default: tile_gather_kernel<CPT, 8><<<grid, 256, 0, st>>>(k, v, nc, ids, topk, n_logical, s); break;
   }
   return hipGetLastError();
 }
