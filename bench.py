@@ -130,10 +130,10 @@ def main():
 
     # stages on their own, same stream
     _, kp, vp, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, w.grid, with_q_tiles=False)
-    oc, lse, sel2 = vsa.vsa_coarse_topk(qc, kc, vc, K)
+    oc, lse, sel2 = vsa.vsa_coarse_topk(qc, kc, vc, K, input_dtype=torch.bfloat16)
     ms_pp = timed(lambda: vsa.vsa_cube_permute_pool(q, k, v, w.grid, with_q_tiles=False),
                   a.steps, a.warmup, stream)
-    ms_coarse = timed(lambda: vsa.vsa_coarse_topk(qc, kc, vc, K), a.steps, a.warmup, stream)
+    ms_coarse = timed(lambda: vsa.vsa_coarse_topk(qc, kc, vc, K, input_dtype=torch.bfloat16), a.steps, a.warmup, stream)
     fout = torch.empty_like(q)
     ms_fine = timed(lambda: vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, w.grid, sel2, topk=K, out=fout),
                     a.steps, a.warmup, stream)
@@ -223,7 +223,7 @@ def extra(a, vsa, torch, stream):
     inp = workload_inputs(w, with_varlen=False)
     q, k, v, gc, gf = (dev(inp[n]) for n in ("q", "k", "v", "gc", "gf"))
     _, kp, vp, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, w.grid, with_q_tiles=False)
-    oc, _, _ = vsa.vsa_coarse_topk(qc, kc, vc, 0)
+    oc, _, _ = vsa.vsa_coarse_topk(qc, kc, vc, 0, input_dtype=torch.bfloat16)
     nc = w.n_cubes
     full = torch.arange(nc, dtype=torch.int32, device="cuda").expand(w.B, w.heads, nc, nc).contiguous()
     fout = torch.empty_like(q)
@@ -242,7 +242,7 @@ def extra(a, vsa, torch, stream):
     inp = workload_inputs(w, with_varlen=False)
     q, k, v, gc, gf = (dev(inp[n]) for n in ("q", "k", "v", "gc", "gf"))
     _, kp, vp, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, w.grid, with_q_tiles=False)
-    oc, _, sel = vsa.vsa_coarse_topk(qc, kc, vc, 32)
+    oc, _, sel = vsa.vsa_coarse_topk(qc, kc, vc, 32, input_dtype=torch.bfloat16)
     fout = torch.empty_like(q)
     ms_fine_s = timed(lambda: vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, w.grid, sel, topk=32, out=fout),
                       steps, warm, stream)

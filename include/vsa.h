@@ -161,9 +161,15 @@ int vsa_cube_permute_pool(const void* q, const void* k, const void* v,
                           float* qc, float* kc, float* vc, hipStream_t stream);
 
 /* Coarse stage: Oc [B,heads,Nc,D] fp32, lse_c [B,heads,Nc] fp32 and, when
- * topk > 0, sel_idx [B,heads,Nc,topk]; topk == 0 skips the selection. */
+ * topk > 0, sel_idx [B,heads,Nc,topk]; topk == 0 skips the selection.
+ * dtype is the element type of the attention inputs and sets the precision
+ * of the two products (logits, P * Vc), which accumulate in fp32 either way:
+ * VSA_F32 multiplies in fp32; VSA_BF16 splits every fp32 operand into bf16
+ * hi + lo and takes hi*hi + hi*lo + lo*hi on the bf16 matrix cores (about
+ * 16 significant bits; the forward entry points use the same choice).  An
+ * unknown dtype is VSA_ERR_INVALID_ARG. */
 int vsa_coarse_topk(const float* qc, const float* kc, const float* vc,
-                    int B, int heads, int head_dim, int n_cubes, int topk,
+                    int B, int heads, int head_dim, int n_cubes, int topk, int dtype,
                     float* oc, float* lse_c, int32_t* sel_idx,
                     hipStream_t stream);
 

@@ -65,9 +65,9 @@ def test_workspace_sizes(lib):
     assert sv >= 4 * (B * nh * nc * D + B * nh * nc + B * nh * N + B * nh * N * D)
     bw = lib.vsa_backward_workspace_bytes(B, nh, D, T, H, W, _lib.VSA_BF16, B * nh * nc * 32)
     assert bw > fw
-    # the coarse stage holds at most 2269 cubes (16 rows of logits in LDS)
-    assert lib.vsa_forward_workspace_bytes(1, 1, 128, 4, 4, 4 * 2269, _lib.VSA_BF16) > 0
-    assert lib.vsa_forward_workspace_bytes(1, 1, 128, 4, 8, 4 * 1135, _lib.VSA_BF16) == 0
+    # the coarse stage holds at most 2272 cubes (16 rows of logits in LDS)
+    assert lib.vsa_forward_workspace_bytes(1, 1, 128, 4, 4, 4 * 2272, _lib.VSA_BF16) > 0
+    assert lib.vsa_forward_workspace_bytes(1, 1, 128, 4, 4, 4 * 2273, _lib.VSA_BF16) == 0
     # invalid shapes size to 0
     assert lib.vsa_forward_workspace_bytes(B, nh, D, 6, H, W, _lib.VSA_BF16) == 0
     assert lib.vsa_forward_workspace_bytes(B, nh, 96, T, H, W, _lib.VSA_BF16) == 0
@@ -116,9 +116,12 @@ def test_varlen_and_backward_reject_bad_arguments(lib):
 
 
 def test_stage_calls_reject_bad_arguments(lib):
-    assert lib.vsa_coarse_topk(FAKE, FAKE, FAKE, 1, 1, 64, 8, 9, FAKE, FAKE, FAKE, None) == INVALID
-    assert lib.vsa_coarse_topk(FAKE, FAKE, FAKE, 1, 1, 64, 8, 2, FAKE, FAKE, None, None) == INVALID
-    assert lib.vsa_coarse_topk(FAKE, FAKE, FAKE, 1, 1, 64, 100000, 2, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    BF = _lib.VSA_BF16
+    assert lib.vsa_coarse_topk(FAKE, FAKE, FAKE, 1, 1, 64, 8, 9, BF, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.vsa_coarse_topk(FAKE, FAKE, FAKE, 1, 1, 64, 8, 2, BF, FAKE, FAKE, None, None) == INVALID
+    assert lib.vsa_coarse_topk(FAKE, FAKE, FAKE, 1, 1, 64, 8, 2, 7, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.vsa_coarse_topk(FAKE, FAKE, FAKE, 1, 1, 64, 100000, 2, BF, FAKE, FAKE, FAKE,
+                               None) == UNSUPPORTED
     assert lib.vsa_fine_forward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 8, 8, 8,
                                 None, FAKE, 2, _lib.VSA_BF16, FAKE, FAKE, None, None) == INVALID
     assert lib.vsa_cube_permute_pool(FAKE, FAKE, FAKE, 1, 1, 64, 8, 8, 5, _lib.VSA_BF16,

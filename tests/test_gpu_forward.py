@@ -99,7 +99,15 @@ def test_permute_pool_stage(dt, D):
         np.testing.assert_allclose(host64(pooled), exp, rtol=1e-6, atol=1e-6, err_msg=name)
 
 
-def test_coarse_stage_and_exact_ties():
+# Coarse-stage bars per product precision.  fp32 products: the fp32 bar.
+# bf16 x 3 products (logits to about 2^-16 relative, i.e. about 1e-5 absolute
+# on these O(1) logits): Oc still within the fp32 bar and lse_c within 5e-5;
+# index parity is unchanged (near-ties are 1e-3 wide).
+COARSE_LSE_ATOL = {F32: 1e-5, BF16: 5e-5}
+
+
+@pytest.mark.parametrize("prec", [F32, BF16], ids=["fp32-products", "bf16x3-products"])
+def test_coarse_stage_and_exact_ties(prec):
     """Coarse output and top-K on pooled tensors, including bitwise-equal
     logits made by copying one key cube into another: the lower id wins."""
     vsa = _vsa()
@@ -116,7 +124,7 @@ def test_coarse_stage_and_exact_ties():
     assert np.array_equal(S[..., 3], S[..., 17])
     straddled = 0
     for K in range(1, 25):
-        oc, lse, sel = vsa.vsa_coarse_topk(qc, kc, vc, K)
+        oc, lse, sel = vsa.vsa_coarse_topk(qc, kc, vc, K, input_dtype=prec)
         torch.cuda.synchronize()
         sel_np = sel.cpu().numpy()
         check_selection(sel_np, S, K)
@@ -126,31 +134,32 @@ def test_coarse_stage_and_exact_ties():
                 straddled += 1
                 assert 3 in sel_np[b, h, r] and 17 not in sel_np[b, h, r]
         if K == 5:
-            assert_close(host64(oc), ref["oc"], F32, "oc")  # fp32 coarse stage
-            np.testing.assert_allclose(host64(lse), ref["lse_c"], atol=1e-5)
+            assert_close(host64(oc), ref["oc"], F32, "oc")  # the fp32 bar in both precisions
+            np.testing.assert_allclose(host64(lse), ref["lse_c"], atol=COARSE_LSE_ATOL[prec])
     assert straddled > 0
 
 
-def test_coarse_stage_at_the_largest_cube_count():
-    """2268 cubes (grid 4x108x336), the most the coarse kernel holds (16
-    rows of logits in LDS, 40 key chunks per row): top-K 32 (pruned
+@pytest.mark.parametrize("prec", [F32, BF16], ids=["fp32-products", "bf16x3-products"])
+def test_coarse_stage_at_the_largest_cube_count(prec):
+    """2272 cubes (grid 4x32x1136), the most the coarse kernel holds (16
+    rows of logits in LDS, 36 key chunks of 64 per row): top-K 32 (pruned
     candidates), 100 (bitwise-search fallback) and Nc, with Oc and lse."""
     vsa = _vsa()
-    grid = (4, 108, 336)
-    log("coarse stage at 2268 cubes")
+    grid = (4, 32, 1136)
+    log(f"coarse stage at 2272 cubes, {prec}")
     inp = make_inputs(1, 1, 128, grid, dtype="bf16", seed=41)
     q, k, v = (dev(inp[n], BF16) for n in "qkv")
     _, _, _, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, grid, with_q_tiles=False)
     nc = qc.shape[2]
-    assert nc == 2268
+    assert nc == 2272
     pooled = [vo.pool(inp[n][0, :, 0].astype(np.float64), *grid) for n in "qkv"]
     oc_ref, S, lse_ref = vo.coarse_attention(*pooled, 1.0 / np.sqrt(128))
     for K in (32, 100, nc):
-        oc, lse, sel = vsa.vsa_coarse_topk(qc, kc, vc, K)
+        oc, lse, sel = vsa.vsa_coarse_topk(qc, kc, vc, K, input_dtype=prec)
         torch.cuda.synchronize()
         check_selection(sel.cpu().numpy(), S[None, None], K)
     assert_close(host64(oc)[0, 0], oc_ref, F32, "oc")
-    np.testing.assert_allclose(host64(lse)[0, 0], lse_ref, atol=1e-5)
+    np.testing.assert_allclose(host64(lse)[0, 0], lse_ref, atol=COARSE_LSE_ATOL[prec])
 
 
 def test_coarse_topk_zero_skips_selection():
@@ -242,7 +251,7 @@ def test_probe_tile_gather_runs_on_every_depth():
     inp = make_inputs(1, 2, 128, grid, dtype="bf16", seed=12)
     q, k, v = (dev(inp[n], BF16) for n in "qkv")
     _, kp, vp, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, grid, with_q_tiles=False)
-    _, _, sel = vsa.vsa_coarse_topk(qc, kc, vc, 5)
+    _, _, sel = vsa.vsa_coarse_topk(qc, kc, vc, 5, input_dtype=BF16)
     kp0, vp0 = kp.clone(), vp.clone()
     for depth in (1, 2, 4, 8):
         vsa.probe_tile_gather(kp, vp, sel, 5, depth)

@@ -29,7 +29,7 @@ SIGNATURES = {
     "block_sparse_attn_varlen_backward": (
         _i, [_p] * 8 + [_i64, _p] + [_i] * 7 + [_p] * 5 + [_p, _sz, _p]),
     "vsa_cube_permute_pool": (_i, [_p] * 3 + [_i] * 7 + [_p] * 6 + [_p]),
-    "vsa_coarse_topk": (_i, [_p] * 3 + [_i] * 5 + [_p] * 3 + [_p]),
+    "vsa_coarse_topk": (_i, [_p] * 3 + [_i] * 6 + [_p] * 3 + [_p]),
     "vsa_fine_forward": (_i, [_p] * 6 + [_i] * 6 + [_p, _p, _i, _i, _p, _p, _p, _p]),
     # include/vsa_probe.h
     "vsa_probe_tile_gather": (_i, [_p, _p, _i, _i, _i, _p, _i, _i, _p, _p]),

@@ -15,9 +15,19 @@
 //      emitted ascending (candidate pruning + direct ranks, see select_row);
 //      then the softmax statistics, and S is overwritten by the
 //      probabilities;
-//   3. Oc = P * vc with fp32 MFMA, vc operands read straight from L2.
-// Everything is fp32: the ranking must match an fp64 reference exactly
-// except at near-ties.
+//   3. Oc = P * vc with MFMA, vc operands read straight from L2.
+// Two precisions of the products in steps 1 and 3, both accumulated in
+// fp32:
+//   * fp32 inputs: fp32 MFMA (v_mfma_f32_16x16x4f32), exact fp32 products;
+//   * bf16 inputs: each fp32 operand x is split into bf16 hi = rn(x) and
+//     lo = rn(x - hi), and a product x*y is taken as hi*hi + hi*lo + lo*hi
+//     on bf16 MFMA (v_mfma_f32_16x16x32_bf16).  The dropped terms are below
+//     about 3 * 2^-16 of |x*y|, so the logits keep about 16 significant
+//     bits: index decisions differ from exact fp32 ones only where two
+//     logits agree to about 1e-5 relative, far inside the 1e-3 near-tie
+//     band of the selection rule, and the bf16 outputs are unaffected.  It
+//     runs on the bf16 matrix rate instead of the fp32 one (16x).
+// The softmax and the ranking are fp32 in both cases.
 #include "vsa_device.h"
 #include "vsa_launch.h"
 
@@ -35,6 +45,19 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
+// x = hi + lo + r with hi = rn_bf16(x), lo = rn_bf16(x - hi) (x - hi is
+// exact in fp32), |r| <= 2^-16 |x|.
+__device__ __forceinline__ void split_bf16x8(const f32x4v a, const f32x4v b, bf16x8& hi,
+                                             bf16x8& lo) {
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const bf16 h = (bf16)x[e];
+    hi[e] = h;
+    lo[e] = (bf16)(x[e] - (float)h);
+  }
+}
+
 // Largest t such that at least k of the wave's 64 lane values are >= t
 // (k in [1, 64]): greedy bitwise search, one ballot per bit.
 __device__ __forceinline__ uint32_t kth_largest_of_lanes(uint32_t x, int k) {
@@ -47,6 +70,11 @@ __device__ __forceinline__ uint32_t kth_largest_of_lanes(uint32_t x, int k) {
 }
 
 constexpr int kNW = 8;        // waves per workgroup
+
+// Row pitch of the logit block (floats): at least nc + 32 (a zero-padded
+// last 32-key step) and a multiple of 8, so that both bf16 planes of a
+// probability row start 16-byte aligned.
+__host__ __device__ constexpr int coarse_pitch(int nc) { return (nc + 39) & ~7; }
 constexpr int kCandCap = 256; // candidates ranked directly per row
 
 // Top-K of one row held by one wave.  `keys` holds this lane's order keys
@@ -147,7 +175,7 @@ __device__ __forceinline__ void select_row(const uint32_t (&keys)[MAXJ], int nc,
 // One workgroup: R = 16 query rows of one (batch, head), 8 waves.
 // Matrix products use v_mfma_f32_16x16x4f32 (fp32 in, fp32 accumulate).
 // Lane l of a 16x16x4 step supplies row/column l % 16 and k-slice l / 16.
-template <int D, int MAXJ>
+template <int D, int MAXJ, bool X3>
 __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
     const float* __restrict__ qc, const float* __restrict__ kc,
     const float* __restrict__ vc, int nc, int topk, float scale,
@@ -156,7 +184,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
   constexpr int DQ = D / 4;          // head_dim slice per lane group
   constexpr int NCW = D / 16;        // waves that own a 16-column output block
   extern __shared__ float lds[];
-  const int s_pitch = (nc + 35) & ~3;  // room for a zero-padded last key block
+  const int s_pitch = coarse_pitch(nc);  // room for a zero-padded last key block
   float* S = lds;                      // [R][s_pitch]
   uint32_t* cand_k = reinterpret_cast<uint32_t*>(S + R * s_pitch);  // [kNW][kCandCap]
   int32_t* cand_i = reinterpret_cast<int32_t*>(cand_k + kNW * kCandCap);
@@ -170,38 +198,80 @@ __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
   const float* kcb = kc + (int64_t)bh * nc * D;
   const float* vcb = vc + (int64_t)bh * nc * D;
 
-  // ---- 1. logits.  Contraction over head_dim: lane group lg covers
-  // d in [lg*DQ, lg*DQ + DQ), one element per k-step.  Wave w takes key
-  // blocks 16w, 16w + 16 kNW, ...; the next block's operands are fetched
-  // while the current one is multiplied.
-  f32x4v qa[DQ / 4];
-  {
-    const int row = min(row0 + li, nc - 1);  // rows past the end are never stored
-    const f32x4v* src = reinterpret_cast<const f32x4v*>(qcb + (int64_t)row * D + lg * DQ);
+  if constexpr (X3) {
+    // ---- 1. logits, bf16 x 3.  k-step t (32 of head_dim): lane group lg
+    // supplies d = 32t + 8lg .. +8 of its row (A: query row li, B: key li).
+    // Wave w takes key blocks 16w, 16w + 16 kNW, ...; the next block's
+    // operands are fetched while the current one is multiplied.
+    constexpr int KT = D / 32;
+    bf16x8 qh[KT], ql[KT];
+    {
+      const int row = min(row0 + li, nc - 1);  // rows past the end are never used
+      const f32x4v* src = reinterpret_cast<const f32x4v*>(qcb + (int64_t)row * D + 8 * lg);
 #pragma unroll
-    for (int i = 0; i < DQ / 4; ++i) qa[i] = src[i];
-  }
-  auto load_k = [&](int j0, f32x4v (&kb)[DQ / 4]) {
-    const f32x4v* src = reinterpret_cast<const f32x4v*>(kcb + (int64_t)min(j0 + li, nc - 1) * D + lg * DQ);
+      for (int t = 0; t < KT; ++t) split_bf16x8(src[8 * t], src[8 * t + 1], qh[t], ql[t]);
+    }
+    auto load_k = [&](int j0, f32x4v (&kb)[2 * KT]) {
+      const f32x4v* src =
+          reinterpret_cast<const f32x4v*>(kcb + (int64_t)min(j0 + li, nc - 1) * D + 8 * lg);
 #pragma unroll
-    for (int i = 0; i < DQ / 4; ++i) kb[i] = src[i];
-  };
-  f32x4v kb[DQ / 4], kn[DQ / 4];
-  if (16 * wave < nc) load_k(16 * wave, kn);
-  for (int j0 = 16 * wave; j0 < nc; j0 += 16 * kNW) {
+      for (int t = 0; t < KT; ++t) { kb[2 * t] = src[8 * t]; kb[2 * t + 1] = src[8 * t + 1]; }
+    };
+    f32x4v kb[2 * KT], kn[2 * KT];
+    if (16 * wave < nc) load_k(16 * wave, kn);
+    for (int j0 = 16 * wave; j0 < nc; j0 += 16 * kNW) {
 #pragma unroll
-    for (int i = 0; i < DQ / 4; ++i) kb[i] = kn[i];
-    if (j0 + 16 * kNW < nc) load_k(j0 + 16 * kNW, kn);
-    f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 2 * KT; ++i) kb[i] = kn[i];
+      if (j0 + 16 * kNW < nc) load_k(j0 + 16 * kNW, kn);
+      f32x4v acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < DQ / 4; ++i)
+      for (int t = 0; t < KT; ++t) {
+        bf16x8 kh, kl;
+        split_bf16x8(kb[2 * t], kb[2 * t + 1], kh, kl);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[t], kh, acc, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[t], kl, acc2, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[t], kh, acc2, 0, 0, 0);
+      }
+      const int key = j0 + li;
+      if (key < nc) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][e], kb[i][e], acc, 0, 0, 0);
-    const int key = j0 + li;
-    if (key < nc) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[(4 * lg + r) * s_pitch + key] = acc[r] * scale;
+        for (int r = 0; r < 4; ++r) S[(4 * lg + r) * s_pitch + key] = (acc[r] + acc2[r]) * scale;
+      }
+    }
+  } else {
+    // ---- 1. logits.  Contraction over head_dim: lane group lg covers
+    // d in [lg*DQ, lg*DQ + DQ), one element per k-step.  Wave w takes key
+    // blocks 16w, 16w + 16 kNW, ...; the next block's operands are fetched
+    // while the current one is multiplied.
+    f32x4v qa[DQ / 4];
+    {
+      const int row = min(row0 + li, nc - 1);  // rows past the end are never stored
+      const f32x4v* src = reinterpret_cast<const f32x4v*>(qcb + (int64_t)row * D + lg * DQ);
+  #pragma unroll
+      for (int i = 0; i < DQ / 4; ++i) qa[i] = src[i];
+    }
+    auto load_k = [&](int j0, f32x4v (&kb)[DQ / 4]) {
+      const f32x4v* src = reinterpret_cast<const f32x4v*>(kcb + (int64_t)min(j0 + li, nc - 1) * D + lg * DQ);
+  #pragma unroll
+      for (int i = 0; i < DQ / 4; ++i) kb[i] = src[i];
+    };
+    f32x4v kb[DQ / 4], kn[DQ / 4];
+    if (16 * wave < nc) load_k(16 * wave, kn);
+    for (int j0 = 16 * wave; j0 < nc; j0 += 16 * kNW) {
+  #pragma unroll
+      for (int i = 0; i < DQ / 4; ++i) kb[i] = kn[i];
+      if (j0 + 16 * kNW < nc) load_k(j0 + 16 * kNW, kn);
+      f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+      for (int i = 0; i < DQ / 4; ++i)
+  #pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i][e], kb[i][e], acc, 0, 0, 0);
+      const int key = j0 + li;
+      if (key < nc) {
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) S[(4 * lg + r) * s_pitch + key] = acc[r] * scale;
+      }
     }
   }
   __syncthreads();
@@ -242,59 +312,132 @@ __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
     }
     z = wave_sum(z);
     const float inv = 1.0f / z;
+    if constexpr (X3) {
+      // P as two bf16 planes in the row's own storage: hi at [0, s_pitch),
+      // lo at [s_pitch, 2 s_pitch) (bf16 elements), zero past nc.
+      bf16* ph = reinterpret_cast<bf16*>(Srow);
+      bf16* pl = ph + s_pitch;
 #pragma unroll
-    for (int j = 0; j < MAXJ; ++j) {
-      const int idx = 64 * j + lane;
-      if (64 * j < nc && idx < nc) Srow[idx] = sv[j] * inv;
+      for (int j = 0; j < MAXJ; ++j) {
+        const int idx = 64 * j + lane;
+        if (64 * j < nc && idx < nc) {
+          const float pv = sv[j] * inv;
+          const bf16 h = (bf16)pv;
+          ph[idx] = h;
+          pl[idx] = (bf16)(pv - (float)h);
+        }
+      }
+      for (int j = nc + lane; j < s_pitch; j += 64) { ph[j] = (bf16)0.f; pl[j] = (bf16)0.f; }
+    } else {
+#pragma unroll
+      for (int j = 0; j < MAXJ; ++j) {
+        const int idx = 64 * j + lane;
+        if (64 * j < nc && idx < nc) Srow[idx] = sv[j] * inv;
+      }
+      for (int j = nc + lane; j < s_pitch; j += 64) Srow[j] = 0.f;  // padded key block
     }
-    for (int j = nc + lane; j < s_pitch; j += 64) Srow[j] = 0.f;  // padded key block
     if (lane == 0) lse[(int64_t)bh * nc + row] = m + logf(z);
   }
   __syncthreads();
 
-  // ---- 3. Oc = P * vc.  Wave w < D/16 owns output columns [16w, 16w + 16);
-  // contraction over keys, lane group lg taking key j0 + 4t + lg at k-step
-  // t.  B operands come straight from L2 (vc of one head is small), the
-  // next 32-key block prefetched during the current.
-  if (wave < NCW) {
-    f32x4v oacc = {0.f, 0.f, 0.f, 0.f};
-    const int col = 16 * wave + li;
+  if constexpr (X3) {
+    // ---- 3. Oc = P * vc, bf16 x 3.  Wave w owns output columns
+    // [16 cb, 16 cb + 16), cb = w % (D/16), and every (kNW/(D/16))-th
+    // 32-key step starting at w / (D/16).  k-step keys j0 + 8lg .. +8:
+    // P from the row's bf16 planes (A: row li), vc read straight from L2
+    // (B: column li) and split in registers; the next step prefetched.
+    constexpr int NCB = D / 16;
+    constexpr int NKS = kNW / NCB;
+    const int cb = wave % NCB, kq = wave / NCB;
+    const int col = 16 * cb + li;
+    const bf16* prow = reinterpret_cast<const bf16*>(S + li * s_pitch);
     auto load_v = [&](int j0, float (&vbuf)[8]) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int key = min(j0 + 4 * t + lg, nc - 1);  // P is 0 past the end
-        vbuf[t] = vcb[(int64_t)key * D + col];
+      for (int e = 0; e < 8; ++e) {
+        const int key = min(j0 + 8 * lg + e, nc - 1);  // P is 0 past the end
+        vbuf[e] = vcb[(int64_t)key * D + col];
       }
     };
+    f32x4v oacc = {0.f, 0.f, 0.f, 0.f}, oacc2 = {0.f, 0.f, 0.f, 0.f};
     float vb[8], vn[8];
-    load_v(0, vn);
-    for (int j0 = 0; j0 < nc; j0 += 32) {
+    if (32 * kq < nc) load_v(32 * kq, vn);
+    for (int j0 = 32 * kq; j0 < nc; j0 += 32 * NKS) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) vb[t] = vn[t];
-      if (j0 + 32 < nc) load_v(j0 + 32, vn);
+      for (int e = 0; e < 8; ++e) vb[e] = vn[e];
+      if (j0 + 32 * NKS < nc) load_v(j0 + 32 * NKS, vn);
+      bf16x8 vh, vl;
+      split_bf16x8(f32x4v{vb[0], vb[1], vb[2], vb[3]}, f32x4v{vb[4], vb[5], vb[6], vb[7]}, vh, vl);
+      const bf16x8 pa = *reinterpret_cast<const bf16x8*>(prow + j0 + 8 * lg);
+      const bf16x8 pb = *reinterpret_cast<const bf16x8*>(prow + s_pitch + j0 + 8 * lg);
+      oacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vh, oacc, 0, 0, 0);
+      oacc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vl, oacc2, 0, 0, 0);
+      oacc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb, vh, oacc2, 0, 0, 0);
+    }
+    oacc += oacc2;
+    if constexpr (NKS > 1) {
+      // key splits of one column block summed through the (now free)
+      // candidate scratch
+      static_assert(NKS == 2, "two key splits at head_dim 64");
+      float* red = reinterpret_cast<float*>(cand_k);
+      if (kq == 1) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float pa = S[li * s_pitch + j0 + 4 * t + lg];
-        oacc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vb[t], oacc, 0, 0, 0);
+        for (int r = 0; r < 4; ++r) red[(cb * 4 + r) * 64 + lane] = oacc[r];
       }
+      __syncthreads();
+      if (kq == 1) return;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) oacc[r] += red[(cb * 4 + r) * 64 + lane];
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = row0 + 4 * lg + r;
       if (row < nc) oc[((int64_t)bh * nc + row) * D + col] = oacc[r];
     }
+  } else {
+    // ---- 3. Oc = P * vc.  Wave w < D/16 owns output columns [16w, 16w + 16);
+    // contraction over keys, lane group lg taking key j0 + 4t + lg at k-step
+    // t.  B operands come straight from L2 (vc of one head is small), the
+    // next 32-key block prefetched during the current.
+    if (wave < NCW) {
+      f32x4v oacc = {0.f, 0.f, 0.f, 0.f};
+      const int col = 16 * wave + li;
+      auto load_v = [&](int j0, float (&vbuf)[8]) {
+  #pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int key = min(j0 + 4 * t + lg, nc - 1);  // P is 0 past the end
+          vbuf[t] = vcb[(int64_t)key * D + col];
+        }
+      };
+      float vb[8], vn[8];
+      load_v(0, vn);
+      for (int j0 = 0; j0 < nc; j0 += 32) {
+  #pragma unroll
+        for (int t = 0; t < 8; ++t) vb[t] = vn[t];
+        if (j0 + 32 < nc) load_v(j0 + 32, vn);
+  #pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float pa = S[li * s_pitch + j0 + 4 * t + lg];
+          oacc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vb[t], oacc, 0, 0, 0);
+        }
+      }
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + 4 * lg + r;
+        if (row < nc) oc[((int64_t)bh * nc + row) * D + col] = oacc[r];
+      }
+    }
   }
 }
 
 size_t coarse_lds_bytes(int nc) {
-  const int s_pitch = (nc + 35) & ~3;
+  const int s_pitch = coarse_pitch(nc);
   return sizeof(float) * ((size_t)16 * s_pitch + (size_t)2 * kNW * kCandCap);
 }
 
-template <int D, int MAXJ>
+template <int D, int MAXJ, bool X3>
 hipError_t launch_coarse_dj(const CoarseArgs& a, hipStream_t st) {
   const size_t lds = coarse_lds_bytes(a.nc);
-  auto kern = coarse_topk_kernel<D, MAXJ>;
+  auto kern = coarse_topk_kernel<D, MAXJ, X3>;
   // Raise the dynamic LDS limit once per kernel instance (host-side call).
   static size_t lds_limit = 0;
   if (lds > lds_limit) {
@@ -308,10 +451,10 @@ hipError_t launch_coarse_dj(const CoarseArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool X3>
 hipError_t launch_coarse_d(const CoarseArgs& a, hipStream_t st) {
-  if (a.nc <= 16 * 64) return launch_coarse_dj<D, 16>(a, st);
-  return launch_coarse_dj<D, 40>(a, st);
+  if (a.nc <= 16 * 64) return launch_coarse_dj<D, 16, X3>(a, st);
+  return launch_coarse_dj<D, 40, X3>(a, st);
 }
 
 }  // namespace
@@ -320,12 +463,14 @@ int coarse_max_cubes(int D) {
   (void)D;
   // 16 rows of logits plus candidate scratch in LDS, and at most 40 key
   // chunks of 64 per row.
-  const int by_lds = (int)((kLdsBudget / sizeof(float) - 2 * kNW * kCandCap) / 16) - 35;
+  const int max_pitch = (int)((kLdsBudget / sizeof(float) - 2 * kNW * kCandCap) / 16) & ~7;
+  const int by_lds = max_pitch - 32;  // largest nc with coarse_pitch(nc) <= max_pitch
   return by_lds < 40 * 64 ? by_lds : 40 * 64;
 }
 
 hipError_t launch_coarse_topk(const CoarseArgs& a, hipStream_t st) {
-  return a.D == 128 ? launch_coarse_d<128>(a, st) : launch_coarse_d<64>(a, st);
+  if (a.x3) return a.D == 128 ? launch_coarse_d<128, true>(a, st) : launch_coarse_d<64, true>(a, st);
+  return a.D == 128 ? launch_coarse_d<128, false>(a, st) : launch_coarse_d<64, false>(a, st);
 }
 
 }  // namespace vsa

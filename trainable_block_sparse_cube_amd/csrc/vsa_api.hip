@@ -93,7 +93,7 @@ int forward_impl(const void* q, const void* k, const void* v, const void* gc, co
                      s.B, s.heads, s.D, s.T, s.H, s.W, bf};
   hipError_t e = launch_permute_pool(pa, st);
   if (e != hipSuccess) return VSA_ERR_HIP;
-  CoarseArgs ca{w.qc, w.kc, w.vc, s.B, s.heads, s.D, (int)s.nc, offs ? 0 : topk, oc, lse_c, sel};
+  CoarseArgs ca{w.qc, w.kc, w.vc, s.B, s.heads, s.D, (int)s.nc, offs ? 0 : topk, oc, lse_c, sel, bf};
   e = launch_coarse_topk(ca, st);
   if (e != hipSuccess) return VSA_ERR_HIP;
   FineArgs fa{q, w.kp, w.vp, oc, gc, gf, s.B, s.heads, s.D, s.T, s.H, s.W,
@@ -233,8 +233,9 @@ int vsa_cube_permute_pool(const void* q, const void* k, const void* v,
 }
 
 int vsa_coarse_topk(const float* qc, const float* kc, const float* vc,
-                    int B, int heads, int head_dim, int n_cubes, int topk,
+                    int B, int heads, int head_dim, int n_cubes, int topk, int dtype,
                     float* oc, float* lse_c, int32_t* sel_idx, hipStream_t stream) {
+  if (dtype != VSA_F32 && dtype != VSA_BF16) return VSA_ERR_INVALID_ARG;
   if (B < 1 || heads < 1 || n_cubes < 1) return VSA_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return VSA_ERR_UNSUPPORTED;
   if (n_cubes > coarse_max_cubes(head_dim) || (int64_t)B * heads > 65535) return VSA_ERR_UNSUPPORTED;
@@ -242,7 +243,7 @@ int vsa_coarse_topk(const float* qc, const float* kc, const float* vc,
   if (!qc || !kc || !vc || !oc || !lse_c || (topk > 0 && !sel_idx)) return VSA_ERR_INVALID_ARG;
   if ((int64_t)B * heads * n_cubes > INT_MAX / 2 || (int64_t)B * heads * n_cubes * topk > INT_MAX)
     return VSA_ERR_UNSUPPORTED;
-  CoarseArgs ca{qc, kc, vc, B, heads, head_dim, n_cubes, topk, oc, lse_c, sel_idx};
+  CoarseArgs ca{qc, kc, vc, B, heads, head_dim, n_cubes, topk, oc, lse_c, sel_idx, dtype == VSA_BF16};
   return hip_status(launch_coarse_topk(ca, stream));
 }
 

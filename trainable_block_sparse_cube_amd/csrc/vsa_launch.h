@@ -26,6 +26,7 @@ struct CoarseArgs {
   int B, heads, D, nc, topk;
   float *oc, *lse;
   int32_t* sel;  // may be null when topk == 0
+  bool x3;       // products as three bf16 MFMAs (bf16 inputs) instead of fp32 MFMA
 };
 // Largest number of cubes the coarse kernel accepts.
 int coarse_max_cubes(int D);

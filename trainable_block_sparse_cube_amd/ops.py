@@ -153,15 +153,18 @@ def vsa_cube_permute_pool(q, k, v, grid, with_q_tiles=True):
     return (qp, kp, vp, *pooled)
 
 
-def vsa_coarse_topk(qc, kc, vc, topk):
-    """Returns (oc, lse_c, sel or None) for fp32 pooled [B, heads, Nc, D]."""
+def vsa_coarse_topk(qc, kc, vc, topk, input_dtype=torch.float32):
+    """Returns (oc, lse_c, sel or None) for fp32 pooled [B, heads, Nc, D].
+    input_dtype, the element type of the attention inputs, sets the product
+    precision: fp32 products for torch.float32, bf16 x 3 for torch.bfloat16
+    (as the forward does for such inputs)."""
     lib = _lib.load()
     B, nh, nc, D = qc.shape
     oc = torch.empty_like(qc)
     lse = torch.empty((B, nh, nc), dtype=torch.float32, device=qc.device)
     sel = torch.empty((B, nh, nc, topk), dtype=torch.int32, device=qc.device) if topk > 0 else None
     st = lib.vsa_coarse_topk(_ptr(qc), _ptr(kc), _ptr(vc), B, nh, D, nc, topk,
-                             _ptr(oc), _ptr(lse), _ptr(sel), _stream())
+                             _DT[input_dtype], _ptr(oc), _ptr(lse), _ptr(sel), _stream())
     _lib.check("vsa_coarse_topk", st)
     return oc, lse, sel
 
