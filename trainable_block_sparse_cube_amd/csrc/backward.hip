@@ -384,7 +384,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(
     const bf16* __restrict__ dofp, const float* __restrict__ lse_f, const float* __restrict__ delta,
     const int32_t* __restrict__ tr_offs, const int32_t* __restrict__ tr_order,
     const int32_t* __restrict__ tr_ids, const float* __restrict__ dkc, const float* __restrict__ dvc,
-    int nh, int nc, int Hg, int Wg, float scale,
+    int nh, int nc, int Hg, int Wg, float scale, int n_logical,
     bf16* __restrict__ dk, bf16* __restrict__ dv) {
   constexpr int KS = D / 16, MD = D / 32, TILE_CH = 64 * D / 8;
   // Tile parity buffers: separate arrays picked at run time, so that the
@@ -400,7 +400,13 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ql = lane & 31, hf = lane >> 5;
   const int kh = wave & 1, qh = wave >> 1;
-  const int blk = blockIdx.x;  // (b*nh + h)*nc + rank of the key cube by list length
+  // Logical block (b*nh + h)*nc + rank of the key cube by list length,
+  // numbered XCD-contiguously (hardware block i runs on XCD i % 8): each XCD
+  // works through whole heads, longest lists first, and keeps one head's
+  // Q and dO tiles in its own L2.  Padding blocks exit at once.
+  const int per = (n_logical + 7) >> 3;
+  const int blk = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  if (blk >= n_logical) return;
   const int bh = blk / nc;
   const int64_t N = (int64_t)nc * 64;
   const int64_t bh_tiles = (int64_t)bh * nc;
@@ -721,10 +727,10 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t st) {
   transpose_rank_kernel<<<(unsigned)((n_lists + 3) / 4), 256, 0, st>>>(a.tr_offs, a.tr_tmp, n_lists, a.tr_ids);
   VSA_TRY(hipGetLastError());
   const unsigned grid = (unsigned)(BH * nc);
-  fine_bwd_dkdv_kernel<D><<<grid, 256, 0, st>>>(
+  fine_bwd_dkdv_kernel<D><<<((grid + 7u) / 8u) * 8u, 256, 0, st>>>(
       (const bf16*)a.qp, (const bf16*)a.kp, (const bf16*)a.vp, (const bf16*)a.dofp,
       a.lse_f, a.delta, a.tr_offs, a.tr_order, a.tr_ids, a.dkc, a.dvc, a.heads, nc, a.H, a.W,
-      scale, (bf16*)a.dk, (bf16*)a.dv);
+      scale, (int)grid, (bf16*)a.dk, (bf16*)a.dv);
   VSA_TRY(hipGetLastError());
   fine_bwd_dq_kernel<D><<<((grid + 7u) / 8u) * 8u, 256, 0, st>>>(
       (const bf16*)a.qp, (const bf16*)a.kp, (const bf16*)a.vp, (const bf16*)a.dofp,
