@@ -131,6 +131,36 @@ def select_topk(S, topk):
     return sel
 
 
+def select_mass(S, mass, k_min, k_max):
+    """Stand-in variable-length selection: key-cube lists of varying length
+    per query cube, as [VSA2-abs] lets each query attend a variable number
+    of key-value pairs.  The pages do not define how VSA2 picks them (its
+    router is not given), so this rule is an assumption of this library, not
+    the method: for each query cube, rank the key cubes as select_topk does
+    (coarse logit descending, cube index ascending) and take the shortest
+    prefix of that ranking whose coarse softmax probability mass reaches
+    `mass` ([VSA-sum, Approach]: the coarse scores mark the critical
+    cubes); clamp its length to [k_min, k_max].
+
+    Returns (lists, lengths): a list of ascending int64 arrays, one per row
+    of S, and their lengths.  0 < mass <= 1, 1 <= k_min <= k_max <= Nc.
+    """
+    nc = S.shape[1]
+    if not (0.0 < mass <= 1.0 and 1 <= k_min <= k_max <= nc):
+        raise ValueError(f"mass={mass}, k_min={k_min}, k_max={k_max} out of range for Nc={nc}")
+    P, _ = _softmax_rows(S)
+    idx = np.arange(nc)
+    lists, lengths = [], np.empty(S.shape[0], dtype=np.int64)
+    for r in range(S.shape[0]):
+        order = np.lexsort((idx, -S[r]))
+        reached = np.nonzero(np.cumsum(P[r, order]) >= mass)[0]
+        n = int(reached[0]) + 1 if reached.size else nc
+        n = min(max(n, k_min), k_max)
+        lists.append(np.sort(order[:n]))
+        lengths[r] = n
+    return lists, lengths
+
+
 def fine_attention(q, k, v, key_lists, T, H, W, scale):
     """Token-level softmax attention restricted to the selected cubes
     ([VSA-abs]: the fine stage attends only inside the selected tiles).

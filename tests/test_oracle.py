@@ -3,6 +3,7 @@ library dense attention (torch fp64 SDPA), index maps built by reshape,
 brute-force scalar loops, closed forms, invariants and central finite
 differences.  CPU only.
 """
+import itertools
 import json
 import math
 import os
@@ -124,6 +125,89 @@ def test_topk_rejects_bad_k():
         vo.select_topk(np.zeros((2, 4)), 0)
     with pytest.raises(ValueError):
         vo.select_topk(np.zeros((2, 4)), 5)
+
+
+# ------------------------------------------- step 3': stand-in mass rule
+def _softmax_lib(row):
+    from scipy.special import softmax
+    return softmax(row)
+
+
+def _check_mass_list(row, ids, mass, k_min, k_max):
+    """Invariants of one list of the mass rule, independent of its code:
+    ascending distinct ids; every chosen logit >= every unchosen one, equal
+    logits going to the lower id; length = the fewest cubes of any subset
+    whose probability mass reaches `mass` (clamped), found by enumeration."""
+    nc = row.shape[0]
+    assert np.all(np.diff(ids) > 0) and 0 <= ids.min() and ids.max() < nc
+    rest = np.setdiff1d(np.arange(nc), ids)
+    for j in rest:
+        for i in ids:
+            assert row[i] > row[j] or (row[i] == row[j] and i < j)
+    p = _softmax_lib(row)
+    best = nc
+    for size in range(1, nc + 1):
+        if any(p[list(c)].sum() >= mass for c in itertools.combinations(range(nc), size)):
+            best = size
+            break
+    assert len(ids) == min(max(best, k_min), k_max)
+
+
+@pytest.mark.parametrize("mass", [0.05, 0.3, 0.5, 0.8, 0.95])
+def test_mass_rule_matches_subset_enumeration(mass):
+    rng = np.random.default_rng(int(mass * 100))
+    S = 1.5 * rng.standard_normal((12, 8))
+    S[4, :] = rng.standard_normal(8) * 1e-3  # a nearly flat row
+    lists, lengths = vo.select_mass(S, mass, 1, 8)
+    for r in range(S.shape[0]):
+        assert lengths[r] == len(lists[r])
+        _check_mass_list(S[r], lists[r], mass, 1, 8)
+    lists, _ = vo.select_mass(S, mass, 2, 5)  # clamped
+    for r in range(S.shape[0]):
+        _check_mass_list(S[r], lists[r], mass, 2, 5)
+
+
+def test_mass_rule_is_topk_when_clamped_to_one_length():
+    rng = np.random.default_rng(5)
+    S = rng.standard_normal((10, 40))
+    S[:, 7] = S[:, 30]  # exact ties
+    for K in (1, 4, 17, 40):
+        for mass in (0.01, 0.5, 1.0):
+            lists, lengths = vo.select_mass(S, mass, K, K)
+            assert np.all(lengths == K)
+            np.testing.assert_array_equal(np.array(lists), _rank_select(S, K))
+
+
+def test_mass_rule_uniform_row_closed_form():
+    nc = 40
+    S = np.full((1, nc), 0.7)  # every cube has probability 1/nc
+    for m in (1, 3, 10, 25, 40):
+        lists, lengths = vo.select_mass(S, (m - 0.5) / nc, 1, nc)
+        assert lengths[0] == m  # ceil(mass * nc)
+        np.testing.assert_array_equal(lists[0], np.arange(m))  # ties: lowest ids
+
+
+def test_mass_rule_monotone_nested_and_clamped():
+    rng = np.random.default_rng(11)
+    S = 2.0 * rng.standard_normal((6, 64))
+    prev = None
+    for mass in (0.1, 0.25, 0.5, 0.75, 0.9, 0.99):
+        lists, lengths = vo.select_mass(S, mass, 1, 64)
+        if prev is not None:
+            assert np.all(lengths >= prev[1])
+            for a, b in zip(prev[0], lists):
+                assert set(a) <= set(b)
+        prev = (lists, lengths)
+    _, lengths = vo.select_mass(S, 1e-9, 3, 64)
+    assert np.all(lengths == 3)  # the single largest cube already carries the mass
+    _, lengths = vo.select_mass(S, 1.0, 1, 20)
+    assert np.all(lengths == 20)
+    with pytest.raises(ValueError):
+        vo.select_mass(S, 0.0, 1, 4)
+    with pytest.raises(ValueError):
+        vo.select_mass(S, 0.5, 5, 4)
+    with pytest.raises(ValueError):
+        vo.select_mass(S, 0.5, 1, 65)
 
 
 def test_exact_tie_from_copied_key_cube_goes_to_lower_index():
