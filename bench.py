@@ -15,8 +15,11 @@ same selection, no arithmetic) and the fine kernel on a shared selection
 The fp64 CPU oracle is timed on a bounded sample of the same workload as the
 CPU baseline.  HBM traffic of the
 fine kernel comes from the committed profiler-counter summary
-(profiles/fine_fwd_bf16_long61k_k32_pmc.txt) and is reported only while the
-kernel source still hashes to the value recorded there.
+(profiles/fine_fwd_bf16_long61k_k32_pmc.txt), as does its shader clock under
+load (with the peak scaled to that clock beside the published one); both are
+reported only while the kernel source still hashes to the value recorded
+there.  Median and minimum per call come from a second pass with one event
+pair per call.
 Prints one JSON line.
 """
 import argparse
@@ -41,17 +44,18 @@ def fine_source_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per fine-kernel launch from the committed counter summary
-    (its last line is JSON), or None if absent or taken on other source."""
+def measured_counters():
+    """The fine kernel's record in the committed counter summary (its last
+    line is JSON: HBM bytes per launch, shader clock), or {} if absent or
+    taken on other kernel source."""
     try:
         with open(PMC_SUMMARY) as f:
             rec = json.loads(f.read().strip().splitlines()[-1])
     except (OSError, ValueError, IndexError):
-        return None
+        return {}
     if rec.get("fine_fwd_source_sha256_16") != fine_source_hash():
-        return None
-    return rec.get("hbm_bytes_per_launch")
+        return {}
+    return rec
 
 
 def parse():
@@ -84,6 +88,21 @@ def timed(fn, steps, warmup, stream):
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
+
+
+def per_call_ms(fn, n, stream):
+    """Median and minimum of n calls, each bracketed by its own events."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    fn()
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(n):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(n))
+    return {"median": t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2]), "min": t[0], "calls": n}
 
 
 def cpu_baseline(inp, w, topk, heads):
@@ -155,6 +174,11 @@ def main():
     ms_shared = timed(lambda: vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, w.grid, shared, topk=K, out=fout),
                       a.steps, a.warmup, stream)
     del shared
+    calls = {"step": per_call_ms(step, a.steps, stream),
+             "fine": per_call_ms(lambda: vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, w.grid, sel2, topk=K,
+                                                             out=fout), a.steps, stream)}
+    counters = measured_counters()
+    clk = counters.get("fine_clock_GHz")
     res = {
         "metric": "VSA fwd effective TFLOP/s & % bf16 MFMA peak at 61440 tokens, K=32",
         "value": (f_fine + f_coarse) / (ms_step * 1e-3) / 1e12,
@@ -177,8 +201,14 @@ def main():
         "fine_TFLOPs": fine_tflops,
         "roofline": {"bound": "mfma", "kernel": "fine_fwd_bf16_kernel<128>",
                      "achieved": fine_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": fine_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
-                     "flops_per_launch": f_fine, "ms_per_launch": ms_fine},
+                     "frac": fine_tflops / PEAK_BF16_TFLOPS, "traffic": counters.get("hbm_bytes_per_launch"),
+                     "flops_per_launch": f_fine, "ms_per_launch": ms_fine,
+                     # the kernel's own shader clock under load (profiler counters) and the
+                     # peak and fraction at that clock; the published peak assumes 2.4 GHz
+                     "clock_GHz": clk,
+                     "peak_at_clock": PEAK_BF16_TFLOPS * clk / 2.4 if clk else None,
+                     "frac_at_clock": fine_tflops / (PEAK_BF16_TFLOPS * clk / 2.4) if clk else None},
+        "per_call_ms": calls,
         "fine_floors": {
             "tile_bytes_per_launch": tile_bytes,
             "tile_delivery_TBps": tile_bytes / (ms_fine * 1e-3) / 1e12,

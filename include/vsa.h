@@ -118,6 +118,38 @@ int block_sparse_attn_varlen(const void* q, const void* k, const void* v,
                              void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* ------------------------------------------- variable-length selection
+ * A stand-in rule for variable-length key lists.  [VSA2-abs] lets each
+ * query attend a variable number of key-value pairs but does not define
+ * how VSA2 picks them (its router is not given); this rule is an
+ * assumption of this library, not the method:
+ *   per query cube, rank the key cubes as the top-K step does (coarse logit
+ *   descending, lower cube index first on ties) and take the shortest
+ *   prefix of that ranking whose coarse softmax probability mass reaches
+ *   `mass` ([VSA-sum, Approach]: the coarse scores mark the critical
+ *   cubes); clamp its length to [k_min, k_max]; report it ascending.
+ * The mass is summed in fp32 on the GPU: where a prefix's mass lies within
+ * rounding of `mass`, the length may differ by one from an exact-arithmetic
+ * evaluation.
+ * mass in (0, 1]; 1 <= k_min <= k_max <= Nc; B*heads*Nc*k_max <= INT_MAX
+ * (else VSA_ERR_UNSUPPORTED); anything else VSA_ERR_INVALID_ARG.
+ *
+ * vsa_forward_mass: vsa_forward with step 3 replaced by this rule.  The
+ * lists it used are written as CSR, ordered by (b, h, query cube):
+ * kv_offsets [B*heads*Nc + 1] and kv_ids (capacity B*heads*Nc*k_max;
+ * kv_offsets[B*heads*Nc] entries are written), ready for
+ * block_sparse_attn_varlen_backward with the same `saved`.  workspace:
+ * vsa_forward_mass_workspace_bytes (0 for an invalid shape or k_max).
+ */
+size_t vsa_forward_mass_workspace_bytes(int B, int heads, int head_dim,
+                                        int T, int H, int W, int dtype, int k_max);
+int vsa_forward_mass(const void* q, const void* k, const void* v,
+                     const void* gate_c, const void* gate_f,
+                     int B, int heads, int head_dim, int T, int H, int W,
+                     float mass, int k_min, int k_max, int dtype,
+                     void* out, int32_t* kv_offsets, int32_t* kv_ids, void* saved,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* --------------------------------------------------------------- backward
  * Gradients of sum(dout * out) for a forward run with `saved` non-NULL
  * ([VSA-abs]: one operator trained end-to-end).  The selection is held
@@ -172,6 +204,24 @@ int vsa_coarse_topk(const float* qc, const float* kc, const float* vc,
                     int B, int heads, int head_dim, int n_cubes, int topk, int dtype,
                     float* oc, float* lse_c, int32_t* sel_idx,
                     hipStream_t stream);
+
+/* Coarse stage with the variable-length rule above instead of top-K: oc
+ * and lse_c as vsa_coarse_topk (dtype sets the product precision the same
+ * way); counts [B,heads,Nc] int32 list lengths; ids [B,heads,Nc,k_max]
+ * int32, list r ascending in ids[r*k_max .. r*k_max + counts[r]) (the rest
+ * of each row is left as it was). */
+int vsa_coarse_select_mass(const float* qc, const float* kc, const float* vc,
+                           int B, int heads, int head_dim, int n_cubes,
+                           float mass, int k_min, int k_max, int dtype,
+                           float* oc, float* lse_c, int32_t* counts, int32_t* ids,
+                           hipStream_t stream);
+
+/* Padded lists (counts [n_rows], ids_padded [n_rows, k_max] as written by
+ * vsa_coarse_select_mass) -> CSR: kv_offsets [n_rows + 1] with
+ * kv_offsets[r] = counts[0] + ... + counts[r-1], and kv_ids holding the
+ * lists back to back in row order.  counts[r] must lie in [0, k_max]. */
+int vsa_pack_lists(const int32_t* counts, const int32_t* ids_padded, int n_rows, int k_max,
+                   int32_t* kv_offsets, int32_t* kv_ids, hipStream_t stream);
 
 /* Fine stage + gated combine.  q: the raster input [B,N,heads,D] (read in
  * place); kp, vp: K and V tiles from vsa_cube_permute_pool; oc: coarse

@@ -7,6 +7,8 @@ import sys
 import numpy as np
 import torch
 
+from oracle import vsa_oracle as vo
+
 # Parity bars.  fp32 path: max abs 1e-4.  bf16 inputs with fp32
 # accumulation: max abs 2e-2 and relative RMS 4e-3 over the whole tensor.
 F32_MAX_ABS = 1e-4
@@ -82,3 +84,34 @@ def check_selection(sel, S, K):
         if not check_selection_row(sel[idx], S[idx], K):
             exempt += 1
     return exempt
+
+
+# Band for the stand-in mass rule: a GPU list may be one longer or shorter
+# than the exact rule's only where the ranked prefix's probability mass
+# crosses `mass` within this distance of it.  The GPU sums fp32
+# probabilities whose logits carry up to about 1e-5 absolute error (bf16 x 3
+# products), so its prefix masses are within a few 1e-5 of exact ones.
+MASS_BAND = 1e-4
+
+
+def check_mass_row(ids_row, logits_row, mass, k_min, k_max):
+    """GPU list of the mass rule for one query cube against fp64 logits.
+
+    The length must equal the oracle's, or differ by one where the mass of
+    the shorter prefix lies within MASS_BAND of `mass`; the ids must then be
+    the top-length cubes of the ranking (near-tie rule of
+    check_selection_row).  Returns True when the length is exact."""
+    ids_row = np.asarray(ids_row, dtype=np.int64)
+    lists, lengths = vo.select_mass(logits_row[None], mass, k_min, k_max)
+    n_ref, n = int(lengths[0]), len(ids_row)
+    exact = n == n_ref
+    if not exact:
+        assert abs(n - n_ref) == 1, f"length {n}, oracle {n_ref}"
+        p = np.exp(logits_row - logits_row.max())
+        p /= p.sum()
+        order = np.lexsort((np.arange(len(logits_row)), -logits_row))
+        crossing = np.cumsum(p[order])[min(n, n_ref) - 1]
+        assert abs(crossing - mass) <= MASS_BAND, (
+            f"length {n} vs oracle {n_ref} with prefix mass {crossing:.6f}, mass {mass}")
+    check_selection_row(ids_row, logits_row, n)
+    return exact

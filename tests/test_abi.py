@@ -37,7 +37,9 @@ def test_header_declares_the_required_entry_points():
     for need in ("vsa_forward", "vsa_backward", "block_sparse_attn_varlen",
                  "block_sparse_attn_varlen_backward", "vsa_forward_workspace_bytes",
                  "vsa_backward_workspace_bytes", "vsa_saved_bytes", "vsa_status_string",
-                 "vsa_cube_permute_pool", "vsa_coarse_topk", "vsa_fine_forward"):
+                 "vsa_cube_permute_pool", "vsa_coarse_topk", "vsa_fine_forward",
+                 "vsa_forward_mass", "vsa_forward_mass_workspace_bytes", "vsa_coarse_select_mass",
+                 "vsa_pack_lists"):
         assert need in names
 
 
@@ -130,3 +132,39 @@ def test_stage_calls_reject_bad_arguments(lib):
     assert lib.vsa_probe_tile_gather(FAKE, FAKE, 1, 8, 128, FAKE, 2, 3, FAKE, None) == 1
     assert lib.vsa_probe_tile_gather(FAKE, FAKE, 1, 8, 96, FAKE, 2, 1, FAKE, None) == 1
     assert lib.vsa_probe_tile_gather(FAKE, FAKE, 1, 8, 128, FAKE, 9, 1, FAKE, None) == 1
+
+
+def test_mass_rule_calls_reject_bad_arguments(lib):
+    BF = _lib.VSA_BF16
+    B, nh, D, T, H, W = 1, 2, 64, 8, 8, 8  # 8 cubes
+    fw = lib.vsa_forward_workspace_bytes(B, nh, D, T, H, W, BF)
+    mw = lib.vsa_forward_mass_workspace_bytes(B, nh, D, T, H, W, BF, 4)
+    # forward workspace + B*heads*Nc counts + B*heads*Nc*k_max padded ids
+    assert mw >= fw + 4 * (B * nh * 8) + 4 * (B * nh * 8 * 4)
+    assert lib.vsa_forward_mass_workspace_bytes(B, nh, D, T, H, W, BF, 0) == 0
+    assert lib.vsa_forward_mass_workspace_bytes(B, nh, D, T, H, W, BF, 9) == 0  # k_max > Nc
+
+    def fwd(mass, k_min, k_max, ws=1 << 40, offs=FAKE, ids=FAKE):
+        return lib.vsa_forward_mass(FAKE, FAKE, FAKE, FAKE, FAKE, B, nh, D, T, H, W, mass, k_min,
+                                    k_max, BF, FAKE, offs, ids, None, FAKE, ws, None)
+    assert fwd(0.0, 1, 4) == INVALID
+    assert fwd(1.5, 1, 4) == INVALID
+    assert fwd(float("nan"), 1, 4) == INVALID
+    assert fwd(0.5, 0, 4) == INVALID
+    assert fwd(0.5, 5, 4) == INVALID
+    assert fwd(0.5, 1, 9) == INVALID
+    assert fwd(0.5, 1, 4, offs=None) == INVALID
+    assert fwd(0.5, 1, 4, ids=None) == INVALID
+    assert fwd(0.5, 1, 4, ws=16) == WORKSPACE
+
+    def coarse(mass, k_min, k_max, dtype=BF, counts=FAKE):
+        return lib.vsa_coarse_select_mass(FAKE, FAKE, FAKE, 1, 1, 64, 8, mass, k_min, k_max, dtype,
+                                          FAKE, FAKE, counts, FAKE, None)
+    assert coarse(0.5, 1, 9) == INVALID
+    assert coarse(-0.1, 1, 4) == INVALID
+    assert coarse(0.5, 1, 4, dtype=7) == INVALID
+    assert coarse(0.5, 1, 4, counts=None) == INVALID
+    assert lib.vsa_pack_lists(FAKE, FAKE, -1, 4, FAKE, FAKE, None) == INVALID
+    assert lib.vsa_pack_lists(FAKE, FAKE, 4, 0, FAKE, FAKE, None) == INVALID
+    assert lib.vsa_pack_lists(FAKE, FAKE, 4, 4, None, FAKE, None) == INVALID
+    assert lib.vsa_pack_lists(FAKE, FAKE, 1 << 20, 1 << 12, FAKE, FAKE, None) == UNSUPPORTED

@@ -1,0 +1,164 @@
+"""GPU parity of the stand-in variable-length selection (shortest
+logit-ranked prefix of key cubes reaching a coarse probability mass, length
+clamped; an assumption of this library, since the pages leave VSA2's router
+undefined) and of the forward that feeds its lists to the variable-length
+fine stage.  Lists are checked against the fp64 oracle's rule (length exact
+except where the prefix mass crosses the threshold within rounding); outputs
+and gradients against the oracle under the GPU's own lists."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import vsa_oracle as vo
+from tests.gpu_util import assert_close, check_mass_row, dev, host64, log
+from workloads import WORKLOADS, make_inputs, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = torch.float32, torch.bfloat16
+GRADS = ("dq", "dk", "dv", "dgc", "dgf")
+
+
+def _vsa():
+    import trainable_block_sparse_cube_amd as vsa
+    return vsa
+
+
+def _check_rows(counts, ids, S, mass, k_min, k_max):
+    """counts [..., Nc], padded ids [..., Nc, k_max], fp64 logits S [..., Nc, Nc];
+    returns the number of rows whose length sat in the rounding band."""
+    banded = 0
+    for idx in np.ndindex(counts.shape):
+        n = int(counts[idx])
+        assert k_min <= n <= k_max
+        if not check_mass_row(ids[idx][:n], S[idx], mass, k_min, k_max):
+            banded += 1
+    return banded
+
+
+# (mass, k_min, k_max): unclamped, clamped below, clamped above, one fixed
+# length, and lists longer than 64 (the ranking's bitwise-search path)
+CASES = [(0.05, 1, 96), (0.3, 1, 96), (0.6, 4, 80), (0.9, 8, 40), (0.5, 16, 16), (0.97, 1, 96)]
+
+
+@pytest.mark.parametrize("prec", [F32, BF16], ids=["fp32-products", "bf16x3-products"])
+def test_mass_stage_against_oracle(prec):
+    vsa = _vsa()
+    B, nh, D, grid = 1, 2, 128, (16, 16, 24)  # 96 cubes
+    log(f"mass-rule coarse stage, {prec}")
+    inp = make_inputs(B, nh, D, grid, dtype="bf16", seed=51)
+    q, k, v = (dev(inp[n], BF16) for n in "qkv")
+    _, _, _, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, grid, with_q_tiles=False)
+    ref = oracle.forward(inp["q"], inp["k"], inp["v"], inp["gc"], inp["gf"], grid, 1)
+    S = ref["S"]
+    for mass, k_min, k_max in CASES:
+        oc, lse, counts, ids = vsa.vsa_coarse_select_mass(qc, kc, vc, mass, k_min, k_max, input_dtype=prec)
+        torch.cuda.synchronize()
+        banded = _check_rows(counts.cpu().numpy(), ids.cpu().numpy(), S, mass, k_min, k_max)
+        log(f"  mass {mass} [{k_min}, {k_max}]: {banded} rows in the rounding band")
+        assert_close(host64(oc), ref["oc"], F32, "oc")
+    # a fixed length reproduces the top-K stage exactly
+    _, _, counts, ids = vsa.vsa_coarse_select_mass(qc, kc, vc, 0.5, 7, 7, input_dtype=prec)
+    _, _, sel = vsa.vsa_coarse_topk(qc, kc, vc, 7, input_dtype=prec)
+    torch.cuda.synchronize()
+    assert torch.all(counts == 7)
+    assert torch.equal(ids, sel)
+
+
+def test_pack_lists_is_exact():
+    vsa = _vsa()
+    rng = np.random.default_rng(3)
+    n_rows, k_max = 10007, 13  # several scan passes, a ragged last one
+    counts = rng.integers(0, k_max + 1, n_rows).astype(np.int32)
+    counts[:5] = 0
+    counts[-3:] = k_max
+    padded = rng.integers(0, 1 << 20, (n_rows, k_max)).astype(np.int32)
+    offs, ids = vsa.pack_lists(torch.from_numpy(counts).cuda(), torch.from_numpy(padded).cuda())
+    torch.cuda.synchronize()
+    exp_offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    np.testing.assert_array_equal(offs.cpu().numpy(), exp_offs)
+    exp_ids = np.concatenate([padded[r, :counts[r]] for r in range(n_rows)])
+    np.testing.assert_array_equal(ids.cpu().numpy()[:exp_offs[-1]], exp_ids)
+    offs, _ = vsa.pack_lists(torch.zeros(0, dtype=torch.int32, device="cuda"),
+                             torch.zeros((0, 4), dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert offs.cpu().tolist() == [0]
+
+
+def _lists(offs, ids, B, nh, nc):
+    return oracle.lists_from_csr(offs.cpu().numpy(), ids.cpu().numpy(), B, nh, nc)
+
+
+@pytest.mark.parametrize("dt,D", [(F32, 64), (BF16, 128), (BF16, 64)])
+def test_forward_mass_small_full_compare(dt, D):
+    vsa = _vsa()
+    B, nh, grid, (mass, k_min, k_max) = 2, 2, (8, 8, 12), (0.4, 2, 10)  # 12 cubes
+    log(f"mass-rule forward {dt} D={D}")
+    inp = make_inputs(B, nh, D, grid, dtype="f32" if dt == F32 else "bf16", seed=52)
+    q, k, v, gc, gf = (dev(inp[n], dt) for n in ("q", "k", "v", "gc", "gf"))
+    out, offs, ids, _ = vsa.vsa_forward_mass(q, k, v, gc, gf, grid, mass, k_min, k_max)
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp["q"], inp["k"], inp["v"], inp["gc"], inp["gf"], grid, 1)
+    o = offs.cpu().numpy()
+    counts = np.diff(o).reshape(B, nh, 12)
+    padded = np.zeros((B, nh, 12, k_max), dtype=np.int64)
+    flat = ids.cpu().numpy()
+    for r, (a, b) in enumerate(zip(o[:-1], o[1:])):
+        padded.reshape(-1, k_max)[r, :b - a] = flat[a:b]
+    _check_rows(counts, padded, ref["S"], mass, k_min, k_max)
+    lists = _lists(offs, ids, B, nh, 12)
+    want = oracle.forward_with_sets(inp["q"], inp["k"], inp["v"], inp["gc"], inp["gf"], grid, lists)
+    assert_close(host64(out), want["o"], dt, "out")
+
+
+def test_forward_mass_then_varlen_backward():
+    vsa = _vsa()
+    B, nh, D, grid = 1, 2, 128, (8, 8, 12)
+    log("mass-rule forward + backward")
+    inp = make_inputs(B, nh, D, grid, dtype="bf16", seed=53, with_dout=True)
+    q, k, v, gc, gf, do = (dev(inp[n], BF16) for n in ("q", "k", "v", "gc", "gf", "dout"))
+    out, offs, ids, saved = vsa.vsa_forward_mass(q, k, v, gc, gf, grid, 0.35, 1, 12, save=True)
+    grads = vsa.block_sparse_attn_varlen_backward(q, k, v, gc, gf, do, offs, ids, saved, grid)
+    torch.cuda.synchronize()
+    lists = _lists(offs, ids, B, nh, 12)
+    ref = oracle.backward(inp["q"], inp["k"], inp["v"], inp["gc"], inp["gf"], inp["dout"], grid, lists)
+    for name, g in zip(GRADS, grads):
+        assert_close(host64(g), ref[name], BF16, name)
+
+
+def test_forward_mass_full_size_sampled():
+    """61440 tokens (12 heads, head_dim 128), mass 0.2, lengths in [8, 64]:
+    list lengths and ids of sampled query cubes against the oracle's rule,
+    their output rows against the oracle under the GPU's lists, and list
+    properties over every row."""
+    vsa = _vsa()
+    w = WORKLOADS["long61k"]
+    mass, k_min, k_max = 0.2, 8, 64
+    log("full-size mass-rule forward long61k: drawing inputs")
+    inp = workload_inputs(w, with_varlen=False)
+    q, k, v, gc, gf = (dev(inp[n], BF16) for n in ("q", "k", "v", "gc", "gf"))
+    log("full-size mass-rule forward long61k: running")
+    out, offs, ids, _ = vsa.vsa_forward_mass(q, k, v, gc, gf, w.grid, mass, k_min, k_max)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out.float()).all())
+    o = offs.cpu().numpy().astype(np.int64)
+    flat = ids.cpu().numpy()
+    counts = np.diff(o)
+    assert counts.min() >= k_min and counts.max() <= k_max
+    nc = w.n_cubes
+    rng = np.random.default_rng(7)
+    outs, refs, banded = [], [], 0
+    for _ in range(12):
+        b, h, c = 0, int(rng.integers(w.heads)), int(rng.integers(nc))
+        r = (b * w.heads + h) * nc + c
+        row = flat[o[r]:o[r + 1]]
+        assert np.all(np.diff(row) > 0) and row.min() >= 0 and row.max() < nc
+        rows, o_ref, _, logits = oracle.query_cube_output(
+            inp["q"], inp["k"], inp["v"], inp["gc"], inp["gf"], w.grid, b, h, c, row)
+        if not check_mass_row(row, logits, mass, k_min, k_max):
+            banded += 1
+        outs.append(out[b, torch.from_numpy(rows).cuda(), h].float().cpu().numpy())
+        refs.append(o_ref)
+    assert_close(np.stack(outs), np.stack(refs), BF16, "long61k mass-rule sampled rows")
+    log(f"  mean list length {counts.mean():.1f}; {banded}/12 sampled rows in the rounding band")

@@ -16,6 +16,7 @@ _p = ctypes.c_void_p
 _i = ctypes.c_int
 _i64 = ctypes.c_int64
 _sz = ctypes.c_size_t
+_f = ctypes.c_float
 
 # name -> (restype, argtypes); mirrors include/vsa.h
 SIGNATURES = {
@@ -31,6 +32,10 @@ SIGNATURES = {
     "vsa_cube_permute_pool": (_i, [_p] * 3 + [_i] * 7 + [_p] * 6 + [_p]),
     "vsa_coarse_topk": (_i, [_p] * 3 + [_i] * 6 + [_p] * 3 + [_p]),
     "vsa_fine_forward": (_i, [_p] * 6 + [_i] * 6 + [_p, _p, _i, _i, _p, _p, _p, _p]),
+    "vsa_forward_mass_workspace_bytes": (_sz, [_i] * 8),
+    "vsa_forward_mass": (_i, [_p] * 5 + [_i] * 6 + [_f, _i, _i, _i] + [_p] * 5 + [_sz, _p]),
+    "vsa_coarse_select_mass": (_i, [_p] * 3 + [_i] * 4 + [_f, _i, _i, _i] + [_p] * 4 + [_p]),
+    "vsa_pack_lists": (_i, [_p, _p, _i, _i, _p, _p, _p]),
     # include/vsa_probe.h
     "vsa_probe_tile_gather": (_i, [_p, _p, _i, _i, _i, _p, _i, _i, _p, _p]),
 }

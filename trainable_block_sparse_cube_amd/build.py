@@ -20,6 +20,7 @@ SOURCES = [
     "vsa_api.hip",
     "permute_pool.hip",
     "coarse_topk.hip",
+    "lists.hip",
     "fine_fwd.hip",
     "backward.hip",
     "probe_gather.hip",

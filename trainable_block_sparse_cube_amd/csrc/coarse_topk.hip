@@ -172,6 +172,51 @@ __device__ __forceinline__ void select_row(const uint32_t (&keys)[MAXJ], int nc,
   }
 }
 
+// Length of a row's list under the mass rule: the shortest prefix of the
+// ranking (order key descending, index ascending) whose probability mass
+// reaches `mass`, clamped to [k_min, k_max].  e[j] * inv is the
+// probability of entry 64 j + lane (0 past the end).  The mass of all
+// entries with key >= t falls as t grows, so the largest t whose mass still
+// reaches `mass` comes from a greedy bitwise search (wave sums are
+// bitwise uniform across lanes); the entries strictly above it carry less
+// than `mass`, and entries equal to it (bitwise-equal logits, hence equal
+// probabilities) are added lowest id first until the mass is reached.
+// Total mass below `mass` (rounding) gives every entry.
+template <int MAXJ>
+__device__ __forceinline__ int mass_length(const uint32_t (&keys)[MAXJ], const float (&e)[MAXJ],
+                                           float inv, int nc, float mass, int k_min, int k_max) {
+  float p[MAXJ];
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) p[j] = e[j] * inv;
+  uint32_t thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = thr | (1u << bit);
+    float a = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j)
+      if (64 * j < nc) a += keys[j] >= c ? p[j] : 0.f;
+    if (wave_sum(a) >= mass) thr = c;
+  }
+  int n_gt = 0, n_eq = 0;
+  float m_gt = 0.f, p_eq = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    if (64 * j < nc) {
+      const bool valid = keys[j] != 0u;
+      const bool gt = valid && keys[j] > thr, eq = valid && keys[j] == thr;
+      n_gt += __popcll(__ballot(gt));
+      n_eq += __popcll(__ballot(eq));
+      m_gt += gt ? p[j] : 0.f;
+      p_eq = fmaxf(p_eq, eq ? p[j] : 0.f);
+    }
+  }
+  m_gt = wave_sum(m_gt);
+  p_eq = wave_max(p_eq);
+  int n = n_gt;
+  for (float acc = m_gt; n - n_gt < n_eq && acc < mass; ++n) acc += p_eq;
+  return min(max(n, k_min), k_max);
+}
+
 // One workgroup: R = 16 query rows of one (batch, head), 8 waves.
 // Matrix products use v_mfma_f32_16x16x4f32 (fp32 in, fp32 accumulate).
 // Lane l of a 16x16x4 step supplies row/column l % 16 and k-slice l / 16.
@@ -179,7 +224,8 @@ template <int D, int MAXJ, bool X3>
 __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
     const float* __restrict__ qc, const float* __restrict__ kc,
     const float* __restrict__ vc, int nc, int topk, float scale,
-    float* __restrict__ oc, float* __restrict__ lse, int32_t* __restrict__ sel) {
+    float* __restrict__ oc, float* __restrict__ lse, int32_t* __restrict__ sel,
+    float mass, int k_min, int k_max, int32_t* __restrict__ counts) {
   constexpr int R = 16;
   constexpr int DQ = D / 4;          // head_dim slice per lane group
   constexpr int NCW = D / 16;        // waves that own a 16-column output block
@@ -291,13 +337,14 @@ __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
       const int idx = 64 * j + lane;
       sv[j] = (64 * j < nc && idx < nc) ? Srow[idx] : -INFINITY;
     }
-    if (topk > 0) {
-      uint32_t keys[MAXJ];
+    uint32_t keys[MAXJ];
+    if (topk > 0 || counts) {
 #pragma unroll
       for (int j = 0; j < MAXJ; ++j) keys[j] = sv[j] == -INFINITY ? 0u : order_key(sv[j]);
+    }
+    if (topk > 0 && !counts)
       select_row<MAXJ>(keys, nc, topk, lane, cand_k + wave * kCandCap, cand_i + wave * kCandCap,
                        sel + ((int64_t)bh * nc + row) * topk);
-    }
     float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < MAXJ; ++j) m = fmaxf(m, sv[j]);
@@ -312,6 +359,12 @@ __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
     }
     z = wave_sum(z);
     const float inv = 1.0f / z;
+    if (counts) {  // mass rule: this row's length, then its top-n by the same ranking
+      const int n = mass_length<MAXJ>(keys, sv, inv, nc, mass, k_min, k_max);
+      if (lane == 0) counts[(int64_t)bh * nc + row] = n;
+      select_row<MAXJ>(keys, nc, n, lane, cand_k + wave * kCandCap, cand_i + wave * kCandCap,
+                       sel + ((int64_t)bh * nc + row) * k_max);
+    }
     if constexpr (X3) {
       // P as two bf16 planes in the row's own storage: hi at [0, s_pitch),
       // lo at [s_pitch, 2 s_pitch) (bf16 elements), zero past nc.
@@ -447,7 +500,7 @@ hipError_t launch_coarse_dj(const CoarseArgs& a, hipStream_t st) {
   }
   dim3 grid((unsigned)((a.nc + 15) / 16), (unsigned)(a.B * a.heads));
   kern<<<grid, 64 * kNW, lds, st>>>(a.qc, a.kc, a.vc, a.nc, a.topk, 1.0f / sqrtf((float)D),
-                                a.oc, a.lse, a.sel);
+                                a.oc, a.lse, a.sel, a.mass, a.k_min, a.k_max, a.counts);
   return hipGetLastError();
 }
 

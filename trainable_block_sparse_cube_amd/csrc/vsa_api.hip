@@ -73,13 +73,30 @@ size_t saved_layout(const Shape& s, char* base, Saved* sv) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_HIP; }
 
-// Shared body of vsa_forward and block_sparse_attn_varlen.
+// Mass-rule selection inside a forward: the coarse stage writes per-row
+// lengths and padded lists into the workspace, then they are packed into
+// the caller's CSR buffers, which the fine stage reads.
+struct MassRule {
+  float mass;
+  int k_min, k_max;
+  int32_t *offsets, *ids;  // caller's CSR output
+};
+
+// Workspace beyond the forward's own for the mass rule: counts and padded
+// lists.
+size_t mass_ws_bytes(const Shape& s, int k_max) {
+  const size_t rows = (size_t)s.B * s.heads * s.nc;
+  return align_up(rows * sizeof(int32_t)) + align_up(rows * (size_t)k_max * sizeof(int32_t));
+}
+
+// Shared body of vsa_forward, block_sparse_attn_varlen and vsa_forward_mass.
 int forward_impl(const void* q, const void* k, const void* v, const void* gc, const void* gf,
                  const Shape& s, int topk, const int32_t* offs, const int32_t* ids,
                  int32_t* sel, void* out, void* saved, void* ws, size_t ws_bytes,
-                 hipStream_t st) {
+                 hipStream_t st, const MassRule* mr = nullptr) {
   FwdWorkspace w;
-  if (ws_bytes < fwd_ws_layout(s, nullptr, nullptr)) return VSA_ERR_WORKSPACE;
+  const size_t fwd_bytes = fwd_ws_layout(s, nullptr, nullptr);
+  if (ws_bytes < fwd_bytes + (mr ? mass_ws_bytes(s, mr->k_max) : 0)) return VSA_ERR_WORKSPACE;
   fwd_ws_layout(s, (char*)ws, &w);
   float *oc = w.oc, *lse_c = w.lse_c, *lse_f = nullptr, *of = nullptr;
   if (saved) {
@@ -94,8 +111,24 @@ int forward_impl(const void* q, const void* k, const void* v, const void* gc, co
   hipError_t e = launch_permute_pool(pa, st);
   if (e != hipSuccess) return VSA_ERR_HIP;
   CoarseArgs ca{w.qc, w.kc, w.vc, s.B, s.heads, s.D, (int)s.nc, offs ? 0 : topk, oc, lse_c, sel, bf};
+  const int rows = (int)((int64_t)s.B * s.heads * s.nc);
+  int32_t* counts = nullptr;
+  int32_t* padded = nullptr;
+  if (mr) {
+    counts = (int32_t*)((char*)ws + fwd_bytes);
+    padded = (int32_t*)((char*)counts + align_up((size_t)rows * sizeof(int32_t)));
+    ca.topk = 0;
+    ca.sel = padded;
+    ca.mass = mr->mass; ca.k_min = mr->k_min; ca.k_max = mr->k_max; ca.counts = counts;
+  }
   e = launch_coarse_topk(ca, st);
   if (e != hipSuccess) return VSA_ERR_HIP;
+  if (mr) {
+    e = launch_pack_lists(counts, padded, rows, mr->k_max, mr->offsets, mr->ids, st);
+    if (e != hipSuccess) return VSA_ERR_HIP;
+    offs = mr->offsets;
+    ids = mr->ids;
+  }
   FineArgs fa{q, w.kp, w.vp, oc, gc, gf, s.B, s.heads, s.D, s.T, s.H, s.W,
               offs, offs ? ids : sel, topk, bf, out, lse_f, of};
   return hip_status(launch_fine_forward(fa, st));
@@ -217,6 +250,64 @@ int block_sparse_attn_varlen(const void* q, const void* k, const void* v,
   if (n_list_entries > INT_MAX) return VSA_ERR_UNSUPPORTED;
   return forward_impl(q, k, v, gate_c, gate_f, s, 0, kv_offsets, kv_ids, nullptr, out, saved,
                       workspace, workspace_bytes, stream);
+}
+
+// Argument checks of the mass rule shared by its entry points.
+static int check_mass(float mass, int k_min, int k_max, int64_t nc, int64_t rows) {
+  if (!(mass > 0.f && mass <= 1.f)) return VSA_ERR_INVALID_ARG;  // also rejects NaN
+  if (k_min < 1 || k_min > k_max || k_max > nc) return VSA_ERR_INVALID_ARG;
+  if (rows * k_max > INT_MAX) return VSA_ERR_UNSUPPORTED;
+  return VSA_OK;
+}
+
+size_t vsa_forward_mass_workspace_bytes(int B, int heads, int head_dim, int T, int H, int W,
+                                        int dtype, int k_max) {
+  Shape s;
+  if (check_shape(B, heads, head_dim, T, H, W, dtype, &s) != VSA_OK) return 0;
+  if (k_max < 1 || k_max > s.nc || (int64_t)B * heads * s.nc * k_max > INT_MAX) return 0;
+  return fwd_ws_layout(s, nullptr, nullptr) + mass_ws_bytes(s, k_max);
+}
+
+int vsa_forward_mass(const void* q, const void* k, const void* v, const void* gate_c,
+                     const void* gate_f, int B, int heads, int head_dim, int T, int H, int W,
+                     float mass, int k_min, int k_max, int dtype, void* out,
+                     int32_t* kv_offsets, int32_t* kv_ids, void* saved, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  Shape s;
+  int st = check_shape(B, heads, head_dim, T, H, W, dtype, &s);
+  if (st != VSA_OK) return st;
+  if (!q || !k || !v || !gate_c || !gate_f || !out || !kv_offsets || !kv_ids || !workspace)
+    return VSA_ERR_INVALID_ARG;
+  st = check_mass(mass, k_min, k_max, s.nc, (int64_t)B * heads * s.nc);
+  if (st != VSA_OK) return st;
+  const MassRule mr{mass, k_min, k_max, kv_offsets, kv_ids};
+  return forward_impl(q, k, v, gate_c, gate_f, s, 0, nullptr, nullptr, nullptr, out, saved,
+                      workspace, workspace_bytes, stream, &mr);
+}
+
+int vsa_coarse_select_mass(const float* qc, const float* kc, const float* vc, int B, int heads,
+                           int head_dim, int n_cubes, float mass, int k_min, int k_max, int dtype,
+                           float* oc, float* lse_c, int32_t* counts, int32_t* ids,
+                           hipStream_t stream) {
+  if (dtype != VSA_F32 && dtype != VSA_BF16) return VSA_ERR_INVALID_ARG;
+  if (B < 1 || heads < 1 || n_cubes < 1) return VSA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return VSA_ERR_UNSUPPORTED;
+  if (n_cubes > coarse_max_cubes(head_dim) || (int64_t)B * heads > 65535) return VSA_ERR_UNSUPPORTED;
+  if (!qc || !kc || !vc || !oc || !lse_c || !counts || !ids) return VSA_ERR_INVALID_ARG;
+  if ((int64_t)B * heads * n_cubes > INT_MAX / 2) return VSA_ERR_UNSUPPORTED;
+  const int st = check_mass(mass, k_min, k_max, n_cubes, (int64_t)B * heads * n_cubes);
+  if (st != VSA_OK) return st;
+  CoarseArgs ca{qc, kc, vc, B, heads, head_dim, n_cubes, 0, oc, lse_c, ids, dtype == VSA_BF16};
+  ca.mass = mass; ca.k_min = k_min; ca.k_max = k_max; ca.counts = counts;
+  return hip_status(launch_coarse_topk(ca, stream));
+}
+
+int vsa_pack_lists(const int32_t* counts, const int32_t* ids_padded, int n_rows, int k_max,
+                   int32_t* kv_offsets, int32_t* kv_ids, hipStream_t stream) {
+  if (n_rows < 0 || k_max < 1) return VSA_ERR_INVALID_ARG;
+  if (!kv_offsets || (n_rows > 0 && (!counts || !ids_padded || !kv_ids))) return VSA_ERR_INVALID_ARG;
+  if ((int64_t)n_rows * k_max > INT_MAX) return VSA_ERR_UNSUPPORTED;
+  return hip_status(launch_pack_lists(counts, ids_padded, n_rows, k_max, kv_offsets, kv_ids, stream));
 }
 
 int vsa_cube_permute_pool(const void* q, const void* k, const void* v,

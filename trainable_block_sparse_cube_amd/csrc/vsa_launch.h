@@ -27,7 +27,18 @@ struct CoarseArgs {
   float *oc, *lse;
   int32_t* sel;  // may be null when topk == 0
   bool x3;       // products as three bf16 MFMAs (bf16 inputs) instead of fp32 MFMA
+  // Mass rule instead of top-K when counts is non-null: per row, the
+  // shortest ranked prefix reaching `mass` of the coarse probability,
+  // length clamped to [k_min, k_max], written to counts[row] and to sel at
+  // stride k_max.
+  float mass = 0.f;
+  int k_min = 0, k_max = 0;
+  int32_t* counts = nullptr;
 };
+// Padded lists -> CSR: offsets[0..n_rows] = exclusive scan of counts, ids
+// packed in row order.
+hipError_t launch_pack_lists(const int32_t* counts, const int32_t* padded, int n_rows, int k_max,
+                             int32_t* offsets, int32_t* ids, hipStream_t st);
 // Largest number of cubes the coarse kernel accepts.
 int coarse_max_cubes(int D);
 hipError_t launch_coarse_topk(const CoarseArgs& a, hipStream_t st);

@@ -97,6 +97,29 @@ def block_sparse_attn_varlen(q, k, v, gate_c, gate_f, grid, kv_offsets, kv_ids, 
     return out, saved
 
 
+def vsa_forward_mass(q, k, v, gate_c, gate_f, grid, mass, k_min, k_max, save=False):
+    """Forward with the stand-in variable-length rule of include/vsa.h (per
+    query cube, the shortest logit-ranked prefix reaching `mass` of the
+    coarse probability, length clamped to [k_min, k_max]).
+    Returns (out, kv_offsets, kv_ids, saved or None).  kv_ids is trimmed to
+    its kv_offsets[-1] entries, which reads that count back to the host
+    (a synchronisation of the current stream)."""
+    lib = _lib.load()
+    B, N, nh, D, T, H, W, dt = _check_inputs(q, k, v, gate_c, gate_f, grid)
+    nc = N // 64
+    out = torch.empty_like(q)
+    offs = torch.empty(B * nh * nc + 1, dtype=torch.int32, device=q.device)
+    ids = torch.empty(B * nh * nc * max(int(k_max), 1), dtype=torch.int32, device=q.device)
+    saved = _workspace(lib.vsa_saved_bytes(B, nh, D, T, H, W), q.device) if save else None
+    wsb = lib.vsa_forward_mass_workspace_bytes(B, nh, D, T, H, W, dt, int(k_max))
+    ws = _workspace(wsb, q.device)
+    st = lib.vsa_forward_mass(_ptr(q), _ptr(k), _ptr(v), _ptr(gate_c), _ptr(gate_f),
+                              B, nh, D, T, H, W, float(mass), int(k_min), int(k_max), dt,
+                              _ptr(out), _ptr(offs), _ptr(ids), _ptr(saved), _ptr(ws), wsb, _stream())
+    _lib.check("vsa_forward_mass", st)
+    return out, offs, ids[:int(offs[-1].item())], saved
+
+
 def vsa_backward(q, k, v, gate_c, gate_f, dout, sel, saved, grid):
     """Gradients of sum(dout * out) for a forward run with save=True.
     Returns (dq, dk, dv, dgate_c, dgate_f); gate gradients are fp32."""
@@ -167,6 +190,37 @@ def vsa_coarse_topk(qc, kc, vc, topk, input_dtype=torch.float32):
                              _DT[input_dtype], _ptr(oc), _ptr(lse), _ptr(sel), _stream())
     _lib.check("vsa_coarse_topk", st)
     return oc, lse, sel
+
+
+def vsa_coarse_select_mass(qc, kc, vc, mass, k_min, k_max, input_dtype=torch.float32):
+    """Coarse stage with the stand-in variable-length rule.  Returns (oc,
+    lse_c, counts [B, heads, Nc], ids [B, heads, Nc, k_max]); row r's list
+    is ids[..., :counts[r]] (ascending)."""
+    lib = _lib.load()
+    B, nh, nc, D = qc.shape
+    oc = torch.empty_like(qc)
+    lse = torch.empty((B, nh, nc), dtype=torch.float32, device=qc.device)
+    counts = torch.empty((B, nh, nc), dtype=torch.int32, device=qc.device)
+    ids = torch.zeros((B, nh, nc, max(int(k_max), 1)), dtype=torch.int32, device=qc.device)
+    st = lib.vsa_coarse_select_mass(_ptr(qc), _ptr(kc), _ptr(vc), B, nh, D, nc, float(mass),
+                                    int(k_min), int(k_max), _DT[input_dtype], _ptr(oc), _ptr(lse),
+                                    _ptr(counts), _ptr(ids), _stream())
+    _lib.check("vsa_coarse_select_mass", st)
+    return oc, lse, counts, ids
+
+
+def pack_lists(counts, ids_padded):
+    """Padded lists -> CSR (kv_offsets [n_rows + 1], kv_ids with capacity
+    n_rows * k_max, of which kv_offsets[-1] entries are written)."""
+    lib = _lib.load()
+    k_max = ids_padded.shape[-1]
+    n_rows = counts.numel()
+    offs = torch.empty(n_rows + 1, dtype=torch.int32, device=counts.device)
+    ids = torch.empty(max(n_rows * k_max, 1), dtype=torch.int32, device=counts.device)
+    st = lib.vsa_pack_lists(_ptr(counts), _ptr(ids_padded), n_rows, k_max, _ptr(offs), _ptr(ids),
+                            _stream())
+    _lib.check("vsa_pack_lists", st)
+    return offs, ids
 
 
 def vsa_fine_forward(q, kp, vp, oc, gate_c, gate_f, grid, kv_ids, topk=0, kv_offsets=None,
