@@ -245,7 +245,11 @@ def extra(a, vsa, torch, stream):
         q, k, v, gc, gf = (dev(inp[n]) for n in ("q", "k", "v", "gc", "gf"))
         ms = timed(lambda: vsa.vsa_forward(q, k, v, gc, gf, w.grid, K), steps, warm, stream)
         fl = fine_flops(w.B, w.heads, w.N, K, w.head_dim) + coarse_flops(w.B, w.heads, w.n_cubes, w.head_dim)
-        return {"ms": ms, "TFLOPs": fl / (ms * 1e-3) / 1e12}
+        # the coarse stage's share of the forward at this length
+        _, _, _, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, w.grid, with_q_tiles=False)
+        ms_c = timed(lambda: vsa.vsa_coarse_topk(qc, kc, vc, K, input_dtype=torch.bfloat16), steps, warm, stream)
+        return {"ms": ms, "TFLOPs": fl / (ms * 1e-3) / 1e12, "coarse_topk_ms": ms_c,
+                "coarse_share": ms_c / ms}
 
     # dense reference through the same fine kernel: every query cube lists
     # all Nc key cubes (plain block attention over the whole clip)
@@ -287,6 +291,23 @@ def extra(a, vsa, torch, stream):
                                                    for c in range(len(s_np) - 1)) / (len(s_np) - 1))}
     del q, k, v, gc, gf, kp, vp, fout, inp
 
+    # the stand-in variable-length rule (mass 0.2 of the coarse probability,
+    # lists clamped to [8, 64]) on the headline shape
+    w = WORKLOADS["long61k"]
+    inp = workload_inputs(w, with_varlen=False)
+    q, k, v, gc, gf = (dev(inp[n]) for n in ("q", "k", "v", "gc", "gf"))
+    _, offs, _, _ = vsa.vsa_forward_mass(q, k, v, gc, gf, w.grid, 0.2, 8, 64, trim=False)
+    n_pairs = int(offs[-1].item())
+    ms = timed(lambda: vsa.vsa_forward_mass(q, k, v, gc, gf, w.grid, 0.2, 8, 64, trim=False),
+               steps, warm, stream)
+    fl = fine_flops_lists(n_pairs, w.head_dim) + coarse_flops(w.B, w.heads, w.n_cubes, w.head_dim)
+    ext["long61k_mass0.2_forward"] = {"ms": ms, "TFLOPs": fl / (ms * 1e-3) / 1e12,
+                                      "mean_list_len": n_pairs / (w.B * w.heads * w.n_cubes),
+                                      "rule": "shortest logit-ranked prefix with coarse mass >= 0.2, "
+                                              "length clamped to [8, 64] (stand-in, not the pages' router)"}
+    del q, k, v, gc, gf, offs, inp
+
+    ext["long61k_k32_forward"] = fwd_case("long61k", 32)
     ext["long61k_k16_forward"] = fwd_case("long61k", 16)
     ext["pretrain16k_k32_forward"] = fwd_case("pretrain16k", 32)
     ext["large70k_k32_forward"] = fwd_case("large70k", 32)

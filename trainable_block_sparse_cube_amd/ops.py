@@ -97,13 +97,14 @@ def block_sparse_attn_varlen(q, k, v, gate_c, gate_f, grid, kv_offsets, kv_ids, 
     return out, saved
 
 
-def vsa_forward_mass(q, k, v, gate_c, gate_f, grid, mass, k_min, k_max, save=False):
+def vsa_forward_mass(q, k, v, gate_c, gate_f, grid, mass, k_min, k_max, save=False, trim=True):
     """Forward with the stand-in variable-length rule of include/vsa.h (per
     query cube, the shortest logit-ranked prefix reaching `mass` of the
     coarse probability, length clamped to [k_min, k_max]).
-    Returns (out, kv_offsets, kv_ids, saved or None).  kv_ids is trimmed to
-    its kv_offsets[-1] entries, which reads that count back to the host
-    (a synchronisation of the current stream)."""
+    Returns (out, kv_offsets, kv_ids, saved or None).  With trim, kv_ids is
+    cut to its kv_offsets[-1] entries, which reads that count back to the
+    host (a synchronisation of the current stream); without, it keeps its
+    B*heads*Nc*k_max capacity and nothing waits."""
     lib = _lib.load()
     B, N, nh, D, T, H, W, dt = _check_inputs(q, k, v, gate_c, gate_f, grid)
     nc = N // 64
@@ -117,7 +118,7 @@ def vsa_forward_mass(q, k, v, gate_c, gate_f, grid, mass, k_min, k_max, save=Fal
                               B, nh, D, T, H, W, float(mass), int(k_min), int(k_max), dt,
                               _ptr(out), _ptr(offs), _ptr(ids), _ptr(saved), _ptr(ws), wsb, _stream())
     _lib.check("vsa_forward_mass", st)
-    return out, offs, ids[:int(offs[-1].item())], saved
+    return out, offs, ids[:int(offs[-1].item())] if trim else ids, saved
 
 
 def vsa_backward(q, k, v, gate_c, gate_f, dout, sel, saved, grid):
