@@ -87,13 +87,40 @@ def cube_members(T, H, W):
     return members
 
 
-def pool(x, T, H, W):
+def pool(x, T, H, W, op="mean"):
     """Mean of the 64 tokens of each cube ([VSA-sum, Approach]: mean pooling).
 
+    op="max" takes the per-channel maximum instead, the alternative that the
+    pooling ablation compares against ([VSA-sum, Surprising findings]: mean
+    pooling did better than max and convolutional pooling).
     x: [N, D] for one (batch, head).  Returns [Nc, D].
     """
     members = cube_members(T, H, W)
-    return x[members].mean(axis=1)
+    if op == "mean":
+        return x[members].mean(axis=1)
+    if op == "max":
+        return x[members].max(axis=1)
+    raise ValueError(f"unknown pooling {op!r}")
+
+
+def cube_attention_mass(q, k, grid, b, h, c, scale=None):
+    """Share of the dense attention of query cube c that lands on each key
+    cube, for one (batch b, head h): every query token of cube c attends to
+    all N keys with a softmax of s q.k; its weights are summed over the 64
+    tokens of each key cube and averaged over the cube's 64 queries.  The
+    key cubes with the most mass are the "critical" ones that the coarse
+    stage tries to find ([VSA-abs]: the attention mass concentrates on a
+    small subset of positions; [VSA-sum, Key results] lists critical-token
+    prediction accuracy among the metrics).  Returns [Nc], summing to 1.
+    """
+    T, H, W = grid
+    members = cube_members(T, H, W)
+    D = q.shape[-1]
+    s = 1.0 / np.sqrt(D) if scale is None else scale
+    Q = _as64(q[b, members[c], h])  # [64, D]
+    K = _as64(k[b, :, h])           # [N, D]
+    Pm, _ = _softmax_rows(s * (Q @ K.T))
+    return Pm[:, members].sum(axis=2).mean(axis=0)
 
 
 def _softmax_rows(logits):

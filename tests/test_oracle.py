@@ -68,6 +68,48 @@ def test_pool_cube_constant_exact_and_sum_invariant():
     np.testing.assert_allclose((64 * vo.pool(y, T, H, W)).sum(0), y.sum(0), rtol=1e-12, atol=1e-12)
 
 
+def _max_pool_by_reshape(x, T, H, W):
+    """Per-cube channel max built from a reshape of the grid, independent of
+    the oracle's member table."""
+    D = x.shape[-1]
+    g = x.reshape(T // 4, 4, H // 4, 4, W // 4, 4, D)
+    return g.max(axis=(1, 3, 5)).reshape(-1, D)
+
+
+def test_max_pool_matches_reshape_and_bounds_mean():
+    T, H, W = 8, 12, 8
+    rng = np.random.default_rng(1)
+    y = rng.standard_normal((T * H * W, 6))
+    mx = vo.pool(y, T, H, W, op="max")
+    np.testing.assert_array_equal(mx, _max_pool_by_reshape(y, T, H, W))
+    assert np.all(mx >= vo.pool(y, T, H, W))
+    vals = rng.standard_normal((vo.cube_members(T, H, W).shape[0], 6))
+    cube, _ = vo.token_cube_map(T, H, W)
+    np.testing.assert_array_equal(vo.pool(vals[cube], T, H, W, op="max"), vals)
+    with pytest.raises(ValueError):
+        vo.pool(y, T, H, W, op="median")
+
+
+def test_cube_attention_mass_against_library_softmax():
+    from scipy.special import softmax
+    T, H, W = 8, 8, 12  # 12 cubes
+    inp = small(nh=2, D=16, seed=4, grid=(T, H, W))
+    cube, _ = vo.token_cube_map(T, H, W)
+    members = vo.cube_members(T, H, W)
+    for b, h, c in ((0, 0, 0), (0, 1, 7), (0, 1, 11)):
+        m = vo.cube_attention_mass(inp["q"], inp["k"], (T, H, W), b, h, c)
+        assert abs(m.sum() - 1.0) < 1e-12 and np.all(m > 0)
+        Q = inp["q"][b, members[c], h].astype(np.float64)
+        K = inp["k"][b, :, h].astype(np.float64)
+        w = softmax(np.einsum("id,jd->ij", Q, K) / 4.0, axis=1)  # 1/sqrt(16)
+        want = np.bincount(cube, weights=w.mean(axis=0), minlength=12)
+        np.testing.assert_allclose(m, want, rtol=1e-12, atol=1e-15)
+    k = inp["k"].copy()
+    k[:] = k[:, :1]  # every key identical: every cube gets 1/Nc
+    np.testing.assert_allclose(vo.cube_attention_mass(inp["q"], k, (T, H, W), 0, 0, 3), np.full(12, 1 / 12),
+                               rtol=1e-12)
+
+
 # ---------------------------------------------------------------- step 3: coarse
 def test_coarse_equals_library_attention_on_pooled():
     inp = small()
