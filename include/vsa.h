@@ -192,6 +192,15 @@ int vsa_cube_permute_pool(const void* q, const void* k, const void* v,
                           int dtype, void* qp, void* kp, void* vp,
                           float* qc, float* kc, float* vc, hipStream_t stream);
 
+/* Pooling ablation: the per-channel maximum of each cube's 64 tokens
+ * instead of the mean, for Q, K and V, as fp32 [B, heads, Nc, D] (exact).
+ * The pages found mean pooling better than max pooling ([VSA-sum,
+ * Surprising findings]); the operator entry points always mean-pool.  This
+ * call feeds vsa_coarse_topk to compare the two selections. */
+int vsa_cube_max_pool(const void* q, const void* k, const void* v,
+                      int B, int heads, int head_dim, int T, int H, int W, int dtype,
+                      float* qc, float* kc, float* vc, hipStream_t stream);
+
 /* Coarse stage: Oc [B,heads,Nc,D] fp32, lse_c [B,heads,Nc] fp32 and, when
  * topk > 0, sel_idx [B,heads,Nc,topk]; topk == 0 skips the selection.
  * dtype is the element type of the attention inputs and sets the precision

@@ -39,7 +39,7 @@ def test_header_declares_the_required_entry_points():
                  "vsa_backward_workspace_bytes", "vsa_saved_bytes", "vsa_status_string",
                  "vsa_cube_permute_pool", "vsa_coarse_topk", "vsa_fine_forward",
                  "vsa_forward_mass", "vsa_forward_mass_workspace_bytes", "vsa_coarse_select_mass",
-                 "vsa_pack_lists"):
+                 "vsa_pack_lists", "vsa_cube_max_pool"):
         assert need in names
 
 
@@ -168,3 +168,5 @@ def test_mass_rule_calls_reject_bad_arguments(lib):
     assert lib.vsa_pack_lists(FAKE, FAKE, 4, 0, FAKE, FAKE, None) == INVALID
     assert lib.vsa_pack_lists(FAKE, FAKE, 4, 4, None, FAKE, None) == INVALID
     assert lib.vsa_pack_lists(FAKE, FAKE, 1 << 20, 1 << 12, FAKE, FAKE, None) == UNSUPPORTED
+    assert lib.vsa_cube_max_pool(FAKE, FAKE, FAKE, 1, 1, 64, 8, 8, 6, BF, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.vsa_cube_max_pool(FAKE, FAKE, FAKE, 1, 1, 64, 8, 8, 8, BF, FAKE, None, FAKE, None) == INVALID

@@ -36,6 +36,7 @@ SIGNATURES = {
     "vsa_forward_mass": (_i, [_p] * 5 + [_i] * 6 + [_f, _i, _i, _i] + [_p] * 5 + [_sz, _p]),
     "vsa_coarse_select_mass": (_i, [_p] * 3 + [_i] * 4 + [_f, _i, _i, _i] + [_p] * 4 + [_p]),
     "vsa_pack_lists": (_i, [_p, _p, _i, _i, _p, _p, _p]),
+    "vsa_cube_max_pool": (_i, [_p] * 3 + [_i] * 7 + [_p] * 3 + [_p]),
     # include/vsa_probe.h
     "vsa_probe_tile_gather": (_i, [_p, _p, _i, _i, _i, _p, _i, _i, _p, _p]),
 }

@@ -8,13 +8,17 @@
 // raster layout), writes them as one contiguous cube-major tile, and reduces
 // the 64 rows to their fp32 mean with wavefront shuffles plus a 4-way LDS
 // combine.  The forward writes the K and V tiles (the fine stage reads Q in
-// place); the backward writes Q, K and V tiles.
+// place); the backward writes Q, K and V tiles.  A second instance takes
+// the per-channel maximum instead of the mean and writes no tiles: the
+// pooling ablation ([VSA-sum, Surprising findings]: mean pooling did better
+// than max pooling).  Both reductions are exact in fp32 (the mean's sum of
+// 64 values rounds per addition, like any fp32 sum).
 #include "vsa_device.h"
 #include "vsa_launch.h"
 
 namespace vsa {
 
-template <typename T, int D>
+template <typename T, int D, bool MAXP>
 __global__ __launch_bounds__(256) void permute_pool_kernel(PermutePoolPtrs p, int nh, int Tg, int Hg, int Wg) {
   constexpr int EPC = 16 / sizeof(T);     // elements per 16-byte chunk
   constexpr int CPR = D / EPC;            // chunks per token row
@@ -43,7 +47,7 @@ __global__ __launch_bounds__(256) void permute_pool_kernel(PermutePoolPtrs p, in
   const int ch = tid % CPR;  // this thread's chunk column, fixed over passes
   float acc[EPC];
 #pragma unroll
-  for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+  for (int e = 0; e < EPC; ++e) acc[e] = MAXP ? -INFINITY : 0.f;
 
 #pragma unroll
   for (int ps = 0; ps < PASSES; ++ps) {
@@ -54,7 +58,7 @@ __global__ __launch_bounds__(256) void permute_pool_kernel(PermutePoolPtrs p, in
     T vals[EPC];
     __builtin_memcpy(vals, &raw, 16);
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[e] += to_f32(vals[e]);
+    for (int e = 0; e < EPC; ++e) acc[e] = MAXP ? fmaxf(acc[e], to_f32(vals[e])) : acc[e] + to_f32(vals[e]);
     if (nat) *reinterpret_cast<u32x4*>(nat + tile + (int64_t)s * D + ch * EPC) = raw;
   }
 
@@ -63,7 +67,10 @@ __global__ __launch_bounds__(256) void permute_pool_kernel(PermutePoolPtrs p, in
 #pragma unroll
     for (int o = CPR; o < 64; o <<= 1)
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], o);
+      for (int e = 0; e < EPC; ++e) {
+        const float other = __shfl_xor(acc[e], o);
+        acc[e] = MAXP ? fmaxf(acc[e], other) : acc[e] + other;
+      }
     const int wave = tid >> 6, lane = tid & 63;
     if (lane < CPR) {
 #pragma unroll
@@ -73,8 +80,9 @@ __global__ __launch_bounds__(256) void permute_pool_kernel(PermutePoolPtrs p, in
   __syncthreads();
   if (pooled) {
     for (int d = tid; d < D; d += 256) {
-      const float mean = ((red[0][d] + red[1][d]) + (red[2][d] + red[3][d])) * (1.0f / kCubeTokens);
-      pooled[((int64_t)(b * nh + h) * nc + c) * D + d] = mean;
+      const float r = MAXP ? fmaxf(fmaxf(red[0][d], red[1][d]), fmaxf(red[2][d], red[3][d]))
+                           : ((red[0][d] + red[1][d]) + (red[2][d] + red[3][d])) * (1.0f / kCubeTokens);
+      pooled[((int64_t)(b * nh + h) * nc + c) * D + d] = r;
     }
   }
 }
@@ -83,7 +91,13 @@ template <typename T, int D>
 static hipError_t launch_pp(const PermutePoolArgs& a, hipStream_t st) {
   const int nc = (a.T / 4) * (a.H / 4) * (a.W / 4);
   dim3 grid((unsigned)(a.B * nc * a.heads), 3);
-  permute_pool_kernel<T, D><<<grid, 256, 0, st>>>(a.p, a.heads, a.T, a.H, a.W);
+  if (a.max_pool) {
+    PermutePoolPtrs p = a.p;
+    p.nat[0] = p.nat[1] = p.nat[2] = nullptr;  // pooled values only
+    permute_pool_kernel<T, D, true><<<grid, 256, 0, st>>>(p, a.heads, a.T, a.H, a.W);
+  } else {
+    permute_pool_kernel<T, D, false><<<grid, 256, 0, st>>>(a.p, a.heads, a.T, a.H, a.W);
+  }
   return hipGetLastError();
 }
 

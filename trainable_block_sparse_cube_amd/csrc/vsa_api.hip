@@ -323,6 +323,19 @@ int vsa_cube_permute_pool(const void* q, const void* k, const void* v,
   return hip_status(launch_permute_pool(pa, stream));
 }
 
+int vsa_cube_max_pool(const void* q, const void* k, const void* v, int B, int heads, int head_dim,
+                      int T, int H, int W, int dtype, float* qc, float* kc, float* vc,
+                      hipStream_t stream) {
+  Shape s;
+  int st = check_shape(B, heads, head_dim, T, H, W, dtype, &s);
+  if (st != VSA_OK) return st;
+  if (!q || !k || !v || !qc || !kc || !vc) return VSA_ERR_INVALID_ARG;
+  PermutePoolArgs pa{{{q, k, v}, {nullptr, nullptr, nullptr}, {qc, kc, vc}},
+                     B, heads, head_dim, T, H, W, dtype == VSA_BF16};
+  pa.max_pool = true;
+  return hip_status(launch_permute_pool(pa, stream));
+}
+
 int vsa_coarse_topk(const float* qc, const float* kc, const float* vc,
                     int B, int heads, int head_dim, int n_cubes, int topk, int dtype,
                     float* oc, float* lse_c, int32_t* sel_idx, hipStream_t stream) {

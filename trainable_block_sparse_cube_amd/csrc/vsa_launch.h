@@ -18,6 +18,7 @@ struct PermutePoolArgs {
   PermutePoolPtrs p;
   int B, heads, D, T, H, W;
   bool bf16;
+  bool max_pool = false;  // per-channel max instead of the mean; no tiles written
 };
 hipError_t launch_permute_pool(const PermutePoolArgs& a, hipStream_t st);
 

@@ -177,6 +177,20 @@ def vsa_cube_permute_pool(q, k, v, grid, with_q_tiles=True):
     return (qp, kp, vp, *pooled)
 
 
+def vsa_cube_max_pool(q, k, v, grid):
+    """Per-channel maximum of each cube's 64 tokens of q, k, v (the pooling
+    ablation).  Returns fp32 (qc, kc, vc) [B, heads, Nc, D]."""
+    lib = _lib.load()
+    B, N, nh, D = q.shape
+    T, H, W = grid
+    nc = N // 64
+    pooled = [torch.empty((B, nh, nc, D), dtype=torch.float32, device=q.device) for _ in range(3)]
+    st = lib.vsa_cube_max_pool(_ptr(q), _ptr(k), _ptr(v), B, nh, D, T, H, W, _DT[q.dtype],
+                               *[_ptr(t) for t in pooled], _stream())
+    _lib.check("vsa_cube_max_pool", st)
+    return tuple(pooled)
+
+
 def vsa_coarse_topk(qc, kc, vc, topk, input_dtype=torch.float32):
     """Returns (oc, lse_c, sel or None) for fp32 pooled [B, heads, Nc, D].
     input_dtype, the element type of the attention inputs, sets the product
