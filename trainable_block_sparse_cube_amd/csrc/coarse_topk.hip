@@ -491,13 +491,10 @@ template <int D, int MAXJ, bool X3>
 hipError_t launch_coarse_dj(const CoarseArgs& a, hipStream_t st) {
   const size_t lds = coarse_lds_bytes(a.nc);
   auto kern = coarse_topk_kernel<D, MAXJ, X3>;
-  // Raise the dynamic LDS limit once per kernel instance (host-side call).
-  static size_t lds_limit = 0;
-  if (lds > lds_limit) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    lds_limit = lds;
-  }
+  // Allow this much dynamic LDS (host-side call, made on every launch: the
+  // setting belongs to the current device, and the call is cheap).
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
   dim3 grid((unsigned)((a.nc + 15) / 16), (unsigned)(a.B * a.heads));
   kern<<<grid, 64 * kNW, lds, st>>>(a.qc, a.kc, a.vc, a.nc, a.topk, 1.0f / sqrtf((float)D),
                                 a.oc, a.lse, a.sel, a.mass, a.k_min, a.k_max, a.counts);
