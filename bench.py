@@ -8,7 +8,8 @@ whole forward, counting the sparse FLOPs the method needs (fine stage QK^T
 and PV over the selected cubes plus the dense coarse stage).
 
 The fine kernel is also timed on its own (HIP events on the stream it is
-launched on) for the roofline entry, next to its two floors on the same
+launched on, in the sorted processing order the forward gives it, and in
+natural order for comparison) for the roofline entry, next to its two floors on the same
 data: the library's tile-gather helper (the fine kernel's K/V reads for the
 same selection, no arithmetic) and the fine kernel on a shared selection
 (every query cube picks the same key cubes, so every tile is an L2 hit).
@@ -153,9 +154,15 @@ def main():
     ms_pp = timed(lambda: vsa.vsa_cube_permute_pool(q, k, v, w.grid, with_q_tiles=False),
                   a.steps, a.warmup, stream)
     ms_coarse = timed(lambda: vsa.vsa_coarse_topk(qc, kc, vc, K, input_dtype=torch.bfloat16), a.steps, a.warmup, stream)
+    # the processing order the forward gives the fine kernel (query cubes
+    # sorted by their lists' middle entries), and the fine kernel with it
+    order = vsa.vsa_fine_order(sel2, w.B, w.heads, w.n_cubes, topk=K)
+    ms_order = timed(lambda: vsa.vsa_fine_order(sel2, w.B, w.heads, w.n_cubes, topk=K), a.steps, a.warmup, stream)
     fout = torch.empty_like(q)
-    ms_fine = timed(lambda: vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, w.grid, sel2, topk=K, out=fout),
-                    a.steps, a.warmup, stream)
+    ms_fine = timed(lambda: vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, w.grid, sel2, topk=K, out=fout,
+                                                 order=order), a.steps, a.warmup, stream)
+    ms_fine_natural = timed(lambda: vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, w.grid, sel2, topk=K, out=fout),
+                            a.steps, a.warmup, stream)
 
     f_fine = fine_flops(w.B, w.heads, w.N, K, w.head_dim)
     f_coarse = coarse_flops(w.B, w.heads, w.n_cubes, w.head_dim)
@@ -176,7 +183,7 @@ def main():
     del shared
     calls = {"step": per_call_ms(step, a.steps, stream),
              "fine": per_call_ms(lambda: vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, w.grid, sel2, topk=K,
-                                                             out=fout), a.steps, stream)}
+                                                             out=fout, order=order), a.steps, stream)}
     counters = measured_counters()
     clk = counters.get("fine_clock_GHz")
     res = {
@@ -195,7 +202,8 @@ def main():
                    "B": w.B, "heads": w.heads, "head_dim": w.head_dim, "grid": list(w.grid),
                    "tokens": w.N, "topk": K, "parallelism": "single GPU"},
         "frac_of_peak_whole_forward": (f_fine + f_coarse) / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-        "stages_ms": {"permute_pool": ms_pp, "coarse_topk": ms_coarse, "fine": ms_fine},
+        "stages_ms": {"permute_pool": ms_pp, "coarse_topk": ms_coarse, "fine_order": ms_order,
+                      "fine": ms_fine, "fine_in_natural_order": ms_fine_natural},
         "stage_GBs": {"permute_pool": pp_bytes / (ms_pp * 1e-3) / 1e9,
                       "coarse_topk": coarse_bytes / (ms_coarse * 1e-3) / 1e9},
         "fine_TFLOPs": fine_tflops,
@@ -278,8 +286,9 @@ def extra(a, vsa, torch, stream):
     _, kp, vp, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, w.grid, with_q_tiles=False)
     oc, _, sel = vsa.vsa_coarse_topk(qc, kc, vc, 32, input_dtype=torch.bfloat16)
     fout = torch.empty_like(q)
-    ms_fine_s = timed(lambda: vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, w.grid, sel, topk=32, out=fout),
-                      steps, warm, stream)
+    order_s = vsa.vsa_fine_order(sel, w.B, w.heads, w.n_cubes, topk=32)
+    ms_fine_s = timed(lambda: vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, w.grid, sel, topk=32, out=fout,
+                                                   order=order_s), steps, warm, stream)
     ms_fwd_s = timed(lambda: vsa.vsa_forward(q, k, v, gc, gf, w.grid, 32), steps, warm, stream)
     s_np = sel[0, 0].cpu().numpy()
     f_s = fine_flops(w.B, w.heads, w.N, 32, w.head_dim)

@@ -239,13 +239,26 @@ int vsa_pack_lists(const int32_t* counts, const int32_t* ids_padded, int n_rows,
  * kv_ids[r*topk .. r*topk + topk); otherwise the CSR lists as in
  * block_sparse_attn_varlen (topk ignored).  lse_f [B,heads,N] and
  * o_fine [B,heads,N,D] (fp32, cube-major) are written only if non-NULL
- * (both or neither). */
+ * (both or neither).  order (optional, NULL = natural order): a permutation
+ * of the B*heads*Nc query cubes (global ids (b*heads + h)*Nc + c, each
+ * (b, h)'s cubes kept together) giving the order in which the bf16 kernel
+ * runs them, as written by vsa_fine_order; it changes no result. */
 int vsa_fine_forward(const void* q, const void* kp, const void* vp,
                      const float* oc, const void* gate_c, const void* gate_f,
                      int B, int heads, int head_dim, int T, int H, int W,
                      const int32_t* kv_offsets, const int32_t* kv_ids, int topk,
                      int dtype, void* out, float* lse_f, float* o_fine,
-                     hipStream_t stream);
+                     const int32_t* order, hipStream_t stream);
+
+/* Processing order for the fine stage: each (b, h)'s query cubes sorted by
+ * the middle entry (index n/2) of their key list, cube index on ties, as
+ * global ids into order [B*heads*Nc] (int32).  Lists as in
+ * vsa_fine_forward; an empty list counts as middle entry 0.  With ascending
+ * lists, cubes whose lists are centred alike then run side by side and
+ * share more tile reads through the L2.  The forward entry points use it
+ * for bf16 inputs.  Nc <= 4096. */
+int vsa_fine_order(const int32_t* kv_offsets, const int32_t* kv_ids, int topk,
+                   int B, int heads, int n_cubes, int32_t* order, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -39,7 +39,7 @@ def test_header_declares_the_required_entry_points():
                  "vsa_backward_workspace_bytes", "vsa_saved_bytes", "vsa_status_string",
                  "vsa_cube_permute_pool", "vsa_coarse_topk", "vsa_fine_forward",
                  "vsa_forward_mass", "vsa_forward_mass_workspace_bytes", "vsa_coarse_select_mass",
-                 "vsa_pack_lists", "vsa_cube_max_pool"):
+                 "vsa_pack_lists", "vsa_cube_max_pool", "vsa_fine_order"):
         assert need in names
 
 
@@ -125,7 +125,10 @@ def test_stage_calls_reject_bad_arguments(lib):
     assert lib.vsa_coarse_topk(FAKE, FAKE, FAKE, 1, 1, 64, 100000, 2, BF, FAKE, FAKE, FAKE,
                                None) == UNSUPPORTED
     assert lib.vsa_fine_forward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 8, 8, 8,
-                                None, FAKE, 2, _lib.VSA_BF16, FAKE, FAKE, None, None) == INVALID
+                                None, FAKE, 2, _lib.VSA_BF16, FAKE, FAKE, None, None, None) == INVALID
+    assert lib.vsa_fine_order(None, FAKE, 0, 1, 1, 8, FAKE, None) == INVALID  # topk 0 without offsets
+    assert lib.vsa_fine_order(None, FAKE, 2, 1, 1, 8, None, None) == INVALID
+    assert lib.vsa_fine_order(FAKE, FAKE, 0, 1, 1, 5000, FAKE, None) == UNSUPPORTED
     assert lib.vsa_cube_permute_pool(FAKE, FAKE, FAKE, 1, 1, 64, 8, 8, 5, _lib.VSA_BF16,
                                      FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
     # measurement helper: bad depth, head_dim, topk

@@ -232,6 +232,38 @@ def test_varlen_with_topk_lists_reproduces_vsa_forward():
     assert_close(host64(out3), host64(out), BF16, "shuffled lists")
 
 
+def test_fine_order_sorts_by_middle_entry_and_changes_nothing():
+    """The fine stage's processing order: each (b, h)'s query cubes sorted by
+    the middle entry of their list, cube index on ties (exact), for fixed
+    and CSR lists with empty ones; running in that order leaves the output
+    bitwise unchanged."""
+    vsa = _vsa()
+    B, nh, D, grid, K = 2, 3, 128, (8, 12, 16), 5  # 24 cubes
+    nc = 24
+    inp = make_inputs(B, nh, D, grid, dtype="bf16", seed=62, varlen=(0, 24))
+    q, k, v, gc, gf = (dev(inp[n], BF16) for n in ("q", "k", "v", "gc", "gf"))
+    _, kp, vp, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, grid, with_q_tiles=False)
+    oc, _, sel = vsa.vsa_coarse_topk(qc, kc, vc, K, input_dtype=BF16)
+    order = vsa.vsa_fine_order(sel, B, nh, nc, topk=K)
+    torch.cuda.synchronize()
+    mid = sel.cpu().numpy().reshape(B * nh, nc, K)[:, :, K // 2]
+    want = np.concatenate([bh * nc + np.lexsort((np.arange(nc), mid[bh])) for bh in range(B * nh)])
+    np.testing.assert_array_equal(order.cpu().numpy(), want)
+    out0, _, _ = vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, grid, sel, topk=K)
+    out1, _, _ = vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, grid, sel, topk=K, order=order)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1)
+    offs, ids = inp["kv_offsets"], inp["kv_ids"]
+    assert (np.diff(offs) == 0).any()
+    order = vsa.vsa_fine_order(torch.from_numpy(ids).cuda(), B, nh, nc,
+                               kv_offsets=torch.from_numpy(offs).cuda())
+    torch.cuda.synchronize()
+    mids = np.array([ids[a + (b - a) // 2] if b > a else 0 for a, b in zip(offs[:-1], offs[1:])])
+    mids = mids.reshape(B * nh, nc)
+    want = np.concatenate([bh * nc + np.lexsort((np.arange(nc), mids[bh])) for bh in range(B * nh)])
+    np.testing.assert_array_equal(order.cpu().numpy(), want)
+
+
 def test_forward_is_deterministic():
     vsa = _vsa()
     grid = (8, 16, 16)

@@ -5,5 +5,5 @@ from .ops import (  # noqa: F401
     block_sparse_attn_varlen, block_sparse_attn_varlen_backward, pack_lists, probe_tile_gather,
     saved_bytes, vsa_backward, vsa_coarse_select_mass, vsa_coarse_topk, vsa_cube_max_pool,
     vsa_cube_permute_pool,
-    vsa_fine_forward, vsa_forward, vsa_forward_mass,
+    vsa_fine_forward, vsa_fine_order, vsa_forward, vsa_forward_mass,
 )

@@ -31,7 +31,8 @@ SIGNATURES = {
         _i, [_p] * 8 + [_i64, _p] + [_i] * 7 + [_p] * 5 + [_p, _sz, _p]),
     "vsa_cube_permute_pool": (_i, [_p] * 3 + [_i] * 7 + [_p] * 6 + [_p]),
     "vsa_coarse_topk": (_i, [_p] * 3 + [_i] * 6 + [_p] * 3 + [_p]),
-    "vsa_fine_forward": (_i, [_p] * 6 + [_i] * 6 + [_p, _p, _i, _i, _p, _p, _p, _p]),
+    "vsa_fine_forward": (_i, [_p] * 6 + [_i] * 6 + [_p, _p, _i, _i, _p, _p, _p, _p, _p]),
+    "vsa_fine_order": (_i, [_p, _p, _i, _i, _i, _i, _p, _p]),
     "vsa_forward_mass_workspace_bytes": (_sz, [_i] * 8),
     "vsa_forward_mass": (_i, [_p] * 5 + [_i] * 6 + [_f, _i, _i, _i] + [_p] * 5 + [_sz, _p]),
     "vsa_coarse_select_mass": (_i, [_p] * 3 + [_i] * 4 + [_f, _i, _i, _i] + [_p] * 4 + [_p]),

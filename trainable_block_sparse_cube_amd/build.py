@@ -21,6 +21,7 @@ SOURCES = [
     "permute_pool.hip",
     "coarse_topk.hip",
     "lists.hip",
+    "schedule.hip",
     "fine_fwd.hip",
     "backward.hip",
     "probe_gather.hip",

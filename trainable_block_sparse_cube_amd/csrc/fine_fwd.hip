@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     const float* __restrict__ oc, const bf16* __restrict__ gc, const bf16* __restrict__ gf,
     int nh, int nc, int Hg, int Wg,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk,
-    float scale_log2, int n_logical,
+    float scale_log2, int n_logical, const int32_t* __restrict__ order,
     bf16* __restrict__ out, float* __restrict__ lse_f, float* __restrict__ o_fine) {
   constexpr int KS = D / 16;          // k-steps of S^T over head_dim
   constexpr int TILE_CH = 64 * D / 8; // 16-byte chunks per K (and per V) tile
@@ -70,15 +70,19 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
   const int kh = wave >> 1;  // key half of every tile: keys 32*kh .. +32
   const int ql = lane & 31, hf = lane >> 5;
 
-  // Logical block (b*nh + h)*nc + c.  Hardware block i runs on XCD i % 8
-  // (round-robin dispatch), so XCD x is given the contiguous logical range
-  // [x per, (x + 1) per): the workgroups that share one XCD's L2 work on
-  // neighbouring query cubes of one head, which select overlapping key
-  // cubes when the inputs have spatial structure.  The grid is padded to a
-  // multiple of 8; padding blocks exit at once.
+  // Logical block i: query cube (b*nh + h)*nc + c = order[i], or i itself
+  // without an order.  Hardware block i runs on XCD i % 8 (round-robin
+  // dispatch), so XCD x is given the contiguous logical range [x per,
+  // (x + 1) per): the workgroups that share one XCD's L2 work on
+  // neighbouring entries of the order, all of one or two heads: query
+  // cubes with similar key lists (the sorted order), or neighbouring query
+  // cubes (natural order), which select overlapping key cubes when the
+  // inputs have spatial structure.  The grid is padded to a multiple of 8;
+  // padding blocks exit at once.
   const int per = (n_logical + 7) >> 3;
-  const int blk = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
-  if (blk >= n_logical) return;
+  const int lblk = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  if (lblk >= n_logical) return;
+  const int blk = order ? order[lblk] : lblk;
   const int bh = blk / nc;
   const int c = blk - bh * nc;
   const int64_t N = (int64_t)nc * 64;
@@ -315,7 +319,7 @@ hipError_t launch_fine_d(const FineArgs& a, hipStream_t st) {
     fine_fwd_bf16_kernel<D><<<((grid + 7u) / 8u) * 8u, 256, 0, st>>>(
         (const bf16*)a.q, (const bf16*)a.kp, (const bf16*)a.vp, a.oc,
         (const bf16*)a.gc, (const bf16*)a.gf, a.heads, nc, a.H, a.W, a.offs, a.ids, a.topk,
-        scale * kLog2e, (int)grid, (bf16*)a.out, a.lse_f, a.o_fine);
+        scale * kLog2e, (int)grid, a.order, (bf16*)a.out, a.lse_f, a.o_fine);
   } else {
     fine_fwd_f32_kernel<D><<<grid, 64, 0, st>>>(
         (const float*)a.q, (const float*)a.kp, (const float*)a.vp, a.oc,

@@ -39,6 +39,7 @@ int check_shape(int B, int heads, int D, int T, int H, int W, int dtype, Shape* 
 struct FwdWorkspace {
   void *kp, *vp;
   float *qc, *kc, *vc, *oc, *lse_c;
+  int32_t* order;  // processing order of the fine stage's query cubes
 };
 
 size_t fwd_ws_layout(const Shape& s, char* base, FwdWorkspace* w) {
@@ -51,6 +52,7 @@ size_t fwd_ws_layout(const Shape& s, char* base, FwdWorkspace* w) {
   t.kp = take(tile_bytes); t.vp = take(tile_bytes);
   t.qc = (float*)take(pooled); t.kc = (float*)take(pooled); t.vc = (float*)take(pooled);
   t.oc = (float*)take(pooled); t.lse_c = (float*)take(lse);
+  t.order = (int32_t*)take(align_up((size_t)s.B * s.heads * s.nc * sizeof(int32_t)));
   if (w) *w = t;
   return off;
 }
@@ -131,6 +133,11 @@ int forward_impl(const void* q, const void* k, const void* v, const void* gc, co
   }
   FineArgs fa{q, w.kp, w.vp, oc, gc, gf, s.B, s.heads, s.D, s.T, s.H, s.W,
               offs, offs ? ids : sel, topk, bf, out, lse_f, of};
+  if (bf) {  // the MFMA kernel runs the query cubes sorted by their lists' middle entries
+    e = launch_fine_order(fa.offs, fa.ids, topk, s.B * s.heads, (int)s.nc, w.order, st);
+    if (e != hipSuccess) return VSA_ERR_HIP;
+    fa.order = w.order;
+  }
   return hip_status(launch_fine_forward(fa, st));
 }
 
@@ -355,7 +362,8 @@ int vsa_fine_forward(const void* q, const void* kp, const void* vp, const float*
                      const void* gate_c, const void* gate_f,
                      int B, int heads, int head_dim, int T, int H, int W,
                      const int32_t* kv_offsets, const int32_t* kv_ids, int topk, int dtype,
-                     void* out, float* lse_f, float* o_fine, hipStream_t stream) {
+                     void* out, float* lse_f, float* o_fine, const int32_t* order,
+                     hipStream_t stream) {
   Shape s;
   int st = check_shape(B, heads, head_dim, T, H, W, dtype, &s);
   if (st != VSA_OK) return st;
@@ -367,7 +375,20 @@ int vsa_fine_forward(const void* q, const void* kp, const void* vp, const float*
   }
   FineArgs fa{q, kp, vp, oc, gate_c, gate_f, B, heads, head_dim, T, H, W,
               kv_offsets, kv_ids, topk, dtype == VSA_BF16, out, lse_f, o_fine};
+  fa.order = order;
   return hip_status(launch_fine_forward(fa, stream));
+}
+
+int vsa_fine_order(const int32_t* kv_offsets, const int32_t* kv_ids, int topk, int B, int heads,
+                   int n_cubes, int32_t* order, hipStream_t stream) {
+  if (B < 1 || heads < 1 || n_cubes < 1 || !order) return VSA_ERR_INVALID_ARG;
+  if (n_cubes > order_max_cubes() || (int64_t)B * heads > 65535) return VSA_ERR_UNSUPPORTED;
+  if ((int64_t)B * heads * n_cubes > INT_MAX / 2) return VSA_ERR_UNSUPPORTED;
+  if (!kv_offsets) {
+    if (topk < 1 || topk > n_cubes || !kv_ids) return VSA_ERR_INVALID_ARG;
+    if ((int64_t)B * heads * n_cubes * topk > INT_MAX) return VSA_ERR_UNSUPPORTED;
+  }
+  return hip_status(launch_fine_order(kv_offsets, kv_ids, topk, B * heads, n_cubes, order, stream));
 }
 
 size_t vsa_backward_workspace_bytes(int B, int heads, int head_dim, int T, int H, int W, int dtype,

@@ -58,8 +58,14 @@ struct FineArgs {
   void* out;            // [B, N, heads, D]
   float* lse_f;         // [B, heads, N] cube-major, optional
   float* o_fine;        // [B, heads, N, D] cube-major, optional
+  const int32_t* order = nullptr;  // processing order of the query cubes (global ids), optional
 };
 hipError_t launch_fine_forward(const FineArgs& a, hipStream_t st);
+// Query cubes of each (b, h) sorted by the middle entry of their key list
+// (cube index on ties), as global ids bh*nc + c, into order[n_bh*nc].
+int order_max_cubes();
+hipError_t launch_fine_order(const int32_t* offs, const int32_t* ids, int topk, int n_bh, int nc,
+                             int32_t* order, hipStream_t st);
 
 // Backward (bf16).  Inputs: raster dout, gates; cube-major tiles qp, kp,
 // vp from the backward permute; fp32 means; forward state (oc, lse_c,

@@ -239,8 +239,9 @@ def pack_lists(counts, ids_padded):
 
 
 def vsa_fine_forward(q, kp, vp, oc, gate_c, gate_f, grid, kv_ids, topk=0, kv_offsets=None,
-                     out=None, save=False):
-    """Fine stage + gated combine on raster q and K / V tiles.
+                     out=None, save=False, order=None):
+    """Fine stage + gated combine on raster q and K / V tiles; `order`
+    (from vsa_fine_order) sets the order the query cubes run in.
     Returns (out, lse_f or None, o_fine or None)."""
     lib = _lib.load()
     B, N, nh, D = q.shape
@@ -252,9 +253,20 @@ def vsa_fine_forward(q, kp, vp, oc, gate_c, gate_f, grid, kv_ids, topk=0, kv_off
         of = torch.empty((B, nh, N, D), dtype=torch.float32, device=q.device)
     st = lib.vsa_fine_forward(_ptr(q), _ptr(kp), _ptr(vp), _ptr(oc), _ptr(gate_c), _ptr(gate_f),
                               B, nh, D, *grid, _ptr(kv_offsets), _ptr(kv_ids), topk,
-                              _DT[q.dtype], _ptr(out), _ptr(lse), _ptr(of), _stream())
+                              _DT[q.dtype], _ptr(out), _ptr(lse), _ptr(of), _ptr(order), _stream())
     _lib.check("vsa_fine_forward", st)
     return out, lse, of
+
+
+def vsa_fine_order(kv_ids, B, heads, n_cubes, topk=0, kv_offsets=None):
+    """Processing order for the fine stage (each (b, h)'s query cubes sorted
+    by the middle entry of their list).  Returns int32 [B * heads * Nc]."""
+    lib = _lib.load()
+    order = torch.empty(B * heads * n_cubes, dtype=torch.int32, device=kv_ids.device)
+    st = lib.vsa_fine_order(_ptr(kv_offsets), _ptr(kv_ids), topk, B, heads, n_cubes, _ptr(order),
+                            _stream())
+    _lib.check("vsa_fine_order", st)
+    return order
 
 
 # ------------------------------------------------------- measurement helper
