@@ -22,9 +22,12 @@
 // global memory into LDS (global_load_lds, no register staging) with an XOR
 // chunk swizzle, double buffered: tile t+1 streams in while tile t is
 // computed, one barrier per tile.  V^T operands come from transposing LDS
-// reads (ds_read_b64_tr_b16).  The epilogue divides by the row sum, mixes in the coarse output
-// with the two gates, rounds once to bf16 and scatters rows back to raster
-// token order.
+// reads (ds_read_b64_tr_b16).  The epilogue divides by the row sum, mixes
+// in the coarse output with the two gates, rounds once to bf16 and
+// scatters rows back to raster token order.  Query cubes run in the order
+// given (the forward sorts them by their lists' middle entries, so that
+// cubes sweeping similar key ranges share an XCD's L2 at the same time),
+// or in natural order.
 //
 // fp32 kernel: plain VALU, one wave per query cube, one lane per query
 // token; it serves the fp32 path, where no reduced precision is allowed.
