@@ -215,7 +215,9 @@ def main():
                      # peak and fraction at that clock; the published peak assumes 2.4 GHz
                      "clock_GHz": clk,
                      "peak_at_clock": PEAK_BF16_TFLOPS * clk / 2.4 if clk else None,
-                     "frac_at_clock": fine_tflops / (PEAK_BF16_TFLOPS * clk / 2.4) if clk else None},
+                     "frac_at_clock": fine_tflops / (PEAK_BF16_TFLOPS * clk / 2.4) if clk else None,
+                     # MFMA utilisation from the counters: busy cycles over all SIMDs' cycles
+                     "mfma_busy_frac_counters": counters.get("fine_mfma_busy_frac")},
         "per_call_ms": calls,
         "fine_floors": {
             "tile_bytes_per_launch": tile_bytes,
