@@ -45,6 +45,32 @@ def _check_inputs(q, k, v, gate_c, gate_f, grid):
     return B, N, nh, D, T, H, W, _DT[q.dtype]
 
 
+def _need(t, name, dtype, shape=None, numel=None, min_numel=None):
+    """A tensor handed to the C ABI as a raw pointer: on the GPU, dense, of
+    the element type (and shape or size) the call assumes."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs at least {min_numel}")
+
+
+def _check_qkv(q, k, v, grid):
+    if q.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype, shape=q.shape)
+    if q.dim() != 4 or q.shape[1] != grid[0] * grid[1] * grid[2]:
+        raise ValueError(f"q must be [B, N, heads, D] with N = {grid[0] * grid[1] * grid[2]}")
+
+
 def _workspace(nbytes, device):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
@@ -126,8 +152,12 @@ def vsa_backward(q, k, v, gate_c, gate_f, dout, sel, saved, grid):
     Returns (dq, dk, dv, dgate_c, dgate_f); gate gradients are fp32."""
     lib = _lib.load()
     B, N, nh, D, T, H, W, dt = _check_inputs(q, k, v, gate_c, gate_f, grid)
-    if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_contiguous():
-        raise ValueError("dout must match q")
+    _need(dout, "dout", q.dtype, shape=q.shape)
+    nc = N // 64
+    if sel.dim() != 4 or tuple(sel.shape[:3]) != (B, nh, nc):
+        raise ValueError("sel must be [B, heads, Nc, topk]")
+    _need(sel, "sel", torch.int32)
+    _need(saved, "saved", torch.uint8, min_numel=int(lib.vsa_saved_bytes(B, nh, D, T, H, W)))
     topk = sel.shape[-1]
     grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
              torch.empty(gate_c.shape, dtype=torch.float32, device=q.device),
@@ -145,6 +175,8 @@ def block_sparse_attn_varlen_backward(q, k, v, gate_c, gate_f, dout, kv_offsets,
     lib = _lib.load()
     B, N, nh, D, T, H, W, dt = _check_inputs(q, k, v, gate_c, gate_f, grid)
     _check_lists(kv_offsets, kv_ids, B, nh, N // 64)
+    _need(dout, "dout", q.dtype, shape=q.shape)
+    _need(saved, "saved", torch.uint8, min_numel=int(lib.vsa_saved_bytes(B, nh, D, T, H, W)))
     grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
              torch.empty(gate_c.shape, dtype=torch.float32, device=q.device),
              torch.empty(gate_f.shape, dtype=torch.float32, device=q.device)]
@@ -164,6 +196,7 @@ def vsa_cube_permute_pool(q, k, v, grid, with_q_tiles=True):
     """Returns (qp, kp, vp, qc, kc, vc) in the library's cube-major layouts
     (qp is None when with_q_tiles is False, as in the forward)."""
     lib = _lib.load()
+    _check_qkv(q, k, v, grid)
     B, N, nh, D = q.shape
     dt = _DT[q.dtype]
     nc = N // 64
@@ -181,6 +214,7 @@ def vsa_cube_max_pool(q, k, v, grid):
     """Per-channel maximum of each cube's 64 tokens of q, k, v (the pooling
     ablation).  Returns fp32 (qc, kc, vc) [B, heads, Nc, D]."""
     lib = _lib.load()
+    _check_qkv(q, k, v, grid)
     B, N, nh, D = q.shape
     T, H, W = grid
     nc = N // 64
@@ -197,6 +231,8 @@ def vsa_coarse_topk(qc, kc, vc, topk, input_dtype=torch.float32):
     precision: fp32 products for torch.float32, bf16 x 3 for torch.bfloat16
     (as the forward does for such inputs)."""
     lib = _lib.load()
+    for name, t in (("qc", qc), ("kc", kc), ("vc", vc)):
+        _need(t, name, torch.float32, shape=qc.shape)
     B, nh, nc, D = qc.shape
     oc = torch.empty_like(qc)
     lse = torch.empty((B, nh, nc), dtype=torch.float32, device=qc.device)
@@ -212,6 +248,8 @@ def vsa_coarse_select_mass(qc, kc, vc, mass, k_min, k_max, input_dtype=torch.flo
     lse_c, counts [B, heads, Nc], ids [B, heads, Nc, k_max]); row r's list
     is ids[..., :counts[r]] (ascending)."""
     lib = _lib.load()
+    for name, t in (("qc", qc), ("kc", kc), ("vc", vc)):
+        _need(t, name, torch.float32, shape=qc.shape)
     B, nh, nc, D = qc.shape
     oc = torch.empty_like(qc)
     lse = torch.empty((B, nh, nc), dtype=torch.float32, device=qc.device)
@@ -230,6 +268,8 @@ def pack_lists(counts, ids_padded):
     lib = _lib.load()
     k_max = ids_padded.shape[-1]
     n_rows = counts.numel()
+    _need(counts, "counts", torch.int32)
+    _need(ids_padded, "ids_padded", torch.int32, numel=n_rows * k_max)
     offs = torch.empty(n_rows + 1, dtype=torch.int32, device=counts.device)
     ids = torch.empty(max(n_rows * k_max, 1), dtype=torch.int32, device=counts.device)
     st = lib.vsa_pack_lists(_ptr(counts), _ptr(ids_padded), n_rows, k_max, _ptr(offs), _ptr(ids),
@@ -244,9 +284,22 @@ def vsa_fine_forward(q, kp, vp, oc, gate_c, gate_f, grid, kv_ids, topk=0, kv_off
     (from vsa_fine_order) sets the order the query cubes run in.
     Returns (out, lse_f or None, o_fine or None)."""
     lib = _lib.load()
-    B, N, nh, D = q.shape
+    B, N, nh, D, T, H, W, dt = _check_inputs(q, q, q, gate_c, gate_f, grid)
+    nc = N // 64
+    _need(kp, "kp", q.dtype, shape=(B, nh, nc, 64, D))
+    _need(vp, "vp", q.dtype, shape=(B, nh, nc, 64, D))
+    _need(oc, "oc", torch.float32, shape=(B, nh, nc, D))
+    _need(kv_ids, "kv_ids", torch.int32)
+    if kv_offsets is not None:
+        _need(kv_offsets, "kv_offsets", torch.int32, numel=B * nh * nc + 1)
+    elif kv_ids.numel() != B * nh * nc * topk:
+        raise ValueError("kv_ids must hold B*heads*Nc*topk ids")
+    if order is not None:
+        _need(order, "order", torch.int32, numel=B * nh * nc)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _need(out, "out", q.dtype, shape=q.shape)
     lse = of = None
     if save:
         lse = torch.empty((B, nh, N), dtype=torch.float32, device=q.device)
@@ -262,6 +315,11 @@ def vsa_fine_order(kv_ids, B, heads, n_cubes, topk=0, kv_offsets=None):
     """Processing order for the fine stage (each (b, h)'s query cubes sorted
     by the middle entry of their list).  Returns int32 [B * heads * Nc]."""
     lib = _lib.load()
+    _need(kv_ids, "kv_ids", torch.int32)
+    if kv_offsets is not None:
+        _need(kv_offsets, "kv_offsets", torch.int32, numel=B * heads * n_cubes + 1)
+    elif kv_ids.numel() != B * heads * n_cubes * topk:
+        raise ValueError("kv_ids must hold B*heads*Nc*topk ids")
     order = torch.empty(B * heads * n_cubes, dtype=torch.int32, device=kv_ids.device)
     st = lib.vsa_fine_order(_ptr(kv_offsets), _ptr(kv_ids), topk, B, heads, n_cubes, _ptr(order),
                             _stream())
@@ -275,7 +333,12 @@ def probe_tile_gather(kp, vp, kv_ids, topk, depth=8):
     the fixed-length lists kv_ids [B, heads, Nc, topk], with no arithmetic
     (the fine stage's data-movement floor).  Queued on the current stream."""
     lib = _lib.load()
+    if kp.dim() != 5 or kp.shape[3] != 64:
+        raise ValueError("kp must be [B, heads, Nc, 64, D]")
     B, nh, nc, _, D = kp.shape
+    _need(kp, "kp", kp.dtype)
+    _need(vp, "vp", kp.dtype, shape=kp.shape)
+    _need(kv_ids, "kv_ids", torch.int32, numel=B * nh * nc * topk)
     sink = torch.empty(4096, dtype=torch.uint8, device=kp.device)
     st = lib.vsa_probe_tile_gather(_ptr(kp), _ptr(vp), B * nh, nc, D, _ptr(kv_ids), topk, depth,
                                    _ptr(sink), _stream())
