@@ -217,10 +217,12 @@ __device__ __forceinline__ int mass_length(const uint32_t (&keys)[MAXJ], const f
   return min(max(n, k_min), k_max);
 }
 
-// One workgroup: R = 16 query rows of one (batch, head), 8 waves.
+// One workgroup: R = 16 query rows of one (batch, head), 8 waves.  With PK
+// (the forward's bf16 path) the pooled K and V come in the packed operand
+// order, so that every load of phases 1 and 3 is one contiguous run.
 // Matrix products use v_mfma_f32_16x16x4f32 (fp32 in, fp32 accumulate).
 // Lane l of a 16x16x4 step supplies row/column l % 16 and k-slice l / 16.
-template <int D, int MAXJ, bool X3>
+template <int D, int MAXJ, bool X3, bool PK>
 __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
     const float* __restrict__ qc, const float* __restrict__ kc,
     const float* __restrict__ vc, int nc, int topk, float scale,
@@ -241,8 +243,11 @@ __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
   const int wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, lg = lane >> 4;
   const float* qcb = qc + (int64_t)bh * nc * D;
-  const float* kcb = kc + (int64_t)bh * nc * D;
-  const float* vcb = vc + (int64_t)bh * nc * D;
+  // PK: kc and vc in the packed (operand-ordered) layouts, keys padded
+  static_assert(X3 || !PK, "packed layouts serve the bf16 x 3 path");
+  const int64_t kv_pitch = PK ? packed_keys(nc) : nc;
+  const float* kcb = kc + (int64_t)bh * kv_pitch * D;
+  const float* vcb = vc + (int64_t)bh * kv_pitch * D;
 
   if constexpr (X3) {
     // ---- 1. logits, bf16 x 3.  k-step t (32 of head_dim): lane group lg
@@ -258,10 +263,16 @@ __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
       for (int t = 0; t < KT; ++t) split_bf16x8(src[8 * t], src[8 * t + 1], qh[t], ql[t]);
     }
     auto load_k = [&](int j0, f32x4v (&kb)[2 * KT]) {
-      const f32x4v* src =
-          reinterpret_cast<const f32x4v*>(kcb + (int64_t)min(j0 + li, nc - 1) * D + 8 * lg);
+      if constexpr (PK) {  // one contiguous KB per load (block j0 / 16)
+        const f32x4v* src = reinterpret_cast<const f32x4v*>(kcb + (int64_t)j0 * D) + lane;
 #pragma unroll
-      for (int t = 0; t < KT; ++t) { kb[2 * t] = src[8 * t]; kb[2 * t + 1] = src[8 * t + 1]; }
+        for (int i = 0; i < 2 * KT; ++i) kb[i] = src[64 * i];
+      } else {
+        const f32x4v* src =
+            reinterpret_cast<const f32x4v*>(kcb + (int64_t)min(j0 + li, nc - 1) * D + 8 * lg);
+#pragma unroll
+        for (int t = 0; t < KT; ++t) { kb[2 * t] = src[8 * t]; kb[2 * t + 1] = src[8 * t + 1]; }
+      }
     };
     f32x4v kb[2 * KT], kn[2 * KT];
     if (16 * wave < nc) load_k(16 * wave, kn);
@@ -405,10 +416,17 @@ __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
     const int col = 16 * cb + li;
     const bf16* prow = reinterpret_cast<const bf16*>(S + li * s_pitch);
     auto load_v = [&](int j0, float (&vbuf)[8]) {
+      if constexpr (PK) {  // this lane's 8 keys of column col, contiguous (step j0 / 32)
+        const f32x4v* src = reinterpret_cast<const f32x4v*>(vcb + (int64_t)j0 * D + (cb * 64 + lane) * 8);
+        const f32x4v a = src[0], b = src[1];
+        vbuf[0] = a.x; vbuf[1] = a.y; vbuf[2] = a.z; vbuf[3] = a.w;
+        vbuf[4] = b.x; vbuf[5] = b.y; vbuf[6] = b.z; vbuf[7] = b.w;
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = min(j0 + 8 * lg + e, nc - 1);  // P is 0 past the end
-        vbuf[e] = vcb[(int64_t)key * D + col];
+        for (int e = 0; e < 8; ++e) {
+          const int key = min(j0 + 8 * lg + e, nc - 1);  // P is 0 past the end
+          vbuf[e] = vcb[(int64_t)key * D + col];
+        }
       }
     };
     f32x4v oacc = {0.f, 0.f, 0.f, 0.f}, oacc2 = {0.f, 0.f, 0.f, 0.f};
@@ -487,10 +505,10 @@ size_t coarse_lds_bytes(int nc) {
   return sizeof(float) * ((size_t)16 * s_pitch + (size_t)2 * kNW * kCandCap);
 }
 
-template <int D, int MAXJ, bool X3>
+template <int D, int MAXJ, bool X3, bool PK>
 hipError_t launch_coarse_dj(const CoarseArgs& a, hipStream_t st) {
   const size_t lds = coarse_lds_bytes(a.nc);
-  auto kern = coarse_topk_kernel<D, MAXJ, X3>;
+  auto kern = coarse_topk_kernel<D, MAXJ, X3, PK>;
   // Allow this much dynamic LDS (host-side call, made on every launch: the
   // setting belongs to the current device, and the call is cheap).
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -501,10 +519,10 @@ hipError_t launch_coarse_dj(const CoarseArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int D, bool X3>
+template <int D, bool X3, bool PK>
 hipError_t launch_coarse_d(const CoarseArgs& a, hipStream_t st) {
-  if (a.nc <= 16 * 64) return launch_coarse_dj<D, 16, X3>(a, st);
-  return launch_coarse_dj<D, 40, X3>(a, st);
+  if (a.nc <= 16 * 64) return launch_coarse_dj<D, 16, X3, PK>(a, st);
+  return launch_coarse_dj<D, 40, X3, PK>(a, st);
 }
 
 }  // namespace
@@ -519,8 +537,10 @@ int coarse_max_cubes(int D) {
 }
 
 hipError_t launch_coarse_topk(const CoarseArgs& a, hipStream_t st) {
-  if (a.x3) return a.D == 128 ? launch_coarse_d<128, true>(a, st) : launch_coarse_d<64, true>(a, st);
-  return a.D == 128 ? launch_coarse_d<128, false>(a, st) : launch_coarse_d<64, false>(a, st);
+  if (a.x3 && a.packed)
+    return a.D == 128 ? launch_coarse_d<128, true, true>(a, st) : launch_coarse_d<64, true, true>(a, st);
+  if (a.x3) return a.D == 128 ? launch_coarse_d<128, true, false>(a, st) : launch_coarse_d<64, true, false>(a, st);
+  return a.D == 128 ? launch_coarse_d<128, false, false>(a, st) : launch_coarse_d<64, false, false>(a, st);
 }
 
 }  // namespace vsa

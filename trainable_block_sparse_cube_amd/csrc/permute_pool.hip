@@ -8,7 +8,9 @@
 // raster layout), writes them as one contiguous cube-major tile, and reduces
 // the 64 rows to their fp32 mean with wavefront shuffles plus a 4-way LDS
 // combine.  The forward writes the K and V tiles (the fine stage reads Q in
-// place); the backward writes Q, K and V tiles.  A second instance takes
+// place); the backward writes Q, K and V tiles.  The forward's bf16 path
+// stores the pooled K and V in the coarse kernel's operand order (packed
+// layouts, zero-padded keys).  A second instance takes
 // the per-channel maximum instead of the mean and writes no tiles: the
 // pooling ablation ([VSA-sum, Surprising findings]: mean pooling did better
 // than max pooling).  Both reductions are exact in fp32 (the mean's sum of
@@ -19,7 +21,8 @@
 namespace vsa {
 
 template <typename T, int D, bool MAXP>
-__global__ __launch_bounds__(256) void permute_pool_kernel(PermutePoolPtrs p, int nh, int Tg, int Hg, int Wg) {
+__global__ __launch_bounds__(256) void permute_pool_kernel(PermutePoolPtrs p, int nh, int Tg, int Hg, int Wg,
+                                                           bool packed_kv) {
   constexpr int EPC = 16 / sizeof(T);     // elements per 16-byte chunk
   constexpr int CPR = D / EPC;            // chunks per token row
   constexpr int ROWS_PER_PASS = 256 / CPR;
@@ -79,10 +82,21 @@ __global__ __launch_bounds__(256) void permute_pool_kernel(PermutePoolPtrs p, in
   }
   __syncthreads();
   if (pooled) {
+    const bool pk = packed_kv && which > 0;
+    const int ncp = packed_keys(nc);
+    float* base = pooled + (int64_t)(b * nh + h) * (pk ? ncp : nc) * D;
     for (int d = tid; d < D; d += 256) {
       const float r = MAXP ? fmaxf(fmaxf(red[0][d], red[1][d]), fmaxf(red[2][d], red[3][d]))
                            : ((red[0][d] + red[1][d]) + (red[2][d] + red[3][d])) * (1.0f / kCubeTokens);
-      pooled[((int64_t)(b * nh + h) * nc + c) * D + d] = r;
+      if (!pk) base[(int64_t)c * D + d] = r;
+      else if (which == 1) base[packed_k_index(c, d, D)] = r;
+      else base[packed_v_index(c, d, D)] = r;
+    }
+    if (pk && c == nc - 1) {  // zero the padding keys of this (b, h)
+      for (int i = tid; i < (ncp - nc) * D; i += 256) {
+        const int j = nc + i / D, d = i % D;
+        base[which == 1 ? packed_k_index(j, d, D) : packed_v_index(j, d, D)] = 0.f;
+      }
     }
   }
 }
@@ -94,9 +108,9 @@ static hipError_t launch_pp(const PermutePoolArgs& a, hipStream_t st) {
   if (a.max_pool) {
     PermutePoolPtrs p = a.p;
     p.nat[0] = p.nat[1] = p.nat[2] = nullptr;  // pooled values only
-    permute_pool_kernel<T, D, true><<<grid, 256, 0, st>>>(p, a.heads, a.T, a.H, a.W);
+    permute_pool_kernel<T, D, true><<<grid, 256, 0, st>>>(p, a.heads, a.T, a.H, a.W, false);
   } else {
-    permute_pool_kernel<T, D, false><<<grid, 256, 0, st>>>(a.p, a.heads, a.T, a.H, a.W);
+    permute_pool_kernel<T, D, false><<<grid, 256, 0, st>>>(a.p, a.heads, a.T, a.H, a.W, a.packed_kv);
   }
   return hipGetLastError();
 }

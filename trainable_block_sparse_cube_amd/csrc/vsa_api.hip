@@ -45,12 +45,14 @@ struct FwdWorkspace {
 size_t fwd_ws_layout(const Shape& s, char* base, FwdWorkspace* w) {
   const size_t tile_bytes = align_up((size_t)s.B * s.heads * s.N * s.D * s.elt);
   const size_t pooled = align_up((size_t)s.B * s.heads * s.nc * s.D * sizeof(float));
+  // pooled K and V may be held in the packed layouts (keys padded)
+  const size_t pooled_kv = align_up((size_t)s.B * s.heads * packed_keys((int)s.nc) * s.D * sizeof(float));
   const size_t lse = align_up((size_t)s.B * s.heads * s.nc * sizeof(float));
   size_t off = 0;
   auto take = [&](size_t bytes) { char* p = base ? base + off : nullptr; off += bytes; return (void*)p; };
   FwdWorkspace t;
   t.kp = take(tile_bytes); t.vp = take(tile_bytes);
-  t.qc = (float*)take(pooled); t.kc = (float*)take(pooled); t.vc = (float*)take(pooled);
+  t.qc = (float*)take(pooled); t.kc = (float*)take(pooled_kv); t.vc = (float*)take(pooled_kv);
   t.oc = (float*)take(pooled); t.lse_c = (float*)take(lse);
   t.order = (int32_t*)take(align_up((size_t)s.B * s.heads * s.nc * sizeof(int32_t)));
   if (w) *w = t;
@@ -108,11 +110,14 @@ int forward_impl(const void* q, const void* k, const void* v, const void* gc, co
   }
   const bool bf = s.dtype == VSA_BF16;
   // The fine stage reads Q in place; K and V are copied into cube tiles.
+  // bf16: pooled K and V go straight into the coarse kernel's operand order.
   PermutePoolArgs pa{{{q, k, v}, {nullptr, w.kp, w.vp}, {w.qc, w.kc, w.vc}},
                      s.B, s.heads, s.D, s.T, s.H, s.W, bf};
+  pa.packed_kv = bf;
   hipError_t e = launch_permute_pool(pa, st);
   if (e != hipSuccess) return VSA_ERR_HIP;
   CoarseArgs ca{w.qc, w.kc, w.vc, s.B, s.heads, s.D, (int)s.nc, offs ? 0 : topk, oc, lse_c, sel, bf};
+  ca.packed = bf;
   const int rows = (int)((int64_t)s.B * s.heads * s.nc);
   int32_t* counts = nullptr;
   int32_t* padded = nullptr;

@@ -14,11 +14,32 @@ struct PermutePoolPtrs {
   void* nat[3];
   float* pooled[3];
 };
+// Operand-ordered ("packed") pooled K and V for the coarse kernel's bf16
+// path: each wave load of an MFMA operand block is one contiguous run.
+// Per (b, h), keys are padded to packed_keys(nc) (a multiple of 32, zeros).
+//   K: element (key j, dim d) at (j / 16) * 16 D + ((2 (d / 32) + (d % 8) / 4)
+//      * 64 + 16 ((d % 32) / 8) + j % 16) * 4 + d % 4
+//      (16-key blocks; lane 16 lg + li of k-step t, half hp, holds key li,
+//      dims 32 t + 8 lg + 4 hp .. +4)
+//   V: element (key j, dim d) at (j / 32) * 32 D + ((d / 16) * 64
+//      + 16 ((j % 32) / 8) + d % 16) * 8 + j % 8
+//      (32-key steps; lane 16 lg + li of column block cb holds column
+//      16 cb + li, keys 8 lg .. +8 of the step)
+__host__ __device__ inline int packed_keys(int nc) { return (nc + 31) & ~31; }
+__host__ __device__ inline int64_t packed_k_index(int j, int d, int D) {
+  return (int64_t)(j >> 4) * 16 * D +
+         ((2 * (d >> 5) + ((d & 7) >> 2)) * 64 + 16 * ((d & 31) >> 3) + (j & 15)) * 4 + (d & 3);
+}
+__host__ __device__ inline int64_t packed_v_index(int j, int d, int D) {
+  return (int64_t)(j >> 5) * 32 * D + (((d >> 4) * 64 + 16 * ((j & 31) >> 3) + (d & 15)) * 8) + (j & 7);
+}
+
 struct PermutePoolArgs {
   PermutePoolPtrs p;
   int B, heads, D, T, H, W;
   bool bf16;
-  bool max_pool = false;  // per-channel max instead of the mean; no tiles written
+  bool max_pool = false;   // per-channel max instead of the mean; no tiles written
+  bool packed_kv = false;  // pooled K and V in the packed layouts (pitch packed_keys(nc))
 };
 hipError_t launch_permute_pool(const PermutePoolArgs& a, hipStream_t st);
 
@@ -28,6 +49,7 @@ struct CoarseArgs {
   float *oc, *lse;
   int32_t* sel;  // may be null when topk == 0
   bool x3;       // products as three bf16 MFMAs (bf16 inputs) instead of fp32 MFMA
+  bool packed = false;  // (x3 only) kc, vc in the packed layouts, pitch packed_keys(nc)
   // Mass rule instead of top-K when counts is non-null: per row, the
   // shortest ranked prefix reaching `mass` of the coarse probability,
   // length clamped to [k_min, k_max], written to counts[row] and to sel at
