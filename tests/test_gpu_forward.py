@@ -139,6 +139,31 @@ def test_coarse_stage_and_exact_ties(prec):
     assert straddled > 0
 
 
+@pytest.mark.parametrize("D,grid", [(128, (8, 12, 20)), (64, (8, 36, 44)), (128, (4, 40, 48))],
+                         ids=["D128-30cubes", "D64-198cubes", "D128-120cubes"])
+def test_forward_coarse_packed_equals_stage_call(D, grid):
+    """The bf16 forward hands the coarse kernel its pooled K and V in packed
+    operand order (padding keys zeroed); the stage call reads plain means.
+    Same products in the same order, so the saved coarse output and LSE and
+    the selection agree bitwise, also with cube counts that leave ragged
+    16- and 32-key blocks."""
+    vsa = _vsa()
+    B, nh, K = 1, 2, 6
+    T, H, W = grid
+    N = T * H * W
+    log(f"packed coarse vs stage call D={D} grid={grid}")
+    inp = make_inputs(B, nh, D, grid, dtype="bf16", seed=77)
+    q, k, v, gc, gf = (dev(inp[n], BF16) for n in ("q", "k", "v", "gc", "gf"))
+    out, sel, saved = vsa.vsa_forward(q, k, v, gc, gf, grid, K, save=True)
+    _, _, _, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, grid, with_q_tiles=False)
+    oc, lse, sel2 = vsa.vsa_coarse_topk(qc, kc, vc, K, input_dtype=BF16)
+    torch.cuda.synchronize()
+    oc_s, lse_s, _, _ = unpack_saved(saved, B, nh, N, D)
+    assert torch.equal(sel, sel2)
+    assert torch.equal(oc_s, oc)
+    assert torch.equal(lse_s, lse)
+
+
 @pytest.mark.parametrize("prec", [F32, BF16], ids=["fp32-products", "bf16x3-products"])
 def test_coarse_stage_at_the_largest_cube_count(prec):
     """2272 cubes (grid 4x32x1136), the most the coarse kernel holds (16
