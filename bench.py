@@ -217,7 +217,13 @@ def main():
                      "peak_at_clock": PEAK_BF16_TFLOPS * clk / 2.4 if clk else None,
                      "frac_at_clock": fine_tflops / (PEAK_BF16_TFLOPS * clk / 2.4) if clk else None,
                      # MFMA utilisation from the counters: busy cycles over all SIMDs' cycles
-                     "mfma_busy_frac_counters": counters.get("fine_mfma_busy_frac")},
+                     "mfma_busy_frac_counters": counters.get("fine_mfma_busy_frac"),
+                     # the measured HBM traffic (counters) over this launch time, against the
+                     # 8 TB/s HBM peak: the tile re-reads that miss L2 are what bound the kernel
+                     "traffic_TBps": (counters["hbm_bytes_per_launch"] / (ms_fine * 1e-3) / 1e12
+                                      if counters.get("hbm_bytes_per_launch") else None),
+                     "traffic_frac_of_hbm_peak": (counters["hbm_bytes_per_launch"] / (ms_fine * 1e-3) / 1e12
+                                                  / (PEAK_HBM_GBS / 1000.0) if counters.get("hbm_bytes_per_launch") else None)},
         "per_call_ms": calls,
         "fine_floors": {
             "tile_bytes_per_launch": tile_bytes,
