@@ -165,18 +165,23 @@ def test_forward_coarse_packed_equals_stage_call(D, grid):
 
 
 @pytest.mark.parametrize("prec", [F32, BF16], ids=["fp32-products", "bf16x3-products"])
-def test_coarse_stage_at_the_largest_cube_count(prec):
+@pytest.mark.parametrize("grid,n_cubes", [((4, 32, 1136), 2272), ((4, 32, 548), 1096)],
+                         ids=["2272cubes", "1096cubes"])
+def test_coarse_stage_at_large_cube_counts(prec, grid, n_cubes):
     """2272 cubes (grid 4x32x1136), the most the coarse kernel holds (16
-    rows of logits in LDS, 36 key chunks of 64 per row): top-K 32 (pruned
-    candidates), 100 (bitwise-search fallback) and Nc, with Oc and lse."""
+    rows of logits in LDS, up to 40 key chunks of 64 per row, one workgroup
+    per CU), and 1096 cubes (20 chunks per row, two workgroups per CU with
+    128 ranking candidates per wave): top-K 32 (pruned candidate ranking),
+    100 (bitwise search) and all cubes, plus the mass rule (long lists, more
+    candidates than the scratch holds)."""
+    from tests.gpu_util import check_mass_row
     vsa = _vsa()
-    grid = (4, 32, 1136)
-    log(f"coarse stage at 2272 cubes, {prec}")
+    log(f"coarse stage at {n_cubes} cubes, {prec}")
     inp = make_inputs(1, 1, 128, grid, dtype="bf16", seed=41)
     q, k, v = (dev(inp[n], BF16) for n in "qkv")
     _, _, _, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, grid, with_q_tiles=False)
     nc = qc.shape[2]
-    assert nc == 2272
+    assert nc == n_cubes
     pooled = [vo.pool(inp[n][0, :, 0].astype(np.float64), *grid) for n in "qkv"]
     oc_ref, S, lse_ref = vo.coarse_attention(*pooled, 1.0 / np.sqrt(128))
     for K in (32, 100, nc):
@@ -185,6 +190,16 @@ def test_coarse_stage_at_the_largest_cube_count(prec):
         check_selection(sel.cpu().numpy(), S[None, None], K)
     assert_close(host64(oc)[0, 0], oc_ref, F32, "oc")
     np.testing.assert_allclose(host64(lse)[0, 0], lse_ref, atol=COARSE_LSE_ATOL[prec])
+    mass, k_min, k_max = 0.3, 4, 96
+    _, _, counts, ids = vsa.vsa_coarse_select_mass(qc, kc, vc, mass, k_min, k_max, input_dtype=prec)
+    torch.cuda.synchronize()
+    counts, ids = counts.cpu().numpy()[0, 0], ids.cpu().numpy()[0, 0]
+    banded = 0
+    for r in range(0, nc, 7):  # every 7th row against the fp64 logits
+        n = int(counts[r])
+        assert k_min <= n <= k_max
+        banded += not check_mass_row(ids[r][:n], S[r], mass, k_min, k_max)
+    assert banded <= 2
 
 
 def test_coarse_topk_zero_skips_selection():

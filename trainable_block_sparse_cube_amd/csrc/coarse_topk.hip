@@ -75,12 +75,24 @@ constexpr int kNW = 8;        // waves per workgroup
 // last 32-key step) and a multiple of 8, so that both bf16 planes of a
 // probability row start 16-byte aligned.
 __host__ __device__ constexpr int coarse_pitch(int nc) { return (nc + 39) & ~7; }
-constexpr int kCandCap = 256; // candidates ranked directly per row
+constexpr int kCandCap = 256; // candidates ranked directly per row (at most)
+
+// Candidate capacity per wave for nc cubes: 256 where two workgroups per CU
+// still fit in LDS with it, else 128 where they fit with that (rows of up
+// to 1120 cubes), else 256 (one workgroup per CU either way).  Rows with
+// more candidates take the bitwise-search path, which gives the same ids.
+int coarse_cand_cap(int nc) {
+  const size_t s_bytes = sizeof(float) * (size_t)16 * coarse_pitch(nc);
+  const size_t half = kLdsBudget / 2;
+  if (s_bytes + sizeof(float) * 2 * kNW * 256 <= half) return 256;
+  if (s_bytes + sizeof(float) * 2 * kNW * 128 <= half) return 128;
+  return kCandCap;
+}
 
 // Top-K of one row held by one wave.  `keys` holds this lane's order keys
 // of entries lane + 64 j (0 past the end; real order keys are never 0).
 // Writes the topk entries with the largest (key, -index) to out[0..topk),
-// ascending by index.  `ck`/`ci` are per-wave LDS scratch of kCandCap words.
+// ascending by index.  `ck`/`ci` are per-wave LDS scratch of `cap` words.
 //
 // For K <= 64 the K-th largest of the 64 per-lane maxima is a lower bound
 // lo on the row's K-th largest key (the lane maxima are row entries), so
@@ -92,7 +104,7 @@ constexpr int kCandCap = 256; // candidates ranked directly per row
 template <int MAXJ>
 __device__ __forceinline__ void select_row(const uint32_t (&keys)[MAXJ], int nc, int topk,
                                            int lane, uint32_t* __restrict__ ck,
-                                           int32_t* __restrict__ ci, int32_t* __restrict__ out) {
+                                           int32_t* __restrict__ ci, int32_t* __restrict__ out, int cap) {
   const uint64_t lt_mask = (1ull << lane) - 1ull;
   uint32_t lo = 0;
   if (topk <= 64) {
@@ -108,11 +120,11 @@ __device__ __forceinline__ void select_row(const uint32_t (&keys)[MAXJ], int nc,
       const bool in = keys[j] >= lo && keys[j] != 0u;
       const uint64_t m = __ballot(in);
       const int pos = ncand + __popcll(m & lt_mask);
-      if (in && pos < kCandCap) { ck[pos] = keys[j]; ci[pos] = 64 * j + lane; }
+      if (in && pos < cap) { ck[pos] = keys[j]; ci[pos] = 64 * j + lane; }
       ncand += __popcll(m);
     }
   }
-  if (ncand <= kCandCap) {
+  if (ncand <= cap) {
     __builtin_amdgcn_wave_barrier();
     int base = 0;
     for (int i0 = 0; i0 < ncand; i0 += 64) {
@@ -227,15 +239,15 @@ __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
     const float* __restrict__ qc, const float* __restrict__ kc,
     const float* __restrict__ vc, int nc, int topk, float scale,
     float* __restrict__ oc, float* __restrict__ lse, int32_t* __restrict__ sel,
-    float mass, int k_min, int k_max, int32_t* __restrict__ counts) {
+    float mass, int k_min, int k_max, int32_t* __restrict__ counts, int cand_cap) {
   constexpr int R = 16;
   constexpr int DQ = D / 4;          // head_dim slice per lane group
   constexpr int NCW = D / 16;        // waves that own a 16-column output block
   extern __shared__ float lds[];
   const int s_pitch = coarse_pitch(nc);  // room for a zero-padded last key block
   float* S = lds;                      // [R][s_pitch]
-  uint32_t* cand_k = reinterpret_cast<uint32_t*>(S + R * s_pitch);  // [kNW][kCandCap]
-  int32_t* cand_i = reinterpret_cast<int32_t*>(cand_k + kNW * kCandCap);
+  uint32_t* cand_k = reinterpret_cast<uint32_t*>(S + R * s_pitch);  // [kNW][cand_cap]
+  int32_t* cand_i = reinterpret_cast<int32_t*>(cand_k + kNW * cand_cap);
 
   const int bh = blockIdx.y;
   const int row0 = blockIdx.x * R;
@@ -354,8 +366,8 @@ __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
       for (int j = 0; j < MAXJ; ++j) keys[j] = sv[j] == -INFINITY ? 0u : order_key(sv[j]);
     }
     if (topk > 0 && !counts)
-      select_row<MAXJ>(keys, nc, topk, lane, cand_k + wave * kCandCap, cand_i + wave * kCandCap,
-                       sel + ((int64_t)bh * nc + row) * topk);
+      select_row<MAXJ>(keys, nc, topk, lane, cand_k + wave * cand_cap, cand_i + wave * cand_cap,
+                       sel + ((int64_t)bh * nc + row) * topk, cand_cap);
     float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < MAXJ; ++j) m = fmaxf(m, sv[j]);
@@ -373,8 +385,8 @@ __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
     if (counts) {  // mass rule: this row's length, then its top-n by the same ranking
       const int n = mass_length<MAXJ>(keys, sv, inv, nc, mass, k_min, k_max);
       if (lane == 0) counts[(int64_t)bh * nc + row] = n;
-      select_row<MAXJ>(keys, nc, n, lane, cand_k + wave * kCandCap, cand_i + wave * kCandCap,
-                       sel + ((int64_t)bh * nc + row) * k_max);
+      select_row<MAXJ>(keys, nc, n, lane, cand_k + wave * cand_cap, cand_i + wave * cand_cap,
+                       sel + ((int64_t)bh * nc + row) * k_max, cand_cap);
     }
     if constexpr (X3) {
       // P as two bf16 planes in the row's own storage: hi at [0, s_pitch),
@@ -502,7 +514,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
 
 size_t coarse_lds_bytes(int nc) {
   const int s_pitch = coarse_pitch(nc);
-  return sizeof(float) * ((size_t)16 * s_pitch + (size_t)2 * kNW * kCandCap);
+  return sizeof(float) * ((size_t)16 * s_pitch + (size_t)2 * kNW * coarse_cand_cap(nc));
 }
 
 template <int D, int MAXJ, bool X3, bool PK>
@@ -515,13 +527,15 @@ hipError_t launch_coarse_dj(const CoarseArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)((a.nc + 15) / 16), (unsigned)(a.B * a.heads));
   kern<<<grid, 64 * kNW, lds, st>>>(a.qc, a.kc, a.vc, a.nc, a.topk, 1.0f / sqrtf((float)D),
-                                a.oc, a.lse, a.sel, a.mass, a.k_min, a.k_max, a.counts);
+                                a.oc, a.lse, a.sel, a.mass, a.k_min, a.k_max, a.counts,
+                                coarse_cand_cap(a.nc));
   return hipGetLastError();
 }
 
 template <int D, bool X3, bool PK>
 hipError_t launch_coarse_d(const CoarseArgs& a, hipStream_t st) {
   if (a.nc <= 16 * 64) return launch_coarse_dj<D, 16, X3, PK>(a, st);
+  if (a.nc <= 20 * 64) return launch_coarse_dj<D, 20, X3, PK>(a, st);
   return launch_coarse_dj<D, 40, X3, PK>(a, st);
 }
 
