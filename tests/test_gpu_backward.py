@@ -38,7 +38,22 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"B{c[0]}h{c[1]}D{c[2]}g{'x'.join(map(str, c[3]))}k{c[4]}")
+def _seeded_shapes(n, seed):
+    """n small backward cases drawn once from a fixed seed: grid sides are
+    multiples of 4 (1 to 3 cubes per side), 1-2 batches, 1-3 heads, D in
+    {64, 128}, K from 1 to all cubes."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        grid = tuple(4 * int(x) for x in rng.integers(1, 4, size=3))
+        nc = grid[0] * grid[1] * grid[2] // 64
+        out.append((int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.choice([64, 128])), grid,
+                    int(rng.integers(1, nc + 1))))
+    return out
+
+
+@pytest.mark.parametrize("case", SMALL + _seeded_shapes(6, 4048),
+                         ids=lambda c: f"B{c[0]}h{c[1]}D{c[2]}g{'x'.join(map(str, c[3]))}k{c[4]}")
 def test_backward_small_full_compare(case):
     B, nh, D, grid, K = case
     log(f"backward small {case}")
