@@ -183,13 +183,14 @@ def test_forward_coarse_packed_equals_stage_call(D, grid):
 
 
 @pytest.mark.parametrize("prec", [F32, BF16], ids=["fp32-products", "bf16x3-products"])
-@pytest.mark.parametrize("grid,n_cubes", [((4, 32, 1136), 2272), ((4, 32, 548), 1096)],
-                         ids=["2272cubes", "1096cubes"])
+@pytest.mark.parametrize("grid,n_cubes", [((4, 32, 1136), 2272), ((4, 32, 548), 1096), ((4, 32, 600), 1200)],
+                         ids=["2272cubes", "1096cubes", "1200cubes"])
 def test_coarse_stage_at_large_cube_counts(prec, grid, n_cubes):
     """2272 cubes (grid 4x32x1136), the most the coarse kernel holds (16
     rows of logits in LDS, up to 40 key chunks of 64 per row, one workgroup
-    per CU), and 1096 cubes (20 chunks per row, two workgroups per CU with
-    128 ranking candidates per wave): top-K 32 (pruned candidate ranking),
+    per CU), 1096 cubes (20 chunks per row, two workgroups per CU with 128
+    ranking candidates per wave) and 1200 cubes (20 chunks, 256 candidates,
+    one workgroup per CU): top-K 32 (pruned candidate ranking),
     100 (bitwise search) and all cubes, plus the mass rule (long lists, more
     candidates than the scratch holds)."""
     from tests.gpu_util import check_mass_row
