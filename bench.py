@@ -62,8 +62,8 @@ def measured_counters():
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="long61k")
     p.add_argument("--topk", type=int, default=32)
     p.add_argument("--cpu-heads", type=int, default=8,
@@ -110,21 +110,33 @@ def cpu_baseline(inp, w, topk, heads):
     import numpy as np
     import oracle
     from workloads import coarse_flops, fine_flops
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        cores = 1
     sl = slice(0, heads)
     args = [np.ascontiguousarray(inp[n][:, :, sl]) for n in ("q", "k", "v", "gc", "gf")]
     t0 = time.perf_counter()
     oracle.forward(*args, w.grid, topk)
     dt = time.perf_counter() - t0
+    # thread pools as loaded by the run (the BLAS library loads on first use)
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        pools = [i for i in info if i.get("user_api") == "blas"] or info  # the oracle's numpy BLAS
+        cores = max((i.get("num_threads", 1) for i in pools), default=1)
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info
+                                 if i.get("user_api") == "blas"})) or blas
+    except Exception:  # pragma: no cover
+        cores = 1
+    cpu_model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     flops = fine_flops(w.B, heads, w.N, topk, w.head_dim) + coarse_flops(w.B, heads, w.n_cubes, w.head_dim)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"full fp64 forward of heads 0..{heads - 1} of {w.heads} (B={w.B}, grid "
                       f"{'x'.join(map(str, w.grid))}, top-K {topk}) in {dt:.1f} s; heads are independent",
-            "seconds": dt, "cpu": platform.processor() or platform.machine()}
+            "seconds": dt, "cpu": cpu_model, "blas": blas}
 
 
 def main():
