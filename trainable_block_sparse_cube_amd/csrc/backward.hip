@@ -85,12 +85,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
     const int s = tid / CPR + ps * RPP;
     const int tok = raster_tok(c, s, Hg, Wg);
     const int64_t gidx = ((int64_t)b * N + tok) * nh + h;
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(dout + gidx * D + ch * EPC);
+    // dO and O_fine are read once in the backward: non-temporal loads
+    const u32x4 raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dout + gidx * D + ch * EPC));
     bf16 gv[EPC];
     __builtin_memcpy(gv, &raw, 16);
     const float gcs = (float)gc[gidx], gfs = (float)gf[gidx];
     const f32x4* op = reinterpret_cast<const f32x4*>(of + ((int64_t)bh * N + (int64_t)c * 64 + s) * D + ch * EPC);
-    const f32x4 o0 = op[0], o1 = op[1];
+    const f32x4 o0 = __builtin_nontemporal_load(op), o1 = __builtin_nontemporal_load(op + 1);
     // pc, pf: dO.Oc and dO.O_fine (the gate gradients, fp32).  pd is
     // Delta = dOf.O_fine taken with dOf rounded to bf16 exactly as the fine
     // kernels use it, so that sum_j P_ij dP_ij = Delta_i holds to fp32
