@@ -27,7 +27,9 @@
 //     logits agree to about 1e-5 relative, far inside the 1e-3 near-tie
 //     band of the selection rule, and the bf16 outputs are unaffected.  It
 //     runs on the bf16 matrix rate instead of the fp32 one (16x).
-// The softmax and the ranking are fp32 in both cases.
+// The softmax and the ranking are fp32 in both cases.  In the forward's
+// bf16 path kc and vc arrive in packed operand order (one contiguous run per
+// wave load); stage calls pass the plain [B, heads, Nc, D] means.
 #include "vsa_device.h"
 #include "vsa_launch.h"
 
