@@ -91,6 +91,33 @@ int coarse_cand_cap(int nc) {
   return kCandCap;
 }
 
+// Writes, ascending by index, every entry of the row with key > thr and
+// the need_eq lowest-index entries with key == thr (at most `limit` ids).
+// `keys` as in select_row; 0 marks entries past the end.
+template <int MAXJ>
+__device__ __forceinline__ void emit_by_threshold(const uint32_t (&keys)[MAXJ], int nc, uint32_t thr,
+                                                  int need_eq, int limit, int lane,
+                                                  int32_t* __restrict__ out) {
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  int base = 0, eq_seen = 0;
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    if (64 * j < nc) {
+      const int idx = 64 * j + lane;
+      const bool valid = idx < nc && keys[j] != 0u;
+      const bool gt = valid && keys[j] > thr;
+      const bool eq = valid && keys[j] == thr;
+      const uint64_t eq_mask = __ballot(eq);
+      const bool take = gt || (eq && (eq_seen + __popcll(eq_mask & lt_mask)) < need_eq);
+      const uint64_t take_mask = __ballot(take);
+      const int pos = base + __popcll(take_mask & lt_mask);
+      if (take && pos < limit) out[pos] = idx;
+      base += __popcll(take_mask);
+      eq_seen += __popcll(eq_mask);
+    }
+  }
+}
+
 // Top-K of one row held by one wave.  `keys` holds this lane's order keys
 // of entries lane + 64 j (0 past the end; real order keys are never 0).
 // Writes the topk entries with the largest (key, -index) to out[0..topk),
@@ -166,29 +193,15 @@ __device__ __forceinline__ void select_row(const uint32_t (&keys)[MAXJ], int nc,
 #pragma unroll
   for (int j = 0; j < MAXJ; ++j)
     if (64 * j < nc) n_gt += __popcll(__ballot(keys[j] > thr));
-  const int need_eq = topk - n_gt;
-  int base = 0, eq_seen = 0;
-#pragma unroll
-  for (int j = 0; j < MAXJ; ++j) {
-    if (64 * j < nc) {
-      const int idx = 64 * j + lane;
-      const bool valid = idx < nc;
-      const bool gt = valid && keys[j] > thr;
-      const bool eq = valid && keys[j] == thr;
-      const uint64_t eq_mask = __ballot(eq);
-      const bool take = gt || (eq && (eq_seen + __popcll(eq_mask & lt_mask)) < need_eq);
-      const uint64_t take_mask = __ballot(take);
-      const int pos = base + __popcll(take_mask & lt_mask);
-      if (take && pos < topk) out[pos] = idx;
-      base += __popcll(take_mask);
-      eq_seen += __popcll(eq_mask);
-    }
-  }
+  emit_by_threshold<MAXJ>(keys, nc, thr, topk - n_gt, topk, lane, out);
 }
 
 // Length of a row's list under the mass rule: the shortest prefix of the
 // ranking (order key descending, index ascending) whose probability mass
-// reaches `mass`, clamped to [k_min, k_max].  e[j] * inv is the
+// reaches `mass` (unclamped; the caller clamps to [k_min, k_max]).  Also
+// returns the threshold key thr and the count n_gt of entries above it, so
+// an unclamped list is emitted directly: the entries above thr plus the
+// first n - n_gt ties at thr.  e[j] * inv is the
 // probability of entry 64 j + lane (0 past the end).  The mass of all
 // entries with key >= t falls as t grows, so the largest t whose mass still
 // reaches `mass` comes from a greedy bitwise search (wave sums are
@@ -198,7 +211,8 @@ __device__ __forceinline__ void select_row(const uint32_t (&keys)[MAXJ], int nc,
 // Total mass below `mass` (rounding) gives every entry.
 template <int MAXJ>
 __device__ __forceinline__ int mass_length(const uint32_t (&keys)[MAXJ], const float (&e)[MAXJ],
-                                           float inv, int nc, float mass, int k_min, int k_max) {
+                                           float inv, int nc, float mass, uint32_t& thr_out,
+                                           int& n_gt_out) {
   float p[MAXJ];
 #pragma unroll
   for (int j = 0; j < MAXJ; ++j) p[j] = e[j] * inv;
@@ -228,7 +242,9 @@ __device__ __forceinline__ int mass_length(const uint32_t (&keys)[MAXJ], const f
   p_eq = wave_max(p_eq);
   int n = n_gt;
   for (float acc = m_gt; n - n_gt < n_eq && acc < mass; ++n) acc += p_eq;
-  return min(max(n, k_min), k_max);
+  thr_out = thr;
+  n_gt_out = n_gt;
+  return n;
 }
 
 // One workgroup: R = 16 query rows of one (batch, head), 8 waves.  With PK
@@ -385,10 +401,17 @@ __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
     z = wave_sum(z);
     const float inv = 1.0f / z;
     if (counts) {  // mass rule: this row's length, then its top-n by the same ranking
-      const int n = mass_length<MAXJ>(keys, sv, inv, nc, mass, k_min, k_max);
+      uint32_t thr;
+      int n_gt;
+      const int n_raw = mass_length<MAXJ>(keys, sv, inv, nc, mass, thr, n_gt);
+      const int n = min(max(n_raw, k_min), k_max);
       if (lane == 0) counts[(int64_t)bh * nc + row] = n;
-      select_row<MAXJ>(keys, nc, n, lane, cand_k + wave * cand_cap, cand_i + wave * cand_cap,
-                       sel + ((int64_t)bh * nc + row) * k_max, cand_cap);
+      int32_t* out = sel + ((int64_t)bh * nc + row) * k_max;
+      if (n == n_raw)  // the top n are the entries above thr and the first ties at thr
+        emit_by_threshold<MAXJ>(keys, nc, thr, n - n_gt, n, lane, out);
+      else
+        select_row<MAXJ>(keys, nc, n, lane, cand_k + wave * cand_cap, cand_i + wave * cand_cap, out,
+                         cand_cap);
     }
     if constexpr (X3) {
       // P as two bf16 planes in the row's own storage: hi at [0, s_pitch),
