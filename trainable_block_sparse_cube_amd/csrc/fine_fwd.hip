@@ -254,6 +254,7 @@ __global__ __launch_bounds__(64) void fine_fwd_f32_kernel(
     float* __restrict__ out, float* __restrict__ lse_f, float* __restrict__ o_fine) {
   __shared__ float k_lds[64 * D];
   __shared__ float v_lds[D * 64];
+  __shared__ float s_lds[64][65];  // this tile's scaled logits, [key][query slot]
   const int slot = threadIdx.x;
   const int blk = blockIdx.x;
   const int bh = blk / nc;
@@ -277,14 +278,13 @@ __global__ __launch_bounds__(64) void fine_fwd_f32_kernel(
     __syncthreads();
     for (int i = slot; i < 64 * D; i += 64) { k_lds[i] = ks[i]; v_lds[i] = vs[i]; }
     __syncthreads();
-    float sj[64];
     float mx = -INFINITY;
     for (int j = 0; j < 64; ++j) {
       float s = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) s = fmaf(qv[d], k_lds[j * D + d], s);
-      sj[j] = s * scale;
-      mx = fmaxf(mx, sj[j]);
+      s_lds[j][slot] = s * scale;
+      mx = fmaxf(mx, s * scale);
     }
     const float m_new = fmaxf(m_run, mx);
     const float alpha = expf(m_run - m_new);
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(64) void fine_fwd_f32_kernel(
 #pragma unroll
     for (int d = 0; d < D; ++d) acc[d] *= alpha;
     for (int j = 0; j < 64; ++j) {
-      const float w = expf(sj[j] - m_new);
+      const float w = expf(s_lds[j][slot] - m_new);
       l_run += w;
 #pragma unroll
       for (int d = 0; d < D; ++d) acc[d] = fmaf(w, v_lds[j * D + d], acc[d]);
