@@ -334,6 +334,29 @@ def test_forward_is_deterministic():
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
+def test_mass_and_varlen_paths_are_deterministic():
+    """The mass-rule forward (coarse rule, CSR packing, sorted fine stage)
+    and the varlen forward and backward give bitwise-equal results when
+    called twice on the same inputs."""
+    vsa = _vsa()
+    grid = (8, 16, 16)
+    inp = make_inputs(2, 3, 128, grid, dtype="bf16", seed=12, with_dout=True)
+    args = [dev(inp[n], BF16) for n in ("q", "k", "v", "gc", "gf")]
+    do = dev(inp["dout"], BF16)
+    runs = [vsa.vsa_forward_mass(*args, grid, 0.3, 2, 20, save=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    (o1, f1, i1, _), (o2, f2, i2, _) = runs
+    assert torch.equal(f1, f2) and torch.equal(i1, i2) and torch.equal(o1, o2)
+    out1, sv1 = vsa.block_sparse_attn_varlen(*args, grid, f1, i1, save=True)
+    out2, sv2 = vsa.block_sparse_attn_varlen(*args, grid, f1, i1, save=True)
+    g1 = vsa.block_sparse_attn_varlen_backward(*args, do, f1, i1, sv1, grid)
+    g2 = vsa.block_sparse_attn_varlen_backward(*args, do, f1, i1, sv2, grid)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(out1, o1)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
 def test_probe_tile_gather_runs_on_every_depth():
     """The measurement helper (no arithmetic) accepts the forward's tiles and
     selection at every depth and leaves the tiles untouched."""
