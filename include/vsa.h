@@ -27,7 +27,10 @@
  *    (round to nearest even).  VSA_F32 uses fp32 arithmetic throughout.
  *  - Shapes: B batch, `heads` heads, head_dim D in {64, 128}; a latent grid
  *    of T x H x W tokens, N = T*H*W, each of T, H, W a positive multiple of
- *    4 ([VSA-sum, Limitations]).  Nc = N / 64 cubes.
+ *    4 ([VSA-sum, Limitations]).  Nc = N / 64 cubes, at most 3584 per
+ *    (batch, head) (VSA_ERR_UNSUPPORTED beyond: the coarse stage keeps
+ *    blocks of logit rows in LDS and the row it ranks in registers);
+ *    B*heads at most 65535.
  *  - Token order is raster, token (t, y, x) at (t*H + y)*W + x.
  *    q, k, v, out, dout, dq, dk, dv: [B, N, heads, D].
  *    gate_c, gate_f: [B, N, heads] (one scalar per token and head,

@@ -67,9 +67,10 @@ def test_workspace_sizes(lib):
     assert sv >= 4 * (B * nh * nc * D + B * nh * nc + B * nh * N + B * nh * N * D)
     bw = lib.vsa_backward_workspace_bytes(B, nh, D, T, H, W, _lib.VSA_BF16, B * nh * nc * 32)
     assert bw > fw
-    # the coarse stage holds at most 2272 cubes (16 rows of logits in LDS)
-    assert lib.vsa_forward_workspace_bytes(1, 1, 128, 4, 4, 4 * 2272, _lib.VSA_BF16) > 0
-    assert lib.vsa_forward_workspace_bytes(1, 1, 128, 4, 4, 4 * 2273, _lib.VSA_BF16) == 0
+    # the coarse stage holds at most 3584 cubes (8 rows of logits in LDS,
+    # 56 chunks of 64 per row in registers)
+    assert lib.vsa_forward_workspace_bytes(1, 1, 128, 4, 4, 4 * 3584, _lib.VSA_BF16) > 0
+    assert lib.vsa_forward_workspace_bytes(1, 1, 128, 4, 4, 4 * 3585, _lib.VSA_BF16) == 0
     # invalid shapes size to 0
     assert lib.vsa_forward_workspace_bytes(B, nh, D, 6, H, W, _lib.VSA_BF16) == 0
     assert lib.vsa_forward_workspace_bytes(B, nh, 96, T, H, W, _lib.VSA_BF16) == 0

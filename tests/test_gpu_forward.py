@@ -157,8 +157,9 @@ def test_coarse_stage_and_exact_ties(prec):
     assert straddled > 0
 
 
-@pytest.mark.parametrize("D,grid", [(128, (8, 12, 20)), (64, (8, 36, 44)), (128, (4, 40, 48))],
-                         ids=["D128-30cubes", "D64-198cubes", "D128-120cubes"])
+@pytest.mark.parametrize("D,grid", [(128, (8, 12, 20)), (64, (8, 36, 44)), (128, (4, 40, 48)),
+                                   (64, (4, 32, 1200))],
+                         ids=["D128-30cubes", "D64-198cubes", "D128-120cubes", "D64-2400cubes"])
 def test_forward_coarse_packed_equals_stage_call(D, grid):
     """The bf16 forward hands the coarse kernel its pooled K and V in packed
     operand order (padding keys zeroed); the stage call reads plain means.
@@ -183,14 +184,17 @@ def test_forward_coarse_packed_equals_stage_call(D, grid):
 
 
 @pytest.mark.parametrize("prec", [F32, BF16], ids=["fp32-products", "bf16x3-products"])
-@pytest.mark.parametrize("grid,n_cubes", [((4, 32, 1136), 2272), ((4, 32, 548), 1096), ((4, 32, 600), 1200)],
-                         ids=["2272cubes", "1096cubes", "1200cubes"])
+@pytest.mark.parametrize("grid,n_cubes", [((4, 32, 1792), 3584), ((4, 32, 1200), 2400),
+                                           ((4, 32, 1136), 2272), ((4, 32, 548), 1096),
+                                           ((4, 32, 600), 1200)],
+                         ids=["3584cubes", "2400cubes", "2272cubes", "1096cubes", "1200cubes"])
 def test_coarse_stage_at_large_cube_counts(prec, grid, n_cubes):
-    """2272 cubes (grid 4x32x1136), the most the coarse kernel holds (16
-    rows of logits in LDS, up to 40 key chunks of 64 per row, one workgroup
-    per CU), 1096 cubes (20 chunks per row, two workgroups per CU with 128
-    ranking candidates per wave) and 1200 cubes (20 chunks, 256 candidates,
-    one workgroup per CU): top-K 32 (pruned candidate ranking),
+    """3584 cubes (grid 4x32x1792), the most the coarse kernel holds (8 rows
+    of logits in LDS, 56 key chunks of 64 per row in registers); 2400 cubes
+    (8 rows, 40 chunks); 2272 cubes, the most with 16 rows; 1096 cubes (20
+    chunks per row, two workgroups per CU with 128 ranking candidates per
+    wave) and 1200 cubes (20 chunks, 256 candidates, one workgroup per CU):
+    top-K 32 (pruned candidate ranking),
     100 (bitwise search) and all cubes, plus the mass rule (long lists, more
     candidates than the scratch holds)."""
     from tests.gpu_util import check_mass_row

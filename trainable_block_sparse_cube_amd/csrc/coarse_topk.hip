@@ -83,8 +83,15 @@ constexpr int kCandCap = 256; // candidates ranked directly per row (at most)
 // still fit in LDS with it, else 128 where they fit with that (rows of up
 // to 1120 cubes), else 256 (one workgroup per CU either way).  Rows with
 // more candidates take the bitwise-search path, which gives the same ids.
+// Rows of logits a workgroup holds in LDS: 16 while they fit with a full
+// candidate scratch (up to 2272 cubes), else 8 (up to 3584 cubes).
+int coarse_rows(int nc) {
+  const size_t need16 = sizeof(float) * ((size_t)16 * coarse_pitch(nc) + (size_t)2 * kNW * kCandCap);
+  return need16 <= kLdsBudget ? 16 : 8;
+}
+
 int coarse_cand_cap(int nc) {
-  const size_t s_bytes = sizeof(float) * (size_t)16 * coarse_pitch(nc);
+  const size_t s_bytes = sizeof(float) * (size_t)coarse_rows(nc) * coarse_pitch(nc);
   const size_t half = kLdsBudget / 2;
   if (s_bytes + sizeof(float) * 2 * kNW * 256 <= half) return 256;
   if (s_bytes + sizeof(float) * 2 * kNW * 128 <= half) return 128;
@@ -257,18 +264,21 @@ __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
     const float* __restrict__ qc, const float* __restrict__ kc,
     const float* __restrict__ vc, int nc, int topk, float scale,
     float* __restrict__ oc, float* __restrict__ lse, int32_t* __restrict__ sel,
-    float mass, int k_min, int k_max, int32_t* __restrict__ counts, int cand_cap) {
+    float mass, int k_min, int k_max, int32_t* __restrict__ counts, int cand_cap, int rows) {
+  // The MFMA tiles span R = 16 query rows; the workgroup owns the first
+  // `rows` of them (16, or 8 for rows too long for 16 in LDS).  Rows past
+  // `rows` are computed in step 1 but neither stored nor used.
   constexpr int R = 16;
   constexpr int DQ = D / 4;          // head_dim slice per lane group
   constexpr int NCW = D / 16;        // waves that own a 16-column output block
   extern __shared__ float lds[];
   const int s_pitch = coarse_pitch(nc);  // room for a zero-padded last key block
   float* S = lds;                      // [R][s_pitch]
-  uint32_t* cand_k = reinterpret_cast<uint32_t*>(S + R * s_pitch);  // [kNW][cand_cap]
+  uint32_t* cand_k = reinterpret_cast<uint32_t*>(S + rows * s_pitch);  // [kNW][cand_cap]
   int32_t* cand_i = reinterpret_cast<int32_t*>(cand_k + kNW * cand_cap);
 
   const int bh = blockIdx.y;
-  const int row0 = blockIdx.x * R;
+  const int row0 = blockIdx.x * rows;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, lg = lane >> 4;
@@ -322,7 +332,8 @@ __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
       const int key = j0 + li;
       if (key < nc) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[(4 * lg + r) * s_pitch + key] = (acc[r] + acc2[r]) * scale;
+        for (int r = 0; r < 4; ++r)
+          if (4 * lg + r < rows) S[(4 * lg + r) * s_pitch + key] = (acc[r] + acc2[r]) * scale;
       }
     }
   } else {
@@ -357,14 +368,15 @@ __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
       const int key = j0 + li;
       if (key < nc) {
   #pragma unroll
-        for (int r = 0; r < 4; ++r) S[(4 * lg + r) * s_pitch + key] = acc[r] * scale;
+        for (int r = 0; r < 4; ++r)
+          if (4 * lg + r < rows) S[(4 * lg + r) * s_pitch + key] = acc[r] * scale;
       }
     }
   }
   __syncthreads();
 
   // ---- 2. per-row top-K and softmax, one wave per row
-  for (int rr = wave; rr < R; rr += kNW) {
+  for (int rr = wave; rr < rows; rr += kNW) {
     const int row = row0 + rr;
     float* Srow = S + rr * s_pitch;
     if (row >= nc) {  // keep padded rows finite for phase 3
@@ -451,7 +463,8 @@ __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
     constexpr int NKS = kNW / NCB;
     const int cb = wave % NCB, kq = wave / NCB;
     const int col = 16 * cb + li;
-    const bf16* prow = reinterpret_cast<const bf16*>(S + li * s_pitch);
+    // rows past `rows` read the last held row: their outputs are dropped
+    const bf16* prow = reinterpret_cast<const bf16*>(S + min(li, rows - 1) * s_pitch);
     auto load_v = [&](int j0, float (&vbuf)[8]) {
       if constexpr (PK) {  // this lane's 8 keys of column col, contiguous (step j0 / 32)
         const f32x4v* src = reinterpret_cast<const f32x4v*>(vcb + (int64_t)j0 * D + (cb * 64 + lane) * 8);
@@ -499,7 +512,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = row0 + 4 * lg + r;
-      if (row < nc) oc[((int64_t)bh * nc + row) * D + col] = oacc[r];
+      if (row < nc && 4 * lg + r < rows) oc[((int64_t)bh * nc + row) * D + col] = oacc[r];
     }
   } else {
     // ---- 3. Oc = P * vc.  Wave w < D/16 owns output columns [16w, 16w + 16);
@@ -524,14 +537,14 @@ __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
         if (j0 + 32 < nc) load_v(j0 + 32, vn);
   #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const float pa = S[li * s_pitch + j0 + 4 * t + lg];
+          const float pa = S[min(li, rows - 1) * s_pitch + j0 + 4 * t + lg];
           oacc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vb[t], oacc, 0, 0, 0);
         }
       }
   #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = row0 + 4 * lg + r;
-        if (row < nc) oc[((int64_t)bh * nc + row) * D + col] = oacc[r];
+        if (row < nc && 4 * lg + r < rows) oc[((int64_t)bh * nc + row) * D + col] = oacc[r];
       }
     }
   }
@@ -539,7 +552,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void coarse_topk_kernel(
 
 size_t coarse_lds_bytes(int nc) {
   const int s_pitch = coarse_pitch(nc);
-  return sizeof(float) * ((size_t)16 * s_pitch + (size_t)2 * kNW * coarse_cand_cap(nc));
+  return sizeof(float) * ((size_t)coarse_rows(nc) * s_pitch + (size_t)2 * kNW * coarse_cand_cap(nc));
 }
 
 template <int D, int MAXJ, bool X3, bool PK>
@@ -550,10 +563,11 @@ hipError_t launch_coarse_dj(const CoarseArgs& a, hipStream_t st) {
   // setting belongs to the current device, and the call is cheap).
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  dim3 grid((unsigned)((a.nc + 15) / 16), (unsigned)(a.B * a.heads));
+  const int rows = coarse_rows(a.nc);
+  dim3 grid((unsigned)((a.nc + rows - 1) / rows), (unsigned)(a.B * a.heads));
   kern<<<grid, 64 * kNW, lds, st>>>(a.qc, a.kc, a.vc, a.nc, a.topk, 1.0f / sqrtf((float)D),
                                 a.oc, a.lse, a.sel, a.mass, a.k_min, a.k_max, a.counts,
-                                coarse_cand_cap(a.nc));
+                                coarse_cand_cap(a.nc), rows);
   return hipGetLastError();
 }
 
@@ -561,18 +575,19 @@ template <int D, bool X3, bool PK>
 hipError_t launch_coarse_d(const CoarseArgs& a, hipStream_t st) {
   if (a.nc <= 16 * 64) return launch_coarse_dj<D, 16, X3, PK>(a, st);
   if (a.nc <= 20 * 64) return launch_coarse_dj<D, 20, X3, PK>(a, st);
-  return launch_coarse_dj<D, 40, X3, PK>(a, st);
+  if (a.nc <= 40 * 64) return launch_coarse_dj<D, 40, X3, PK>(a, st);
+  return launch_coarse_dj<D, 56, X3, PK>(a, st);  // the most chunks that fit in registers
 }
 
 }  // namespace
 
 int coarse_max_cubes(int D) {
   (void)D;
-  // 16 rows of logits plus candidate scratch in LDS, and at most 40 key
-  // chunks of 64 per row.
-  const int max_pitch = (int)((kLdsBudget / sizeof(float) - 2 * kNW * kCandCap) / 16) & ~7;
+  // 8 rows of logits plus candidate scratch in LDS, and at most 56 key
+  // chunks of 64 per row (the row a wave ranks sits in its registers).
+  const int max_pitch = (int)((kLdsBudget / sizeof(float) - 2 * kNW * kCandCap) / 8) & ~7;
   const int by_lds = max_pitch - 32;  // largest nc with coarse_pitch(nc) <= max_pitch
-  return by_lds < 40 * 64 ? by_lds : 40 * 64;
+  return by_lds < 56 * 64 ? by_lds : 56 * 64;
 }
 
 hipError_t launch_coarse_topk(const CoarseArgs& a, hipStream_t st) {
