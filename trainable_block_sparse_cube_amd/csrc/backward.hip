@@ -29,6 +29,10 @@
 // Both stream their per-pair tiles (Q and dOf, resp. K and V; 16 KB each
 // at D = 128, natural [token][D] layout) with global->LDS copies, double
 // buffered, and take every transposed operand from transposing LDS reads.
+// Each wave raises its issue priority for its two MFMA bursts per tile
+// (s_setprio 1, back to 0 for the softmax arithmetic), so a SIMD's matrix
+// unit is fed first while the other resident wave runs its VALU work; the
+// order of every wave's own arithmetic, hence the result, is unchanged.
 #include <climits>
 
 #include "vsa_device.h"
@@ -464,6 +468,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(
     f32x16 sa, da;
 #pragma unroll
     for (int r = 0; r < 16; ++r) { sa[r] = 0.f; da[r] = 0.f; }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kB[s], sa, 0, 0, 0);
@@ -474,6 +479,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(
     const uint32_t xbase = lds_addr(qh ? qb : ob);
     bf16x8 xa[4];
     tile_tr8_asm<D, 4>(xa, xbase + tr_lo, xbase + tr_hi);
+    __builtin_amdgcn_s_setprio(0);
     // this lane: key column ql, query rows 32qh + 8(r/4) + 4hf + r%4
     bf16x8 pB[2], dsB[2];
 #pragma unroll
@@ -499,6 +505,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(
       bq0[g] = qh ? other : pB[g];
       bq1[g] = qh ? dsB[g] : other;
     }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int m = 0; m < MD; ++m) {
       if (m > 0) tile_tr8_asm<D, 4>(xa, (xbase + tr_lo) ^ (m << 6), (xbase + tr_hi) ^ (m << 6));
@@ -506,6 +513,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(
       for (int t = 0; t < 4; ++t)
         acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[t], t < 2 ? bq0[t] : bq1[t - 2], acc[m], 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // raster rows of this wave's keys, coarse share (mean adjoint) added
@@ -621,6 +629,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(
     f32x16 sa, da;
 #pragma unroll
     for (int r = 0; r < 16; ++r) { sa[r] = 0.f; da[r] = 0.f; }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qB[s], sa, 0, 0, 0);
@@ -630,6 +639,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(
     const uint32_t kbase = lds_addr(kb);
     bf16x8 ta[MD][2];
     tile_tr8_asm_cols<D, MD>(ta, kbase + tr_lo, kbase + tr_hi);
+    __builtin_amdgcn_s_setprio(0);
     // this lane: query column ql, key rows 32kh + 8(r/4) + 4hf + r%4
     bf16x8 hiB[2], loB[2];
 #pragma unroll
@@ -641,6 +651,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(
       hiB[r >> 3][r & 7] = hi;
       loB[r >> 3][r & 7] = (bf16)(ds - (float)hi);
     }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int m = 0; m < MD; ++m)
 #pragma unroll
@@ -648,6 +659,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(
         acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[m][g], hiB[g], acc[m], 0, 0, 0);
         acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[m][g], loB[g], acc[m], 0, 0, 0);
       }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   ssum += swap_halves(ssum);  // over this wave's 32 keys of every tile
