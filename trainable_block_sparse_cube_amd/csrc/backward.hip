@@ -84,18 +84,34 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
 #pragma unroll
   for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
 
+  // All passes' loads first, so that they are in flight together (the
+  // compiler keeps each pass's loads behind the previous pass's stores).
+  // dO and O_fine are read once in the backward: non-temporal loads.
+  u32x4 raws[PASSES];
+  f32x4 o0s[PASSES], o1s[PASSES];
+  float gcv[PASSES], gfv[PASSES];
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int s = tid / CPR + ps * RPP;
+    const int64_t gidx = ((int64_t)b * N + raster_tok(c, s, Hg, Wg)) * nh + h;
+    raws[ps] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dout + gidx * D + ch * EPC));
+    gcv[ps] = (float)gc[gidx];
+    gfv[ps] = (float)gf[gidx];
+    const f32x4* op = reinterpret_cast<const f32x4*>(of + ((int64_t)bh * N + (int64_t)c * 64 + s) * D + ch * EPC);
+    o0s[ps] = __builtin_nontemporal_load(op);
+    o1s[ps] = __builtin_nontemporal_load(op + 1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int ps = 0; ps < PASSES; ++ps) {
     const int s = tid / CPR + ps * RPP;
     const int tok = raster_tok(c, s, Hg, Wg);
     const int64_t gidx = ((int64_t)b * N + tok) * nh + h;
-    // dO and O_fine are read once in the backward: non-temporal loads
-    const u32x4 raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dout + gidx * D + ch * EPC));
+    const u32x4 raw = raws[ps];
     bf16 gv[EPC];
     __builtin_memcpy(gv, &raw, 16);
-    const float gcs = (float)gc[gidx], gfs = (float)gf[gidx];
-    const f32x4* op = reinterpret_cast<const f32x4*>(of + ((int64_t)bh * N + (int64_t)c * 64 + s) * D + ch * EPC);
-    const f32x4 o0 = __builtin_nontemporal_load(op), o1 = __builtin_nontemporal_load(op + 1);
+    const float gcs = gcv[ps], gfs = gfv[ps];
+    const f32x4 o0 = o0s[ps], o1 = o1s[ps];
     // pc, pf: dO.Oc and dO.O_fine (the gate gradients, fp32).  pd is
     // Delta = dOf.O_fine taken with dOf rounded to bf16 exactly as the fine
     // kernels use it, so that sum_j P_ij dP_ij = Delta_i holds to fp32
