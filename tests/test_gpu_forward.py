@@ -185,13 +185,15 @@ def test_forward_coarse_packed_equals_stage_call(D, grid):
 
 @pytest.mark.parametrize("prec", [F32, BF16], ids=["fp32-products", "bf16x3-products"])
 @pytest.mark.parametrize("grid,n_cubes", [((4, 32, 1792), 3584), ((4, 32, 1200), 2400),
-                                           ((4, 32, 1136), 2272), ((4, 32, 548), 1096),
-                                           ((4, 32, 600), 1200)],
-                         ids=["3584cubes", "2400cubes", "2272cubes", "1096cubes", "1200cubes"])
+                                           ((4, 36, 1012), 2277), ((4, 32, 1136), 2272),
+                                           ((4, 32, 548), 1096), ((4, 32, 600), 1200)],
+                         ids=["3584cubes", "2400cubes", "2277cubes", "2272cubes", "1096cubes",
+                              "1200cubes"])
 def test_coarse_stage_at_large_cube_counts(prec, grid, n_cubes):
     """3584 cubes (grid 4x32x1792), the most the coarse kernel holds (8 rows
     of logits in LDS, 56 key chunks of 64 per row in registers); 2400 cubes
-    (8 rows, 40 chunks); 2272 cubes, the most with 16 rows; 1096 cubes (20
+    (8 rows, 40 chunks); 2277 cubes (8 rows, the last block holding 5);
+    2272 cubes, the most with 16 rows; 1096 cubes (20
     chunks per row, two workgroups per CU with 128 ranking candidates per
     wave) and 1200 cubes (20 chunks, 256 candidates, one workgroup per CU):
     top-K 32 (pruned candidate ranking),
