@@ -333,9 +333,16 @@ __global__ __launch_bounds__(256) void transpose_scatter_kernel(
   for (int j = tid; j < nc; j += 256) cnt[j] = 0;
   for (int v = tid; v <= nc; v += 256) hist[v] = 0;
   __syncthreads();
-  for (int e = tid; e < total; e += 256) {
-    const int j = ids[base + e];
-    if (j >= 0 && j < nc) atomicAdd(&cnt[j], 1);
+  // Entries are read kBatch at a time, so that their loads are in flight
+  // together rather than one memory round trip per entry.
+  constexpr int kBatch = 8;
+  for (int e0 = tid; e0 < total; e0 += 256 * kBatch) {
+    int jj[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) jj[u] = e0 + 256 * u < total ? ids[base + e0 + 256 * u] : -1;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (jj[u] >= 0 && jj[u] < nc) atomicAdd(&cnt[jj[u]], 1);
   }
   __syncthreads();
   block_exclusive_scan(cnt, nc, start, wsum);
@@ -357,9 +364,13 @@ __global__ __launch_bounds__(256) void transpose_scatter_kernel(
   for (int c = tid; c < nc; c += 256) {
     const int e0 = offs ? offs[r0 + c] : (int)((r0 + c) * topk);
     const int e1 = offs ? offs[r0 + c + 1] : e0 + topk;
-    for (int e = e0; e < e1; ++e) {
-      const int j = ids[e];
-      if (j >= 0 && j < nc) tmp[base + atomicAdd(&cnt[j], 1)] = c;
+    for (int e = e0; e < e1; e += kBatch) {
+      int jj[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) jj[u] = e + u < e1 ? ids[e + u] : -1;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (jj[u] >= 0 && jj[u] < nc) tmp[base + atomicAdd(&cnt[jj[u]], 1)] = c;
     }
   }
 }
