@@ -400,6 +400,29 @@ def _sampled_check(w, inp, out, sel_np, K, n_samples, rng, lists=None):
     return exempt
 
 
+def test_forward_at_the_largest_cube_count():
+    """3584 cubes per (batch, head) (grid 4x32x1792, head_dim 64, 2 heads),
+    the most the library accepts: the processing-order sort at its largest
+    size (4096 keys), the coarse stage with 8-row workgroups and 56-chunk
+    rows on packed means, and the fine stage.  Every row's ids valid, and
+    sampled query cubes against the oracle one by one."""
+    import types
+    vsa = _vsa()
+    grid, B, nh, D, K = (4, 32, 1792), 1, 2, 64, 32
+    w = types.SimpleNamespace(name="3584cubes", B=B, heads=nh, head_dim=D, n_cubes=3584, grid=grid)
+    log("forward at 3584 cubes: drawing inputs")
+    inp = make_inputs(B, nh, D, grid, dtype="bf16", seed=91)
+    q, k, v, gc, gf = (dev(inp[n], BF16) for n in ("q", "k", "v", "gc", "gf"))
+    out, sel, _ = vsa.vsa_forward(q, k, v, gc, gf, grid, K)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out.float()).all())
+    sel_np = sel.cpu().numpy()
+    assert sel_np.shape == (B, nh, 3584, K)
+    assert np.all(np.diff(sel_np, axis=-1) > 0) and sel_np.min() >= 0 and sel_np.max() < 3584
+    exempt = _sampled_check(w, inp, out, sel_np, K, 8, np.random.default_rng(5))
+    log(f"  3584 cubes: sampled rows ok, near-tie exemptions {exempt}/8")
+
+
 @pytest.mark.parametrize("name,K", [("pretrain16k", 32), ("long61k", 16), ("long61k", 32),
                                     ("large70k", 32), ("train16k", 32), ("long61k_smooth", 32)])
 def test_forward_full_size_sampled(name, K):
