@@ -126,6 +126,41 @@ def test_backward_training_workload_sampled():
     log("  train16k sampled gradients ok")
 
 
+def test_backward_at_the_largest_cube_count():
+    """3584 cubes per (batch, head) (grid 4x32x1792, head_dim 64, one head),
+    the most the library accepts: the list transpose at its largest LDS
+    footprint, coarse GEMMs on 3584 x 3584 logits, long key lists for the
+    dK/dV kernel.  Gradients of sampled query and key cubes against
+    oracle.backward_sampled."""
+    grid, K = (4, 32, 1792), 32
+    log("backward at 3584 cubes: drawing inputs")
+    inp = make_inputs(1, 1, 64, grid, dtype="bf16", seed=93, with_dout=True)
+    sel, grads = _run(inp, grid, K)
+    g = [t.float().cpu().numpy() for t in grads]
+    for t in g:
+        assert np.all(np.isfinite(t))
+    members = vo.cube_members(*grid)
+    rng = np.random.default_rng(6)
+    qcs = [int(x) for x in rng.choice(3584, 4, replace=False)]
+    kcs = [int(x) for x in rng.choice(3584, 4, replace=False)]
+    out = oracle.backward_sampled(inp["q"], inp["k"], inp["v"], inp["gc"], inp["gf"], inp["dout"],
+                                  grid, list(sel[0, 0]), 0, 0, qcs, kcs)
+    acts = {n: [] for n in GRADS}
+    refs = {n: [] for n in GRADS}
+    for c in qcs:
+        rows = members[c]
+        acts["dq"].append(g[0][0, rows, 0]); refs["dq"].append(out[("dq", c)])
+        acts["dgc"].append(g[3][0, rows, 0]); refs["dgc"].append(out[("dgc", c)])
+        acts["dgf"].append(g[4][0, rows, 0]); refs["dgf"].append(out[("dgf", c)])
+    for j in kcs:
+        rows = members[j]
+        acts["dk"].append(g[1][0, rows, 0]); refs["dk"].append(out[("dk", j)])
+        acts["dv"].append(g[2][0, rows, 0]); refs["dv"].append(out[("dv", j)])
+    for n in GRADS:
+        assert_close(np.stack(acts[n]), np.stack(refs[n]), BF16, f"3584 cubes {n}")
+    log("  3584 cubes: sampled gradients ok")
+
+
 def test_backward_rejects_fp32_and_missing_state():
     vsa = _vsa()
     from trainable_block_sparse_cube_amd import _lib
