@@ -164,6 +164,43 @@ def test_forward_mass_full_size_sampled():
     log(f"  mean list length {counts.mean():.1f}; {banded}/12 sampled rows in the rounding band")
 
 
+def test_forward_mass_at_the_largest_cube_count():
+    """3584 cubes per (batch, head) (grid 4x32x1792, head_dim 64, 2 heads),
+    mass 0.1, lengths in [4, 96] (most rows unclamped, at 30 to 90 cubes):
+    the mass stage with 8-row workgroups, list packing over 7168 rows and
+    the fine stage on the packed lists.
+    Sampled rows' ids against the oracle's rule and their outputs against
+    the oracle under the GPU's lists; list properties over every row."""
+    vsa = _vsa()
+    grid, nh, mass, k_min, k_max = (4, 32, 1792), 2, 0.1, 4, 96
+    nc = 3584
+    log("mass-rule forward at 3584 cubes: drawing inputs")
+    inp = make_inputs(1, nh, 64, grid, dtype="bf16", seed=95)
+    q, k, v, gc, gf = (dev(inp[n], BF16) for n in ("q", "k", "v", "gc", "gf"))
+    out, offs, ids, _ = vsa.vsa_forward_mass(q, k, v, gc, gf, grid, mass, k_min, k_max)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out.float()).all())
+    o = offs.cpu().numpy().astype(np.int64)
+    flat = ids.cpu().numpy()
+    counts = np.diff(o)
+    assert counts.shape == (nh * nc,) and counts.min() >= k_min and counts.max() <= k_max
+    assert (counts < k_max).mean() > 0.9  # the unclamped path is the common one here
+    rng = np.random.default_rng(8)
+    outs, refs, banded = [], [], 0
+    for _ in range(8):
+        h, c = int(rng.integers(nh)), int(rng.integers(nc))
+        row = flat[o[h * nc + c]:o[h * nc + c + 1]]
+        assert np.all(np.diff(row) > 0) and row.min() >= 0 and row.max() < nc
+        rows, o_ref, _, logits = oracle.query_cube_output(
+            inp["q"], inp["k"], inp["v"], inp["gc"], inp["gf"], grid, 0, h, c, row)
+        if not check_mass_row(row, logits, mass, k_min, k_max):
+            banded += 1
+        outs.append(out[0, torch.from_numpy(rows).cuda(), h].float().cpu().numpy())
+        refs.append(o_ref)
+    assert_close(np.stack(outs), np.stack(refs), BF16, "3584 cubes mass-rule sampled rows")
+    log(f"  mean list length {counts.mean():.1f}; {banded}/8 sampled rows in the rounding band")
+
+
 # ------------------------------------------- selection quality (NEXT-4)
 @pytest.mark.parametrize("dt,D", [(F32, 64), (BF16, 128)])
 def test_max_pool_stage_is_exact(dt, D):
