@@ -9,10 +9,13 @@ and PV over the selected cubes plus the dense coarse stage).
 
 The fine kernel is also timed on its own (HIP events on the stream it is
 launched on, in the sorted processing order the forward gives it, and in
-natural order for comparison) for the roofline entry, next to its two floors on the same
-data: the library's tile-gather helper (the fine kernel's K/V reads for the
-same selection, no arithmetic) and the fine kernel on a shared selection
-(every query cube picks the same key cubes, so every tile is an L2 hit).
+natural order for comparison) for the roofline entry, next to its compute
+ceiling on the same data: the fine kernel on a shared selection (every query
+cube picks the same key cubes, so every tile is an L2 hit).  The same line
+carries the coarse stage's share of the step, the backward of the training
+workload (B=2, 12 heads, 16x32x32, top-K 32) after its forward, and a dense
+reference: the fine kernel with every key cube selected, whose MFU the
+sparse fine stage is compared with.
 The fp64 CPU oracle is timed on a bounded sample of the same workload as the
 CPU baseline.  HBM traffic of the
 fine kernel comes from the committed profiler-counter summary
@@ -72,7 +75,9 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain 1 GiB device copy (for scaling profiler byte counters)")
     p.add_argument("--extra", action="store_true",
-                   help="also time a dense reference, top-K 16, the 16K and 70400-token workloads, varlen and backward")
+                   help="also time top-K 16, the 16K and 70400-token workloads, varlen, the mass rule "
+                        "and smooth inputs")
+    p.add_argument("--no-dense", action="store_true", help="skip the dense reference (about 0.1 s of GPU time)")
     return p.parse_args()
 
 
@@ -185,10 +190,8 @@ def main():
     coarse_bytes = 4 * pooled_bytes + w.B * w.heads * w.n_cubes * (4 + 4 * K)
     fine_tflops = f_fine / (ms_fine * 1e-3) / 1e12
 
-    # floors of the fine kernel on the same data
+    # compute ceiling of the fine kernel on the same data
     tile_bytes = w.B * w.heads * w.n_cubes * K * 2 * 64 * w.head_dim * elt  # K and V tiles read
-    gather_ms = {d: timed(lambda: vsa.probe_tile_gather(kp, vp, sel2, K, d), a.steps, a.warmup, stream)
-                 for d in (1, 8)}
     shared = torch.arange(K, dtype=torch.int32, device="cuda").expand(w.B, w.heads, w.n_cubes, K).contiguous()
     ms_shared = timed(lambda: vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, w.grid, shared, topk=K, out=fout),
                       a.steps, a.warmup, stream)
@@ -216,6 +219,8 @@ def main():
         "frac_of_peak_whole_forward": (f_fine + f_coarse) / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "stages_ms": {"permute_pool": ms_pp, "coarse_topk": ms_coarse, "fine_order": ms_order,
                       "fine": ms_fine, "fine_in_natural_order": ms_fine_natural},
+        # the pages report the unfused coarse top-K at about 14 % of runtime
+        "coarse_share_of_step": ms_coarse / ms_step,
         "stage_GBs": {"permute_pool": pp_bytes / (ms_pp * 1e-3) / 1e9,
                       "coarse_topk": coarse_bytes / (ms_coarse * 1e-3) / 1e9},
         "fine_TFLOPs": fine_tflops,
@@ -240,12 +245,14 @@ def main():
         "fine_floors": {
             "tile_bytes_per_launch": tile_bytes,
             "tile_delivery_TBps": tile_bytes / (ms_fine * 1e-3) / 1e12,
-            "gather_only_ms": {f"depth{d}": t for d, t in gather_ms.items()},
-            "fine_over_best_gather": ms_fine / min(gather_ms.values()),
             "shared_selection_ms": ms_shared,
             "shared_selection_TFLOPs": f_fine / (ms_shared * 1e-3) / 1e12,
         },
     }
+    del kp, vp, fout, q, k, v, gc, gf, out
+    res["backward_train16k"] = backward_case(vsa, torch, stream, a)
+    if not a.no_dense:
+        res["dense_reference"] = dense_case(vsa, torch, stream, ms_step, fine_tflops)
     if a.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -253,7 +260,6 @@ def main():
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = 1 << 30
     if a.extra:
-        del kp, vp, fout
         res["extra"] = extra(a, vsa, torch, stream)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, w, K, min(a.cpu_heads, w.heads))
@@ -327,12 +333,23 @@ def extra(a, vsa, torch, stream):
     q, k, v, gc, gf = (dev(inp[n]) for n in ("q", "k", "v", "gc", "gf"))
     offs = torch.from_numpy(inp["kv_offsets"]).cuda()
     ids = torch.from_numpy(inp["kv_ids"]).cuda()
-    ms = timed(lambda: vsa.block_sparse_attn_varlen(q, k, v, gc, gf, w.grid, offs, ids), steps, warm, stream)
+    vsa.block_sparse_attn_varlen(q, k, v, gc, gf, w.grid, offs, ids)  # lists checked once
+    ms = timed(lambda: vsa.block_sparse_attn_varlen(q, k, v, gc, gf, w.grid, offs, ids, validate=False),
+               steps, warm, stream)
     fl = fine_flops_lists(int(ids.numel()), w.head_dim) + coarse_flops(w.B, w.heads, w.n_cubes, w.head_dim)
     ext["large70k_varlen_forward"] = {"ms": ms, "TFLOPs": fl / (ms * 1e-3) / 1e12,
                                       "mean_list_len": int(ids.numel()) / (w.B * w.heads * w.n_cubes)}
     del q, k, v, gc, gf, offs, ids, inp
 
+    return ext
+
+
+def backward_case(vsa, torch, stream, a):
+    """Forward with saved state, then the backward, on the training workload
+    (B=2, 12 heads, head_dim 128, 16x32x32, top-K 32)."""
+    from workloads import WORKLOADS, coarse_flops, fine_flops, workload_inputs
+    dev = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda().contiguous()
+    steps, warm = max(3, a.steps // 2), 3
     w = WORKLOADS["train16k"]
     inp = workload_inputs(w)
     q, k, v, gc, gf, do = (dev(inp[n]) for n in ("q", "k", "v", "gc", "gf", "dout"))
@@ -341,30 +358,40 @@ def extra(a, vsa, torch, stream):
     ms_b = timed(lambda: vsa.vsa_backward(q, k, v, gc, gf, do, sel, saved, w.grid), steps, warm, stream)
     ff = fine_flops(w.B, w.heads, w.N, 32, w.head_dim)
     fc = coarse_flops(w.B, w.heads, w.n_cubes, w.head_dim)
-    ext["train16k_k32"] = {"forward_ms": ms_f, "backward_ms": ms_b,
-                           "forward_TFLOPs": (ff + fc) / (ms_f * 1e-3) / 1e12,
-                           "backward_TFLOPs": (2.5 * ff + 2 * fc) / (ms_b * 1e-3) / 1e12,
-                           "backward_flop_model": "2.5 x fine forward + 2 x coarse forward"}
-    # dense reference through the same fine kernel: every query cube lists
-    # all Nc key cubes (plain block attention over the whole clip).  Last:
-    # its long launches heat the device, which would slow what follows.
+    tf_b = (2.5 * ff + 2 * fc) / (ms_b * 1e-3) / 1e12
+    return {"workload": f"{w.name}: B={w.B}, heads={w.heads}, head_dim={w.head_dim}, "
+                        f"grid {'x'.join(map(str, w.grid))}, top-K 32",
+            "forward_ms": ms_f, "backward_ms": ms_b,
+            "forward_TFLOPs": (ff + fc) / (ms_f * 1e-3) / 1e12,
+            "backward_TFLOPs": tf_b, "backward_frac_of_peak": tf_b / PEAK_BF16_TFLOPS,
+            "backward_flop_model": "2.5 x fine forward + 2 x coarse forward"}
+
+
+def dense_case(vsa, torch, stream, ms_step, sparse_fine_tflops):
+    """Dense reference on the headline shape through the same fine kernel:
+    every query cube lists all Nc key cubes (block attention over the whole
+    clip).  Reports its MFU, the sparse fine stage's MFU as a share of it
+    (the pages' figure of merit is 85 % of FlashAttention-3 MFU) and the
+    whole VSA forward's speedup over dense fine attention.  Run last: its
+    long launches heat the device."""
+    from workloads import WORKLOADS, fine_flops, workload_inputs
+    dev = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda().contiguous()
     w = WORKLOADS["long61k"]
     inp = workload_inputs(w, with_varlen=False)
     q, k, v, gc, gf = (dev(inp[n]) for n in ("q", "k", "v", "gc", "gf"))
+    del inp
     _, kp, vp, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, w.grid, with_q_tiles=False)
     oc, _, _ = vsa.vsa_coarse_topk(qc, kc, vc, 0, input_dtype=torch.bfloat16)
     nc = w.n_cubes
     full = torch.arange(nc, dtype=torch.int32, device="cuda").expand(w.B, w.heads, nc, nc).contiguous()
     fout = torch.empty_like(q)
-    ms_sparse = timed(lambda: vsa.vsa_forward(q, k, v, gc, gf, w.grid, 32), steps, warm, stream)
     ms_dense = timed(lambda: vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, w.grid, full, topk=nc, out=fout),
                      2, 1, stream)
-    f_dense = fine_flops(w.B, w.heads, w.N, nc, w.head_dim)
-    ext["long61k_dense_fine"] = {"ms": ms_dense, "TFLOPs": f_dense / (ms_dense * 1e-3) / 1e12,
-                                 "vsa_k32_forward_ms": ms_sparse,
-                                 "speedup_vsa_k32_over_dense": ms_dense / ms_sparse}
-    del full, fout, kp, vp, q, k, v, gc, gf, inp
-    return ext
+    tf = fine_flops(w.B, w.heads, w.N, nc, w.head_dim) / (ms_dense * 1e-3) / 1e12
+    return {"what": "fine kernel with K = Nc = 960 on the headline shape",
+            "ms": ms_dense, "TFLOPs": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS,
+            "sparse_fine_mfu_over_dense_mfu": sparse_fine_tflops / tf,
+            "speedup_vsa_k32_forward_over_dense_fine": ms_dense / ms_step}
 
 
 if __name__ == "__main__":

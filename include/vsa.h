@@ -110,7 +110,12 @@ int vsa_forward(const void* q, const void* k, const void* v,
  * indexes kv_ids, lists ordered by (b, h, query cube).  n_list_entries
  * (host) equals kv_offsets[B*heads*Nc].  Ids must lie in [0, Nc) and be
  * distinct within a list; any order.  An empty list gives O_fine = 0.
- * Out-of-range ids are not checked on the GPU: the caller guarantees them.
+ * Lists are not checked unless asked for (vsa_validate_lists, or
+ * VSA_VALIDATE=1 in the environment, below).  Malformed lists give
+ * unspecified outputs but never a memory access outside the buffers:
+ * every kernel clamps list ranges to [0, n_list_entries) and skips any id
+ * outside [0, Nc); an id listed twice counts twice, consistently in the
+ * forward and the backward.
  */
 int block_sparse_attn_varlen(const void* q, const void* k, const void* v,
                              const void* gate_c, const void* gate_f,
@@ -160,9 +165,12 @@ int vsa_forward_mass(const void* q, const void* k, const void* v,
  * gradient to the pooled tensors, which spread it evenly over each cube's
  * 64 tokens.  sel_idx / kv lists must be the ones the forward used.
  * Outputs dq, dk, dv [B,N,heads,D] (dtype) and dgate_c, dgate_f [B,N,heads]
- * (fp32) are overwritten.  Only dtype VSA_BF16 is built (VSA_F32 returns
- * VSA_ERR_UNSUPPORTED).  workspace: vsa_backward_workspace_bytes with
- * n_list_entries = B*heads*Nc*topk (resp. the varlen total).
+ * (fp32) are overwritten.  VSA_BF16 runs the products on the bf16 matrix
+ * cores with fp32 accumulation; VSA_F32 uses fp32 arithmetic throughout
+ * (plain vector code, for accuracy rather than speed).  workspace:
+ * vsa_backward_workspace_bytes with n_list_entries = B*heads*Nc*topk
+ * (resp. the varlen total).  With VSA_VALIDATE=1 the key lists (sel_idx
+ * included) are checked first as in vsa_validate_lists.
  */
 int vsa_backward(const void* q, const void* k, const void* v,
                  const void* gate_c, const void* gate_f, const void* dout,
@@ -239,8 +247,9 @@ int vsa_pack_lists(const int32_t* counts, const int32_t* ids_padded, int n_rows,
  * place); kp, vp: K and V tiles from vsa_cube_permute_pool; oc: coarse
  * output.
  * Key lists: when kv_offsets is NULL, list r is
- * kv_ids[r*topk .. r*topk + topk); otherwise the CSR lists as in
- * block_sparse_attn_varlen (topk ignored).  lse_f [B,heads,N] and
+ * kv_ids[r*topk .. r*topk + topk) (n_list_entries ignored); otherwise the
+ * CSR lists as in block_sparse_attn_varlen, kv_ids holding n_list_entries
+ * ids (topk ignored).  lse_f [B,heads,N] and
  * o_fine [B,heads,N,D] (fp32, cube-major) are written only if non-NULL
  * (both or neither).  order (optional, NULL = natural order): a permutation
  * of the B*heads*Nc query cubes (global ids (b*heads + h)*Nc + c, each
@@ -249,7 +258,8 @@ int vsa_pack_lists(const int32_t* counts, const int32_t* ids_padded, int n_rows,
 int vsa_fine_forward(const void* q, const void* kp, const void* vp,
                      const float* oc, const void* gate_c, const void* gate_f,
                      int B, int heads, int head_dim, int T, int H, int W,
-                     const int32_t* kv_offsets, const int32_t* kv_ids, int topk,
+                     const int32_t* kv_offsets, const int32_t* kv_ids,
+                     int64_t n_list_entries, int topk,
                      int dtype, void* out, float* lse_f, float* o_fine,
                      const int32_t* order, hipStream_t stream);
 
@@ -260,8 +270,30 @@ int vsa_fine_forward(const void* q, const void* kp, const void* vp,
  * lists, cubes whose lists are centred alike then run side by side and
  * share more tile reads through the L2.  The forward entry points use it
  * for bf16 inputs.  Nc <= 4096. */
-int vsa_fine_order(const int32_t* kv_offsets, const int32_t* kv_ids, int topk,
+int vsa_fine_order(const int32_t* kv_offsets, const int32_t* kv_ids,
+                   int64_t n_list_entries, int topk,
                    int B, int heads, int n_cubes, int32_t* order, hipStream_t stream);
+
+/* --------------------------------------------------- list preconditions
+ * vsa_validate_lists: checks caller-made key lists against what the fine
+ * stage assumes ([VSA2-abs]: each query attends its own variable-length
+ * set of key-value pairs, so the lists are caller input):
+ *   CSR (kv_offsets non-NULL, n_rows + 1 entries): kv_offsets[0] == 0,
+ *   non-decreasing, kv_offsets[n_rows] == n_list_entries;
+ *   fixed length (kv_offsets NULL): n_rows lists of topk ids,
+ *   n_list_entries == n_rows * topk;
+ *   every id in [0, n_cubes) and no id twice within one list.
+ * result (device, 2 int32, overwritten): result[0] = number of offset
+ * faults, result[1] = number of lists with a bad or repeated id; both 0
+ * means well formed.  Asynchronous like every call; read result after the
+ * stream has drained.  n_cubes <= 4096 (VSA_ERR_UNSUPPORTED beyond).
+ * VSA_VALIDATE=1 in the environment makes block_sparse_attn_varlen and
+ * both backward calls run this check themselves, synchronize the stream
+ * and return VSA_ERR_INVALID_ARG (queueing nothing more) for bad lists.
+ */
+int vsa_validate_lists(const int32_t* kv_offsets, const int32_t* kv_ids,
+                       int64_t n_list_entries, int topk, int n_rows, int n_cubes,
+                       int32_t* result, hipStream_t stream);
 
 #ifdef __cplusplus
 }

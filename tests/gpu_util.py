@@ -1,8 +1,11 @@
 """Helpers shared by the GPU parity tests: device upload of seeded inputs,
 the tolerance checks and the top-K comparison rule.  Nothing here computes
 attention; expected values come from the fp64 oracle."""
+import functools
 import math
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -115,3 +118,84 @@ def check_mass_row(ids_row, logits_row, mass, k_min, k_max):
             f"length {n} vs oracle {n_ref} with prefix mass {crossing:.6f}, mass {mass}")
     check_selection_row(ids_row, logits_row, n)
     return exact
+
+
+# ------------------------------------------------ whole-tensor comparisons
+def oracle_workers():
+    """Threads for per-head oracle runs: the host cores this process may use
+    (at most 16, the share of one GPU's host on the test boxes)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def per_head(fn, pairs):
+    """fn(b, h) for every (b, h) in pairs, in a thread pool with BLAS held to
+    one thread per worker (numpy releases the GIL in its kernels).  Results
+    in the order of pairs."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1), ThreadPoolExecutor(oracle_workers()) as ex:
+        return list(ex.map(lambda bh: fn(*bh), pairs))
+
+
+class Stats:
+    """Whole-tensor error statistics accumulated slice by slice: max abs
+    error, and the squared norms that give the relative RMS error
+    ||actual - expected|| / ||expected|| over the whole tensor."""
+
+    def __init__(self):
+        self.max_abs = 0.0
+        self.err2 = 0.0
+        self.ref2 = 0.0
+        self.count = 0
+
+    @staticmethod
+    def of(actual, expected):
+        st = Stats()
+        actual = np.asarray(actual, dtype=np.float64)
+        expected = np.asarray(expected, dtype=np.float64)
+        assert actual.shape == expected.shape, (actual.shape, expected.shape)
+        if not np.all(np.isfinite(actual)):
+            st.max_abs = math.inf
+        else:
+            d = actual - expected
+            st.max_abs = float(np.abs(d).max()) if d.size else 0.0
+            st.err2 = float(np.sum(d * d))
+        st.ref2 = float(np.sum(expected * expected))
+        st.count = actual.size
+        return st
+
+    def add(self, other):
+        self.max_abs = max(self.max_abs, other.max_abs)
+        self.err2 += other.err2
+        self.ref2 += other.ref2
+        self.count += other.count
+        return self
+
+    @property
+    def rel_rms(self):
+        return math.sqrt(self.err2 / self.ref2) if self.ref2 > 0 else math.sqrt(self.err2)
+
+    def check(self, dtype, what):
+        """The parity bar over the whole tensor (fp32: max abs; bf16 inputs:
+        max abs and relative RMS)."""
+        assert math.isfinite(self.max_abs), f"{what}: non-finite values"
+        if dtype == torch.float32:
+            assert self.max_abs <= F32_MAX_ABS, f"{what}: max abs {self.max_abs:.3e} > {F32_MAX_ABS}"
+        else:
+            assert self.max_abs <= BF16_MAX_ABS, f"{what}: max abs {self.max_abs:.3e} > {BF16_MAX_ABS}"
+            assert self.rel_rms <= BF16_REL_RMS, f"{what}: rel RMS {self.rel_rms:.3e} > {BF16_REL_RMS}"
+        return f"{what}: {self.count} values, max abs {self.max_abs:.3e}, rel RMS {self.rel_rms:.3e}"
+
+
+def sum_stats(items):
+    total = Stats()
+    for st in items:
+        total.add(st)
+    return total
+
+
+@functools.lru_cache(maxsize=2)
+def cached_inputs(name, with_varlen):
+    """Seeded inputs of a named workload, kept for the next test on the same
+    workload (drawing the largest ones takes most of a test's time)."""
+    from workloads import WORKLOADS, workload_inputs
+    return workload_inputs(WORKLOADS[name], with_varlen=with_varlen)

@@ -11,7 +11,6 @@ from trainable_block_sparse_cube_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "vsa.h")
-PROBE_HEADER = os.path.join(ROOT, "include", "vsa_probe.h")
 
 OK, INVALID, UNSUPPORTED, WORKSPACE = (_lib.VSA_OK, _lib.VSA_ERR_INVALID_ARG,
                                        _lib.VSA_ERR_UNSUPPORTED, _lib.VSA_ERR_WORKSPACE)
@@ -39,13 +38,12 @@ def test_header_declares_the_required_entry_points():
                  "vsa_backward_workspace_bytes", "vsa_saved_bytes", "vsa_status_string",
                  "vsa_cube_permute_pool", "vsa_coarse_topk", "vsa_fine_forward",
                  "vsa_forward_mass", "vsa_forward_mass_workspace_bytes", "vsa_coarse_select_mass",
-                 "vsa_pack_lists", "vsa_cube_max_pool", "vsa_fine_order"):
+                 "vsa_pack_lists", "vsa_cube_max_pool", "vsa_fine_order", "vsa_validate_lists"):
         assert need in names
 
 
 def test_library_exports_every_declared_symbol(lib):
-    names = declared_functions() + declared_functions(PROBE_HEADER)
-    assert "vsa_probe_tile_gather" in names
+    names = declared_functions()
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, f"{name} missing from the Python binding"
@@ -111,8 +109,11 @@ def test_varlen_and_backward_reject_bad_arguments(lib):
                           _lib.VSA_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
     assert st == INVALID  # no saved state
     st = lib.vsa_backward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 64, 8, 8, 8, 2,
-                          _lib.VSA_F32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
-    assert st == UNSUPPORTED  # fp32 backward is not built
+                          _lib.VSA_F32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None)
+    assert st == WORKSPACE  # fp32 is accepted: it gets as far as the workspace check
+    st = lib.vsa_backward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 64, 8, 8, 8, 2,
+                          7, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == UNSUPPORTED  # unknown dtype
     st = lib.vsa_backward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 64, 8, 8, 8, 2,
                           _lib.VSA_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None)
     assert st == WORKSPACE
@@ -126,16 +127,18 @@ def test_stage_calls_reject_bad_arguments(lib):
     assert lib.vsa_coarse_topk(FAKE, FAKE, FAKE, 1, 1, 64, 100000, 2, BF, FAKE, FAKE, FAKE,
                                None) == UNSUPPORTED
     assert lib.vsa_fine_forward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 8, 8, 8,
-                                None, FAKE, 2, _lib.VSA_BF16, FAKE, FAKE, None, None, None) == INVALID
-    assert lib.vsa_fine_order(None, FAKE, 0, 1, 1, 8, FAKE, None) == INVALID  # topk 0 without offsets
-    assert lib.vsa_fine_order(None, FAKE, 2, 1, 1, 8, None, None) == INVALID
-    assert lib.vsa_fine_order(FAKE, FAKE, 0, 1, 1, 5000, FAKE, None) == UNSUPPORTED
+                                None, FAKE, 0, 2, _lib.VSA_BF16, FAKE, FAKE, None, None, None) == INVALID
+    # CSR lists: a negative entry count, or more entries than every list full
+    assert lib.vsa_fine_forward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 8, 8, 8,
+                                FAKE, FAKE, -1, 0, _lib.VSA_BF16, FAKE, None, None, None, None) == INVALID
+    assert lib.vsa_fine_forward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 8, 8, 8,
+                                FAKE, FAKE, 65, 0, _lib.VSA_BF16, FAKE, None, None, None, None) == INVALID
+    assert lib.vsa_fine_order(None, FAKE, 0, 0, 1, 1, 8, FAKE, None) == INVALID  # topk 0 without offsets
+    assert lib.vsa_fine_order(None, FAKE, 0, 2, 1, 1, 8, None, None) == INVALID
+    assert lib.vsa_fine_order(FAKE, FAKE, 10, 0, 1, 1, 5000, FAKE, None) == UNSUPPORTED
+    assert lib.vsa_fine_order(FAKE, FAKE, 65, 0, 1, 1, 8, FAKE, None) == INVALID
     assert lib.vsa_cube_permute_pool(FAKE, FAKE, FAKE, 1, 1, 64, 8, 8, 5, _lib.VSA_BF16,
                                      FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
-    # measurement helper: bad depth, head_dim, topk
-    assert lib.vsa_probe_tile_gather(FAKE, FAKE, 1, 8, 128, FAKE, 2, 3, FAKE, None) == 1
-    assert lib.vsa_probe_tile_gather(FAKE, FAKE, 1, 8, 96, FAKE, 2, 1, FAKE, None) == 1
-    assert lib.vsa_probe_tile_gather(FAKE, FAKE, 1, 8, 128, FAKE, 9, 1, FAKE, None) == 1
 
 
 def test_mass_rule_calls_reject_bad_arguments(lib):
@@ -174,3 +177,16 @@ def test_mass_rule_calls_reject_bad_arguments(lib):
     assert lib.vsa_pack_lists(FAKE, FAKE, 1 << 20, 1 << 12, FAKE, FAKE, None) == UNSUPPORTED
     assert lib.vsa_cube_max_pool(FAKE, FAKE, FAKE, 1, 1, 64, 8, 8, 6, BF, FAKE, FAKE, FAKE, None) == INVALID
     assert lib.vsa_cube_max_pool(FAKE, FAKE, FAKE, 1, 1, 64, 8, 8, 8, BF, FAKE, None, FAKE, None) == INVALID
+
+
+def test_validate_lists_rejects_bad_arguments(lib):
+    v = lib.vsa_validate_lists
+    assert v(FAKE, FAKE, 10, 0, 4, 8, None, None) == INVALID      # no result buffer
+    assert v(FAKE, FAKE, 10, 0, -1, 8, FAKE, None) == INVALID     # negative row count
+    assert v(FAKE, FAKE, 10, 0, 4, 0, FAKE, None) == INVALID      # no cubes
+    assert v(FAKE, FAKE, -1, 0, 4, 8, FAKE, None) == INVALID      # negative entry count
+    assert v(FAKE, None, 10, 0, 4, 8, FAKE, None) == INVALID      # entries but no ids
+    assert v(FAKE, FAKE, 10, 0, 4, 5000, FAKE, None) == UNSUPPORTED
+    # fixed length: n_list_entries must be n_rows * topk
+    assert v(None, FAKE, 10, 3, 4, 8, FAKE, None) == INVALID
+    assert v(None, FAKE, 12, 0, 4, 8, FAKE, None) == INVALID

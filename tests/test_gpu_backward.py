@@ -1,13 +1,14 @@
 """GPU parity of the backward (C ABI via the thin binding) against the fp64
-oracle: full tensors at small sizes, sampled cubes at the training workload
-size, determinism, and the argument checks of the backward entry points."""
+oracle: full tensors at small sizes (bf16 and fp32) and at the training
+workload size, sampled cubes at the largest accepted cube count,
+determinism, and the argument checks of the backward entry points."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from oracle import vsa_oracle as vo
-from tests.gpu_util import assert_close, dev, host64, log
+from tests.gpu_util import Stats, assert_close, dev, host64, log, per_head, sum_stats
 from workloads import WORKLOADS, make_inputs, workload_inputs
 
 pytestmark = pytest.mark.gpu
@@ -20,9 +21,12 @@ def _vsa():
     return vsa
 
 
-def _run(inp, grid, K):
+F32 = torch.float32
+
+
+def _run(inp, grid, K, dtype=BF16):
     vsa = _vsa()
-    q, k, v, gc, gf, do = (dev(inp[n], BF16) for n in ("q", "k", "v", "gc", "gf", "dout"))
+    q, k, v, gc, gf, do = (dev(inp[n], dtype) for n in ("q", "k", "v", "gc", "gf", "dout"))
     out, sel, saved = vsa.vsa_forward(q, k, v, gc, gf, grid, K, save=True)
     grads = vsa.vsa_backward(q, k, v, gc, gf, do, sel, saved, grid)
     torch.cuda.synchronize()
@@ -92,38 +96,28 @@ def test_varlen_backward_small_including_empty_lists():
         assert_close(host64(g), ref[name], BF16, name)
 
 
-def test_backward_training_workload_sampled():
+def test_backward_training_workload_whole_tensor():
     """train16k: B=2, 12 heads, head_dim 128, 16x32x32 grid, top-K 32.
-    Gradients of sampled query and key cubes against the fp64 oracle."""
+    All five gradients over the whole tensors against oracle.backward under
+    the GPU's selection (one (batch, head) per worker thread)."""
     w = WORKLOADS["train16k"]
     log("backward train16k: drawing inputs")
     inp = workload_inputs(w)
     sel, grads = _run(inp, w.grid, 32)
     g = [t.float().cpu().numpy() for t in grads]
-    for t in g:
-        assert np.all(np.isfinite(t))
-    members = vo.cube_members(*w.grid)
-    rng = np.random.default_rng(4)
-    acts = {n: [] for n in GRADS}
-    refs = {n: [] for n in GRADS}
-    for _ in range(4):
-        b, h = int(rng.integers(w.B)), int(rng.integers(w.heads))
-        qcs = [int(x) for x in rng.choice(w.n_cubes, 3, replace=False)]
-        kcs = [int(x) for x in rng.choice(w.n_cubes, 3, replace=False)]
-        out = oracle.backward_sampled(inp["q"], inp["k"], inp["v"], inp["gc"], inp["gf"], inp["dout"],
-                                      w.grid, list(sel[b, h]), b, h, qcs, kcs)
-        for c in qcs:
-            rows = members[c]
-            acts["dq"].append(g[0][b, rows, h]); refs["dq"].append(out[("dq", c)])
-            acts["dgc"].append(g[3][b, rows, h]); refs["dgc"].append(out[("dgc", c)])
-            acts["dgf"].append(g[4][b, rows, h]); refs["dgf"].append(out[("dgf", c)])
-        for j in kcs:
-            rows = members[j]
-            acts["dk"].append(g[1][b, rows, h]); refs["dk"].append(out[("dk", j)])
-            acts["dv"].append(g[2][b, rows, h]); refs["dv"].append(out[("dv", j)])
-    for n in GRADS:
-        assert_close(np.stack(acts[n]), np.stack(refs[n]), BF16, f"train16k {n}")
-    log("  train16k sampled gradients ok")
+    del grads
+
+    def work(b, h):
+        sl = lambda n: inp[n][b:b + 1, :, h:h + 1]
+        ref = oracle.backward(sl("q"), sl("k"), sl("v"), sl("gc"), sl("gf"), sl("dout"), w.grid,
+                              [[list(sel[b, h])]])
+        return [Stats.of(g[0][b, :, h], ref["dq"][0, :, 0]), Stats.of(g[1][b, :, h], ref["dk"][0, :, 0]),
+                Stats.of(g[2][b, :, h], ref["dv"][0, :, 0]), Stats.of(g[3][b, :, h], ref["dgc"][0, :, 0]),
+                Stats.of(g[4][b, :, h], ref["dgf"][0, :, 0])]
+    log(f"backward train16k: oracle on {w.B * w.heads} heads")
+    res = per_head(work, [(b, h) for b in range(w.B) for h in range(w.heads)])
+    for i, name in enumerate(GRADS):
+        log("  " + sum_stats(r[i] for r in res).check(BF16, f"train16k {name}"))
 
 
 def test_backward_at_the_largest_cube_count():
@@ -161,13 +155,75 @@ def test_backward_at_the_largest_cube_count():
     log("  3584 cubes: sampled gradients ok")
 
 
-def test_backward_rejects_fp32_and_missing_state():
+F32_CASES = [
+    # B, heads, D, grid, topk
+    (1, 2, 128, (8, 8, 12), 4),
+    (2, 2, 64, (4, 8, 12), 3),
+    (1, 3, 64, (8, 12, 16), 24),  # K = Nc: dense fine stage
+    (2, 1, 128, (4, 4, 4), 1),    # a single cube
+]
+
+
+def test_backward_f32_tiny_workload():
+    """The tiny fp32 workload (B=1, 2 heads, head_dim 64, 8x8x8, top-K 2)
+    with dO ~ N(0, 1): all five gradients against the oracle at the fp32
+    bar (max abs 1e-4)."""
+    w = WORKLOADS["tiny_f32"]
+    inp = make_inputs(w.B, w.heads, w.head_dim, w.grid, dtype="f32", seed=w.seed, with_dout=True)
+    sel, grads = _run(inp, w.grid, w.topk[0], F32)
+    ref = oracle.backward(inp["q"], inp["k"], inp["v"], inp["gc"], inp["gf"], inp["dout"], w.grid,
+                          oracle.lists_from_sel(sel))
+    for name, g in zip(GRADS, grads):
+        assert g.dtype == F32
+        m, _ = assert_close(host64(g), ref[name], F32, name)
+        log(f"  tiny_f32 {name}: max abs {m:.2e}")
+
+
+@pytest.mark.parametrize("case", F32_CASES,
+                         ids=lambda c: f"B{c[0]}h{c[1]}D{c[2]}g{'x'.join(map(str, c[3]))}k{c[4]}")
+def test_backward_f32_small_full_compare(case):
+    B, nh, D, grid, K = case
+    log(f"fp32 backward small {case}")
+    inp = make_inputs(B, nh, D, grid, dtype="f32", seed=300 + K, with_dout=True)
+    sel, grads = _run(inp, grid, K, F32)
+    ref = oracle.backward(inp["q"], inp["k"], inp["v"], inp["gc"], inp["gf"], inp["dout"], grid,
+                          oracle.lists_from_sel(sel))
+    for name, g in zip(GRADS, grads):
+        assert_close(host64(g), ref[name], F32, name)
+
+
+def test_backward_f32_varlen_including_empty_lists():
     vsa = _vsa()
-    from trainable_block_sparse_cube_amd import _lib
+    B, nh, D, grid = 2, 2, 64, (8, 8, 12)
+    inp = make_inputs(B, nh, D, grid, dtype="f32", seed=33, with_dout=True, varlen=(0, 12))
+    assert (np.diff(inp["kv_offsets"]) == 0).any()
+    offs = torch.from_numpy(inp["kv_offsets"]).cuda()
+    ids = torch.from_numpy(inp["kv_ids"]).cuda()
+    q, k, v, gc, gf, do = (dev(inp[n], F32) for n in ("q", "k", "v", "gc", "gf", "dout"))
+    _, saved = vsa.block_sparse_attn_varlen(q, k, v, gc, gf, grid, offs, ids, save=True)
+    grads = vsa.block_sparse_attn_varlen_backward(q, k, v, gc, gf, do, offs, ids, saved, grid)
+    torch.cuda.synchronize()
+    lists = oracle.lists_from_csr(inp["kv_offsets"], inp["kv_ids"], B, nh, 12)
+    ref = oracle.backward(inp["q"], inp["k"], inp["v"], inp["gc"], inp["gf"], inp["dout"], grid, lists)
+    for name, g in zip(GRADS, grads):
+        assert_close(host64(g), ref[name], F32, name)
+
+
+def test_backward_f32_is_deterministic():
+    grid = (8, 8, 8)
+    inp = make_inputs(1, 2, 128, grid, dtype="f32", seed=6, with_dout=True)
+    _, g1 = _run(inp, grid, 3, F32)
+    _, g2 = _run(inp, grid, 3, F32)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_backward_rejects_missing_state():
+    vsa = _vsa()
     grid = (4, 4, 8)
     inp = make_inputs(1, 1, 64, grid, dtype="f32", seed=1, with_dout=True)
-    q, k, v, gc, gf, do = (dev(inp[n], torch.float32) for n in ("q", "k", "v", "gc", "gf", "dout"))
-    out, sel, saved = vsa.vsa_forward(q, k, v, gc, gf, grid, 1, save=True)
-    with pytest.raises(_lib.VSAError) as e:
+    q, k, v, gc, gf, do = (dev(inp[n], F32) for n in ("q", "k", "v", "gc", "gf", "dout"))
+    out, sel, saved = vsa.vsa_forward(q, k, v, gc, gf, grid, 1, save=False)
+    assert saved is None
+    with pytest.raises(ValueError):
         vsa.vsa_backward(q, k, v, gc, gf, do, sel, saved, grid)
-    assert e.value.status == _lib.VSA_ERR_UNSUPPORTED

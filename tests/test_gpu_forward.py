@@ -1,14 +1,17 @@
 """GPU parity of the forward path (C ABI via the thin binding) against the
-fp64 oracle.  Small shapes are compared element by element; the full
-workload shapes are compared on sampled query cubes the oracle computes one
-by one, plus properties that hold at any size."""
+fp64 oracle.  Small shapes and every full workload shape are compared
+element by element over the whole output (the full shapes run the oracle
+one (batch, head) at a time in a thread pool), with the top-K ids checked
+on every row; the largest accepted cube count is checked on sampled query
+cubes."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from oracle import vsa_oracle as vo
-from tests.gpu_util import assert_close, check_selection, check_selection_row, dev, host64, log
+from tests.gpu_util import (Stats, assert_close, cached_inputs, check_selection, check_selection_row,
+                            dev, host64, log, per_head, sum_stats)
 from workloads import WORKLOADS, make_inputs, workload_inputs
 
 pytestmark = pytest.mark.gpu
@@ -363,24 +366,6 @@ def test_mass_and_varlen_paths_are_deterministic():
         assert torch.equal(a, b)
 
 
-def test_probe_tile_gather_runs_on_every_depth():
-    """The measurement helper (no arithmetic) accepts the forward's tiles and
-    selection at every depth and leaves the tiles untouched."""
-    vsa = _vsa()
-    grid = (8, 16, 16)
-    inp = make_inputs(1, 2, 128, grid, dtype="bf16", seed=12)
-    q, k, v = (dev(inp[n], BF16) for n in "qkv")
-    _, kp, vp, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, grid, with_q_tiles=False)
-    _, _, sel = vsa.vsa_coarse_topk(qc, kc, vc, 5, input_dtype=BF16)
-    kp0, vp0 = kp.clone(), vp.clone()
-    for depth in (1, 2, 4, 8):
-        vsa.probe_tile_gather(kp, vp, sel, 5, depth)
-    torch.cuda.synchronize()
-    assert torch.equal(kp, kp0) and torch.equal(vp, vp0)
-    with pytest.raises(RuntimeError):
-        vsa.probe_tile_gather(kp, vp, sel, 5, 3)
-
-
 # --------------------------------------------------------------- full sizes
 def _sampled_check(w, inp, out, sel_np, K, n_samples, rng, lists=None):
     B, nh, D = w.B, w.heads, w.head_dim
@@ -423,39 +408,68 @@ def test_forward_at_the_largest_cube_count():
     log(f"  3584 cubes: sampled rows ok, near-tie exemptions {exempt}/8")
 
 
-@pytest.mark.parametrize("name,K", [("pretrain16k", 32), ("long61k", 16), ("long61k", 32),
-                                    ("large70k", 32), ("train16k", 32), ("long61k_smooth", 32)])
-def test_forward_full_size_sampled(name, K):
+def _whole_forward_check(w, inp, o_np, lists_of, sel_np=None, K=None):
+    """Per (b, h), in a thread pool: the oracle forward under the GPU's
+    lists (or the caller's), compared over the whole head; with sel_np, the
+    ids of every row are checked against the oracle's fp64 logits.
+    Returns (Stats over the whole output, near-tie exemptions)."""
+    def work(b, h):
+        sl = lambda n: inp[n][b:b + 1, :, h:h + 1]
+        r = oracle.forward_with_sets(sl("q"), sl("k"), sl("v"), sl("gc"), sl("gf"), w.grid,
+                                     [[lists_of(b, h)]])
+        exempt = check_selection(sel_np[b, h][None], r["S"][0], K) if sel_np is not None else 0
+        return Stats.of(o_np[b, :, h], r["o"][0, :, 0]), exempt
+    res = per_head(work, [(b, h) for b in range(w.B) for h in range(w.heads)])
+    return sum_stats(r[0] for r in res), sum(r[1] for r in res)
+
+
+# large70k last, so that the varlen test below reuses its drawn inputs
+@pytest.mark.parametrize("name,K", [("pretrain16k", 32), ("train16k", 32), ("long61k_smooth", 32),
+                                    ("long61k", 16), ("long61k", 32), ("large70k", 32)])
+def test_forward_full_size_whole_tensor(name, K):
+    """Every workload shape at full size: the output starts as NaN (so an
+    unwritten row cannot pass), then the whole tensor is compared with the
+    oracle under the GPU's own selection, and every row's ids with the
+    oracle's fp64 coarse logits (near-tie rule)."""
     vsa = _vsa()
     w = WORKLOADS[name]
     log(f"full-size forward {name} K={K}: drawing inputs")
-    inp = workload_inputs(w, with_varlen=False)
+    inp = cached_inputs(name, w.varlen is not None)
     q, k, v, gc, gf = (dev(inp[n], BF16) for n in ("q", "k", "v", "gc", "gf"))
+    out = torch.full_like(q, float("nan"))
     log(f"full-size forward {name} K={K}: running")
-    out, sel, _ = vsa.vsa_forward(q, k, v, gc, gf, w.grid, K)
+    _, sel, _ = vsa.vsa_forward(q, k, v, gc, gf, w.grid, K, out=out)
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(out.float()).all())
     sel_np = sel.cpu().numpy()
-    # properties at any size: K distinct ascending ids in range per row
+    o_np = out.float().cpu().numpy()
+    del q, k, v, gc, gf, out
     assert np.all(np.diff(sel_np, axis=-1) > 0) and sel_np.min() >= 0 and sel_np.max() < w.n_cubes
-    exempt = _sampled_check(w, inp, out, sel_np, K, 12, np.random.default_rng(K))
-    log(f"  {name} K={K}: sampled rows ok, near-tie exemptions {exempt}/12")
+    log(f"full-size forward {name} K={K}: oracle on {w.B * w.heads} heads")
+    st, exempt = _whole_forward_check(w, inp, o_np, lambda b, h: list(sel_np[b, h]), sel_np, K)
+    msg = st.check(BF16, f"{name} K={K} whole output")
+    log(f"  {msg}; near-tie rows {exempt}/{sel_np.shape[0] * sel_np.shape[1] * sel_np.shape[2]}")
 
 
-def test_varlen_full_size_sampled():
+def test_varlen_full_size_whole_tensor():
+    """large70k with per-query-cube lists of 8..64 random cubes: whole
+    output against the oracle under the same lists."""
     vsa = _vsa()
     w = WORKLOADS["large70k"]
     log("full-size varlen large70k: drawing inputs")
-    inp = workload_inputs(w)
+    inp = cached_inputs("large70k", True)
     offs, ids = inp["kv_offsets"], inp["kv_ids"]
     q, k, v, gc, gf = (dev(inp[n], BF16) for n in ("q", "k", "v", "gc", "gf"))
-    out, _ = vsa.block_sparse_attn_varlen(q, k, v, gc, gf, w.grid, torch.from_numpy(offs).cuda(),
-                                          torch.from_numpy(ids).cuda())
+    out = torch.full_like(q, float("nan"))
+    vsa.block_sparse_attn_varlen(q, k, v, gc, gf, w.grid, torch.from_numpy(offs).cuda(),
+                                 torch.from_numpy(ids).cuda(), out=out)
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(out.float()).all())
+    o_np = out.float().cpu().numpy()
+    del q, k, v, gc, gf, out
     nc = w.n_cubes
 
-    def lists(b, h, c):
-        r = (b * w.heads + h) * nc + c
-        return ids[offs[r]:offs[r + 1]]
-    _sampled_check(w, inp, out, None, None, 12, np.random.default_rng(5), lists=lists)
+    def lists_of(b, h):
+        r0 = (b * w.heads + h) * nc
+        return [ids[offs[r0 + c]:offs[r0 + c + 1]] for c in range(nc)]
+    log("full-size varlen large70k: oracle")
+    st, _ = _whole_forward_check(w, inp, o_np, lists_of)
+    log("  " + st.check(BF16, "large70k varlen whole output"))

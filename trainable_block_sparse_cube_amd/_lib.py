@@ -1,6 +1,5 @@
 """ctypes view of libvsa.so: one Python callable per C entry point of
-include/vsa.h (and the measurement helper of include/vsa_probe.h), with the
-same names and argument order.  Nothing here
+include/vsa.h, with the same names and argument order.  Nothing here
 computes; it only loads the library and declares the C signatures."""
 from __future__ import annotations
 
@@ -31,15 +30,14 @@ SIGNATURES = {
         _i, [_p] * 8 + [_i64, _p] + [_i] * 7 + [_p] * 5 + [_p, _sz, _p]),
     "vsa_cube_permute_pool": (_i, [_p] * 3 + [_i] * 7 + [_p] * 6 + [_p]),
     "vsa_coarse_topk": (_i, [_p] * 3 + [_i] * 6 + [_p] * 3 + [_p]),
-    "vsa_fine_forward": (_i, [_p] * 6 + [_i] * 6 + [_p, _p, _i, _i, _p, _p, _p, _p, _p]),
-    "vsa_fine_order": (_i, [_p, _p, _i, _i, _i, _i, _p, _p]),
+    "vsa_fine_forward": (_i, [_p] * 6 + [_i] * 6 + [_p, _p, _i64, _i, _i, _p, _p, _p, _p, _p]),
+    "vsa_fine_order": (_i, [_p, _p, _i64, _i, _i, _i, _i, _p, _p]),
+    "vsa_validate_lists": (_i, [_p, _p, _i64, _i, _i, _i, _p, _p]),
     "vsa_forward_mass_workspace_bytes": (_sz, [_i] * 8),
     "vsa_forward_mass": (_i, [_p] * 5 + [_i] * 6 + [_f, _i, _i, _i] + [_p] * 5 + [_sz, _p]),
     "vsa_coarse_select_mass": (_i, [_p] * 3 + [_i] * 4 + [_f, _i, _i, _i] + [_p] * 4 + [_p]),
     "vsa_pack_lists": (_i, [_p, _p, _i, _i, _p, _p, _p]),
     "vsa_cube_max_pool": (_i, [_p] * 3 + [_i] * 7 + [_p] * 3 + [_p]),
-    # include/vsa_probe.h
-    "vsa_probe_tile_gather": (_i, [_p, _p, _i, _i, _i, _p, _i, _i, _p, _p]),
 }
 
 _lib = None

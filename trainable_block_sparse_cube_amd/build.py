@@ -24,7 +24,6 @@ SOURCES = [
     "schedule.hip",
     "fine_fwd.hip",
     "backward.hip",
-    "probe_gather.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

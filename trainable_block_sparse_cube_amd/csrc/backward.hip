@@ -49,12 +49,37 @@ __device__ __forceinline__ int raster_tok(int c, int s, int Hg, int Wg) {
 }
 
 // ---------------------------------------------------------------- prep
-template <int D>
+// Eight consecutive elements of a bf16 or fp32 row as floats, and back.
+__device__ __forceinline__ void load8(const bf16* p, float (&x)[8]) {
+  const u32x4 raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  bf16 v[8];
+  __builtin_memcpy(v, &raw, 16);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+}
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + 1);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+}
+__device__ __forceinline__ void store8(bf16* p, const bf16 (&v)[8]) {
+  u32x4 packed;
+  __builtin_memcpy(&packed, v, 16);
+  *reinterpret_cast<u32x4*>(p) = packed;
+}
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  *(reinterpret_cast<f32x4*>(p) + 1) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
+// T: element type of dO, the gates and the dOf tile (bf16 or fp32).
+template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(
-    const bf16* __restrict__ dout, const bf16* __restrict__ gc, const bf16* __restrict__ gf,
+    const T* __restrict__ dout, const T* __restrict__ gc, const T* __restrict__ gf,
     const float* __restrict__ of, const float* __restrict__ oc, int nh, int Tg, int Hg, int Wg,
     float* __restrict__ dgc, float* __restrict__ dgf, float* __restrict__ delta,
-    bf16* __restrict__ dofp, float* __restrict__ doc, float* __restrict__ deltac) {
+    T* __restrict__ dofp, float* __restrict__ doc, float* __restrict__ deltac) {
   constexpr int EPC = 8;
   constexpr int CPR = D / EPC;
   constexpr int RPP = 256 / CPR;
@@ -87,14 +112,14 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
   // All passes' loads first, so that they are in flight together (the
   // compiler keeps each pass's loads behind the previous pass's stores).
   // dO and O_fine are read once in the backward: non-temporal loads.
-  u32x4 raws[PASSES];
+  float gvs[PASSES][EPC];
   f32x4 o0s[PASSES], o1s[PASSES];
   float gcv[PASSES], gfv[PASSES];
 #pragma unroll
   for (int ps = 0; ps < PASSES; ++ps) {
     const int s = tid / CPR + ps * RPP;
     const int64_t gidx = ((int64_t)b * N + raster_tok(c, s, Hg, Wg)) * nh + h;
-    raws[ps] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dout + gidx * D + ch * EPC));
+    load8(dout + gidx * D + ch * EPC, gvs[ps]);
     gcv[ps] = (float)gc[gidx];
     gfv[ps] = (float)gf[gidx];
     const f32x4* op = reinterpret_cast<const f32x4*>(of + ((int64_t)bh * N + (int64_t)c * 64 + s) * D + ch * EPC);
@@ -107,26 +132,23 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
     const int s = tid / CPR + ps * RPP;
     const int tok = raster_tok(c, s, Hg, Wg);
     const int64_t gidx = ((int64_t)b * N + tok) * nh + h;
-    const u32x4 raw = raws[ps];
-    bf16 gv[EPC];
-    __builtin_memcpy(gv, &raw, 16);
     const float gcs = gcv[ps], gfs = gfv[ps];
     const f32x4 o0 = o0s[ps], o1 = o1s[ps];
     // pc, pf: dO.Oc and dO.O_fine (the gate gradients, fp32).  pd is
-    // Delta = dOf.O_fine taken with dOf rounded to bf16 exactly as the fine
-    // kernels use it, so that sum_j P_ij dP_ij = Delta_i holds to fp32
-    // accuracy and dS sums to zero over each row.
+    // Delta = dOf.O_fine taken with dOf rounded to the element type exactly
+    // as the fine kernels use it, so that sum_j P_ij dP_ij = Delta_i holds
+    // to fp32 accuracy and dS sums to zero over each row.
     float pc = 0.f, pf = 0.f, pd = 0.f;
-    bf16 dv[EPC];
+    T dv[EPC];
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
-      const float g = (float)gv[e];
+      const float g = gvs[ps][e];
       const float ofe = e < 4 ? o0[e] : o1[e - 4];
       pc = fmaf(g, ocv[e], pc);
       pf = fmaf(g, ofe, pf);
       acc[e] = fmaf(gcs, g, acc[e]);
-      dv[e] = (bf16)(gfs * g);
-      pd = fmaf((float)dv[e], ofe, pd);
+      dv[e] = from_f32<T>(gfs * g);
+      pd = fmaf(to_f32(dv[e]), ofe, pd);
     }
 #pragma unroll
     for (int o = 1; o < CPR; o <<= 1) {
@@ -139,9 +161,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
       dgf[gidx] = pf;
       delta[(int64_t)bh * N + (int64_t)c * 64 + s] = pd;
     }
-    u32x4 packed;
-    __builtin_memcpy(&packed, dv, 16);
-    *reinterpret_cast<u32x4*>(dofp + tile + (int64_t)s * D + ch * EPC) = packed;
+    store8(dofp + tile + (int64_t)s * D + ch * EPC, dv);
   }
 #pragma unroll
   for (int o = CPR; o < 64; o <<= 1)
@@ -316,8 +336,8 @@ __device__ void block_exclusive_scan(const int32_t* in, int n, int32_t* out, int
 // over the query cubes stay in step, which helps L2 reuse).  The order
 // among equal lengths is arbitrary; results do not depend on it.
 __global__ __launch_bounds__(256) void transpose_scatter_kernel(
-    const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk, int nc,
-    int32_t* __restrict__ tr_offs, int32_t* __restrict__ tr_order, int32_t* __restrict__ tmp) {
+    const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk, int64_t n_ids,
+    int nc, int32_t* __restrict__ tr_offs, int32_t* __restrict__ tr_order, int32_t* __restrict__ tmp) {
   // LDS: cnt [nc] (counts, then cursors), start [nc + 1], hist [nc + 1],
   // hpos [nc + 2]
   extern __shared__ int32_t cnt[];
@@ -328,8 +348,11 @@ __global__ __launch_bounds__(256) void transpose_scatter_kernel(
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t r0 = (int64_t)bh * nc;
-  const int base = offs ? offs[r0] : (int)(r0 * topk);
-  const int total = (offs ? offs[r0 + nc] : (int)((r0 + nc) * topk)) - base;
+  // Entries of this (b, h): [base, base + total), clamped to the id array;
+  // every position written below stays inside it whatever the offsets hold.
+  const int64_t base = offs ? min(max((int64_t)offs[r0], (int64_t)0), n_ids) : r0 * topk;
+  const int total = (int)((offs ? min(max((int64_t)offs[r0 + nc], base), n_ids)
+                                : (r0 + nc) * topk) - base);
   for (int j = tid; j < nc; j += 256) cnt[j] = 0;
   for (int v = tid; v <= nc; v += 256) hist[v] = 0;
   __syncthreads();
@@ -362,29 +385,40 @@ __global__ __launch_bounds__(256) void transpose_scatter_kernel(
   for (int j = tid; j < nc; j += 256) cnt[j] = start[j];  // fill cursors
   __syncthreads();
   for (int c = tid; c < nc; c += 256) {
-    const int e0 = offs ? offs[r0 + c] : (int)((r0 + c) * topk);
-    const int e1 = offs ? offs[r0 + c + 1] : e0 + topk;
-    for (int e = e0; e < e1; e += kBatch) {
+    int64_t e0;
+    int len;
+    list_range(offs, r0 + c, topk, n_ids, &e0, &len);
+    const int64_t e1 = e0 + len;
+    for (int64_t e = e0; e < e1; e += kBatch) {
       int jj[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) jj[u] = e + u < e1 ? ids[e + u] : -1;
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)
-        if (jj[u] >= 0 && jj[u] < nc) tmp[base + atomicAdd(&cnt[jj[u]], 1)] = c;
+        if (cube_ok(jj[u], nc)) {
+          // rows of well-formed offsets tile [base, base + total) exactly;
+          // others may not, and what would not fit is dropped
+          const int pos = atomicAdd(&cnt[jj[u]], 1);
+          if (pos < total) tmp[base + pos] = c;
+        }
     }
   }
 }
 
-// transpose_rank: one wave per list r < n_lists, sorting it by rank (a
-// query cube occurs at most once per list, so ranks are distinct): every
-// lane counts the list's smaller entries through readlane broadcasts.
+// transpose_rank: one wave per list r < n_lists, sorting it by rank: every
+// lane counts the entries that precede its own, smaller values first and
+// equal values by position (a query cube that lists a key cube twice
+// appears twice), through readlane broadcasts.  Ranks are therefore
+// distinct and every slot of the list is written.
 __global__ __launch_bounds__(256) void transpose_rank_kernel(
     const int32_t* __restrict__ tr_offs, const int32_t* __restrict__ tmp, int64_t n_lists,
-    int32_t* __restrict__ tr_ids) {
+    int64_t n_ids, int32_t* __restrict__ tr_ids) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= n_lists) return;
-  const int s0 = tr_offs[r], n = tr_offs[r + 1] - s0;
+  int64_t s0;
+  int n;
+  list_range(tr_offs, r, 0, n_ids, &s0, &n);
   const int32_t* lst = tmp + s0;
   for (int c0 = 0; c0 < n; c0 += 64) {
     const int idx = c0 + lane;
@@ -393,7 +427,10 @@ __global__ __launch_bounds__(256) void transpose_rank_kernel(
     for (int k0 = 0; k0 < n; k0 += 64) {
       const int u = k0 + lane < n ? lst[k0 + lane] : INT_MAX;
       const int m = min(64, n - k0);
-      for (int i = 0; i < m; ++i) rank += __builtin_amdgcn_readlane(u, i) < v;
+      for (int i = 0; i < m; ++i) {
+        const int w = __builtin_amdgcn_readlane(u, i);
+        rank += w < v || (w == v && k0 + i < idx);
+      }
     }
     if (idx < n) tr_ids[s0 + rank] = v;
   }
@@ -415,8 +452,8 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(
     const bf16* __restrict__ qp, const bf16* __restrict__ kp, const bf16* __restrict__ vp,
     const bf16* __restrict__ dofp, const float* __restrict__ lse_f, const float* __restrict__ delta,
     const int32_t* __restrict__ tr_offs, const int32_t* __restrict__ tr_order,
-    const int32_t* __restrict__ tr_ids, const float* __restrict__ dkc, const float* __restrict__ dvc,
-    int nh, int nc, int Hg, int Wg, float scale, int n_logical,
+    const int32_t* __restrict__ tr_ids, int64_t n_ids, const float* __restrict__ dkc,
+    const float* __restrict__ dvc, int nh, int nc, int Hg, int Wg, float scale, int n_logical,
     bf16* __restrict__ dk, bf16* __restrict__ dv) {
   constexpr int KS = D / 16, MD = D / 32, TILE_CH = 64 * D / 8;
   // Tile parity buffers: separate arrays picked at run time, so that the
@@ -463,8 +500,11 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(
     for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
 
   const uint32_t tr_lo = tr_offset<D>(lane, 0), tr_hi = tr_offset<D>(lane, 1);
-  const int e0 = tr_offs[bh_tiles + j], n = tr_offs[bh_tiles + j + 1] - e0;
+  int64_t e0;
+  int n;
+  list_range(tr_offs, bh_tiles + j, 0, n_ids, &e0, &n);
   auto copy_tile = [&](int c, int buf) {
+    c = cube_or_0(c, nc);  // the library's own transposed lists always pass
     const int64_t t = (bh_tiles + c) * 64;
     dma_tile<D>(qp + t * D, buf ? q_lds1 : q_lds0, wave, lane);
     dma_tile<D>(dofp + t * D, buf ? o_lds1 : o_lds0, wave, lane);
@@ -582,7 +622,7 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(
     const bf16* __restrict__ qp, const bf16* __restrict__ kp, const bf16* __restrict__ vp,
     const bf16* __restrict__ dofp, const float* __restrict__ lse_f, const float* __restrict__ delta,
-    const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk,
+    const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk, int64_t n_ids,
     const float* __restrict__ dqc, const float* __restrict__ kc_mean,
     int nh, int nc, int Hg, int Wg, float scale, int n_logical, bf16* __restrict__ dq) {
   constexpr int KS = D / 16, MD = D / 32, TILE_CH = 64 * D / 8;
@@ -604,9 +644,9 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(
   const int64_t N = (int64_t)nc * 64;
   const int64_t bh_tiles = (int64_t)bh * nc;
   const float scale_log2 = scale * kLog2e;
-  int start, n;
-  if (offs) { start = offs[blk]; n = offs[blk + 1] - start; }
-  else { start = blk * topk; n = topk; }
+  int64_t start;
+  int n;
+  list_range(offs, blk, topk, n_ids, &start, &n);
   const int32_t* list = ids + start;
 
   const int slot = 32 * qh + ql;
@@ -628,7 +668,9 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(
     for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
   float ssum = 0.f;  // this lane's share of sum_j dS_j
 
+  // An entry outside [0, nc) reads cube 0 and is skipped.
   auto copy_tile = [&](int kc, int buf) {
+    kc = cube_or_0(kc, nc);
     dma_tile<D>(kp + (bh_tiles + kc) * 64 * D, buf ? k_lds1 : k_lds0, wave, lane);
     dma_tile<D>(vp + (bh_tiles + kc) * 64 * D, buf ? v_lds1 : v_lds0, wave, lane);
   };
@@ -640,9 +682,11 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(
 
   for (int it = 0; it < n; ++it) {
     const int buf = it & 1;
+    const bool tile_ok = cube_ok(list[it], nc);
     wait_vmcnt<0>();
     __syncthreads();
     if (it + 1 < n) copy_tile(list[it + 1], buf ^ 1);
+    if (!tile_ok) continue;
     const u32x4* kb = buf ? k_lds1 : k_lds0;
     const u32x4* vb = buf ? v_lds1 : v_lds0;
 
@@ -705,7 +749,7 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(
   __syncthreads();
   if (kh == 1) return;
   ssum += xs[ql];
-  const float* c0 = kc_mean + (bh_tiles + (n > 0 ? list[0] : 0)) * D;
+  const float* c0 = kc_mean + (bh_tiles + (n > 0 ? cube_or_0(list[0], nc) : 0)) * D;
 
   const int b = bh / nh, h = bh - b * nh;
   const int tok = raster_tok(c, slot, Hg, Wg);
@@ -729,6 +773,192 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(
     }
 }
 
+// ---------------------------------------------------------------- fp32
+// fp32 inputs: the same two fine kernels in plain fp32 VALU arithmetic (no
+// reduced precision anywhere), one workgroup of 256 threads per query cube
+// (dQ) or per key cube (dK, dV).  Tiles sit in LDS as fp32 rows; a row that
+// lanes read at different rows of the same column is padded by one float,
+// so those reads fall on distinct banks.  Work is split into 32-row halves
+// of the streamed tile so that everything fits in LDS at D = 128.  Each
+// pair's products are formed as in the oracle's formulas, in a fixed order,
+// so results are deterministic.
+
+// Copy `rows` rows of D floats from src (contiguous) into dst with row
+// pitch `pitch` floats, by the 256 threads of the workgroup.
+template <int D>
+__device__ __forceinline__ void copy_rows_f32(const float* __restrict__ src, float* dst, int rows, int pitch) {
+  constexpr int V = D / 4;  // float4 per row
+  for (int i = threadIdx.x; i < rows * V; i += 256) {
+    const int r = i / V, c4 = i - r * V;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(src + (int64_t)r * D + 4 * c4);
+    float* d = dst + r * pitch + 4 * c4;
+    d[0] = x[0]; d[1] = x[1]; d[2] = x[2]; d[3] = x[3];
+  }
+}
+
+// dQ of one query cube: for each selected key cube, two halves of 32 keys.
+//   phase A: thread (query i = t % 64, keys j = t / 64 + 4e, e < 8):
+//            s = q_i.k_j, dP = dOf_i.v_j, P = exp(s s - lse_i),
+//            dS = P (dP - Delta_i) into dsm[i][j]
+//   phase B: thread (query i, dims d = t / 64 + 4m): dq_i[d] += sum_j dS k_j[d]
+template <int D>
+__global__ __launch_bounds__(256) void fine_bwd_dq_f32_kernel(
+    const float* __restrict__ qp, const float* __restrict__ kp, const float* __restrict__ vp,
+    const float* __restrict__ dofp, const float* __restrict__ lse_f, const float* __restrict__ delta,
+    const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk, int64_t n_ids,
+    const float* __restrict__ dqc, int nh, int nc, int Hg, int Wg, float scale,
+    float* __restrict__ dq) {
+  constexpr int P1 = D + 1;
+  __shared__ float qs[64 * P1], os[64 * P1];
+  __shared__ float ks[32 * D], vs[32 * D];
+  __shared__ float dsm[64 * 33];
+  const int tid = threadIdx.x, i = tid & 63, w = tid >> 6;
+  const int blk = blockIdx.x;
+  const int bh = blk / nc, c = blk - bh * nc;
+  const int64_t N = (int64_t)nc * 64;
+  const int64_t bh_tiles = (int64_t)bh * nc;
+  int64_t start;
+  int n;
+  list_range(offs, blk, topk, n_ids, &start, &n);
+  copy_rows_f32<D>(qp + (bh_tiles + c) * 64 * D, qs, 64, P1);
+  copy_rows_f32<D>(dofp + (bh_tiles + c) * 64 * D, os, 64, P1);
+  const float lse = lse_f[(int64_t)bh * N + (int64_t)c * 64 + i];
+  const float del = delta[(int64_t)bh * N + (int64_t)c * 64 + i];
+  float acc[D / 4];
+#pragma unroll
+  for (int m = 0; m < D / 4; ++m) acc[m] = 0.f;
+  for (int it = 0; it < n; ++it) {
+    const int kc = ids[start + it];
+    if (!cube_ok(kc, nc)) continue;  // not a key cube: no contribution
+    for (int half = 0; half < 2; ++half) {
+      __syncthreads();  // previous phase B done with ks, dsm
+      const int64_t row0 = (bh_tiles + kc) * 64 + 32 * half;
+      copy_rows_f32<D>(kp + row0 * D, ks, 32, D);
+      copy_rows_f32<D>(vp + row0 * D, vs, 32, D);
+      __syncthreads();
+      float sv[8], dp[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { sv[e] = 0.f; dp[e] = 0.f; }
+#pragma unroll 8
+      for (int d = 0; d < D; ++d) {
+        const float qd = qs[i * P1 + d], od = os[i * P1 + d];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = w + 4 * e;
+          sv[e] = fmaf(qd, ks[j * D + d], sv[e]);
+          dp[e] = fmaf(od, vs[j * D + d], dp[e]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = expf(sv[e] * scale - lse);
+        dsm[i * 33 + w + 4 * e] = p * (dp[e] - del);
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int j = 0; j < 32; ++j) {
+        const float dsv = dsm[i * 33 + j];
+#pragma unroll
+        for (int m = 0; m < D / 4; ++m) acc[m] = fmaf(dsv, ks[j * D + w + 4 * m], acc[m]);
+      }
+    }
+  }
+  const int b = bh / nh, h = bh - b * nh;
+  const int64_t gidx = ((int64_t)b * N + raster_tok(c, i, Hg, Wg)) * nh + h;
+  const float* qcr = dqc + (bh_tiles + c) * D;
+#pragma unroll
+  for (int m = 0; m < D / 4; ++m) {
+    const int d = w + 4 * m;
+    dq[gidx * D + d] = fmaf(scale, acc[m], qcr[d] * (1.0f / kCubeTokens));
+  }
+}
+
+// dK, dV of one key cube: for each query cube that selected it (ascending),
+// two halves of 32 queries.
+//   phase A: thread (key j = t % 64, queries i = t / 64 + 4e, e < 8):
+//            P = exp(s q_i.k_j - lse_i), dS = P (dOf_i.v_j - Delta_i)
+//   phase B: thread (key j, dims d = t / 64 + 4m):
+//            dk_j[d] += sum_i dS q_i[d],  dv_j[d] += sum_i P dOf_i[d]
+template <int D>
+__global__ __launch_bounds__(256) void fine_bwd_dkdv_f32_kernel(
+    const float* __restrict__ qp, const float* __restrict__ kp, const float* __restrict__ vp,
+    const float* __restrict__ dofp, const float* __restrict__ lse_f, const float* __restrict__ delta,
+    const int32_t* __restrict__ tr_offs, const int32_t* __restrict__ tr_ids, int64_t n_ids,
+    const float* __restrict__ dkc, const float* __restrict__ dvc, int nh, int nc, int Hg, int Wg,
+    float scale, float* __restrict__ dk, float* __restrict__ dv) {
+  constexpr int P1 = D + 1;
+  __shared__ float ks[64 * P1], vs[64 * P1];
+  __shared__ float qs[32 * D], os[32 * D];
+  __shared__ float pm[32 * 64], dsm[32 * 64];
+  __shared__ float ls[32], ds_[32];
+  const int tid = threadIdx.x, j = tid & 63, w = tid >> 6;
+  const int blk = blockIdx.x;
+  const int bh = blk / nc, kc = blk - bh * nc;
+  const int64_t N = (int64_t)nc * 64;
+  const int64_t bh_tiles = (int64_t)bh * nc;
+  int64_t e0;
+  int n;
+  list_range(tr_offs, blk, 0, n_ids, &e0, &n);
+  copy_rows_f32<D>(kp + (bh_tiles + kc) * 64 * D, ks, 64, P1);
+  copy_rows_f32<D>(vp + (bh_tiles + kc) * 64 * D, vs, 64, P1);
+  float ak[D / 4], av[D / 4];
+#pragma unroll
+  for (int m = 0; m < D / 4; ++m) { ak[m] = 0.f; av[m] = 0.f; }
+  for (int it = 0; it < n; ++it) {
+    const int c = cube_or_0(tr_ids[e0 + it], nc);  // the library's transposed lists always pass
+    for (int half = 0; half < 2; ++half) {
+      __syncthreads();  // previous phase B done with qs, os, pm, dsm
+      const int64_t row0 = (bh_tiles + c) * 64 + 32 * half;
+      copy_rows_f32<D>(qp + row0 * D, qs, 32, D);
+      copy_rows_f32<D>(dofp + row0 * D, os, 32, D);
+      if (tid < 32) ls[tid] = lse_f[(int64_t)bh * N + row0 - bh_tiles * 64 + tid];
+      else if (tid < 64) ds_[tid - 32] = delta[(int64_t)bh * N + row0 - bh_tiles * 64 + tid - 32];
+      __syncthreads();
+      float sv[8], dp[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { sv[e] = 0.f; dp[e] = 0.f; }
+#pragma unroll 8
+      for (int d = 0; d < D; ++d) {
+        const float kd = ks[j * P1 + d], vd = vs[j * P1 + d];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = w + 4 * e;
+          sv[e] = fmaf(qs[i * D + d], kd, sv[e]);
+          dp[e] = fmaf(os[i * D + d], vd, dp[e]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = w + 4 * e;
+        const float p = expf(sv[e] * scale - ls[i]);
+        pm[i * 64 + j] = p;
+        dsm[i * 64 + j] = p * (dp[e] - ds_[i]);
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int i = 0; i < 32; ++i) {
+        const float pv = pm[i * 64 + j], dsv = dsm[i * 64 + j];
+#pragma unroll
+        for (int m = 0; m < D / 4; ++m) {
+          const int d = w + 4 * m;
+          ak[m] = fmaf(dsv, qs[i * D + d], ak[m]);
+          av[m] = fmaf(pv, os[i * D + d], av[m]);
+        }
+      }
+    }
+  }
+  const int b = bh / nh, h = bh - b * nh;
+  const int64_t gidx = ((int64_t)b * N + raster_tok(kc, j, Hg, Wg)) * nh + h;
+  const float* kcr = dkc + (bh_tiles + kc) * D;
+  const float* vcr = dvc + (bh_tiles + kc) * D;
+#pragma unroll
+  for (int m = 0; m < D / 4; ++m) {
+    const int d = w + 4 * m;
+    dk[gidx * D + d] = fmaf(scale, ak[m], kcr[d] * (1.0f / kCubeTokens));
+    dv[gidx * D + d] = av[m] + vcr[d] * (1.0f / kCubeTokens);
+  }
+}
+
 template <bool TA, bool TB>
 hipError_t gemm(const float* A, int lda, int64_t sA, const float* B, int ldb, int64_t sB,
                 float* C, int ldc, int64_t sC, int M, int N, int K, float alpha, int batch,
@@ -745,9 +975,15 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t st) {
   const float scale = 1.0f / sqrtf((float)D);
   hipError_t e;
 #define VSA_TRY(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
-  bwd_prep_kernel<D><<<(unsigned)(a.B * nc * a.heads), 256, 0, st>>>(
-      (const bf16*)a.dout, (const bf16*)a.gc, (const bf16*)a.gf, a.of, a.oc, a.heads, a.T, a.H, a.W,
-      (float*)a.dgc, (float*)a.dgf, a.delta, (bf16*)a.dofp, a.doc, a.deltac);
+  if (a.bf16) {
+    bwd_prep_kernel<D, bf16><<<(unsigned)(a.B * nc * a.heads), 256, 0, st>>>(
+        (const bf16*)a.dout, (const bf16*)a.gc, (const bf16*)a.gf, a.of, a.oc, a.heads, a.T, a.H,
+        a.W, (float*)a.dgc, (float*)a.dgf, a.delta, (bf16*)a.dofp, a.doc, a.deltac);
+  } else {
+    bwd_prep_kernel<D, float><<<(unsigned)(a.B * nc * a.heads), 256, 0, st>>>(
+        (const float*)a.dout, (const float*)a.gc, (const float*)a.gf, a.of, a.oc, a.heads, a.T,
+        a.H, a.W, (float*)a.dgc, (float*)a.dgf, a.delta, (float*)a.dofp, a.doc, a.deltac);
+  }
   VSA_TRY(hipGetLastError());
   // coarse backward on the cube means
   const int64_t sq = (int64_t)nc * D, ss = (int64_t)nc * nc;
@@ -761,20 +997,35 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t st) {
   VSA_TRY((gemm<true, false>(a.S, nc, ss, a.doc, D, sq, a.dvc, D, sq, nc, D, nc, 1.0f, BH, st)));
   // transposed selection
   transpose_scatter_kernel<<<(unsigned)BH, 256, sizeof(int32_t) * (4 * nc + 4), st>>>(
-      a.offs, a.ids, a.topk, nc, a.tr_offs, a.tr_order, a.tr_tmp);
+      a.offs, a.ids, a.topk, a.n_ids, nc, a.tr_offs, a.tr_order, a.tr_tmp);
   VSA_TRY(hipGetLastError());
   const int64_t n_lists = (int64_t)BH * nc;
-  transpose_rank_kernel<<<(unsigned)((n_lists + 3) / 4), 256, 0, st>>>(a.tr_offs, a.tr_tmp, n_lists, a.tr_ids);
+  transpose_rank_kernel<<<(unsigned)((n_lists + 3) / 4), 256, 0, st>>>(a.tr_offs, a.tr_tmp, n_lists,
+                                                                       a.n_ids, a.tr_ids);
   VSA_TRY(hipGetLastError());
   const unsigned grid = (unsigned)(BH * nc);
+  if (!a.bf16) {
+    // the transposed lists are in natural key-cube order: tr_offs row = blk
+    fine_bwd_dkdv_f32_kernel<D><<<grid, 256, 0, st>>>(
+        (const float*)a.qp, (const float*)a.kp, (const float*)a.vp, (const float*)a.dofp,
+        a.lse_f, a.delta, a.tr_offs, a.tr_ids, a.n_ids, a.dkc, a.dvc, a.heads, nc, a.H, a.W, scale,
+        (float*)a.dk, (float*)a.dv);
+    VSA_TRY(hipGetLastError());
+    fine_bwd_dq_f32_kernel<D><<<grid, 256, 0, st>>>(
+        (const float*)a.qp, (const float*)a.kp, (const float*)a.vp, (const float*)a.dofp,
+        a.lse_f, a.delta, a.offs, a.ids, a.topk, a.n_ids, a.dqc, a.heads, nc, a.H, a.W, scale,
+        (float*)a.dq);
+    VSA_TRY(hipGetLastError());
+    return hipSuccess;
+  }
   fine_bwd_dkdv_kernel<D><<<((grid + 7u) / 8u) * 8u, 256, 0, st>>>(
       (const bf16*)a.qp, (const bf16*)a.kp, (const bf16*)a.vp, (const bf16*)a.dofp,
-      a.lse_f, a.delta, a.tr_offs, a.tr_order, a.tr_ids, a.dkc, a.dvc, a.heads, nc, a.H, a.W,
+      a.lse_f, a.delta, a.tr_offs, a.tr_order, a.tr_ids, a.n_ids, a.dkc, a.dvc, a.heads, nc, a.H, a.W,
       scale, (int)grid, (bf16*)a.dk, (bf16*)a.dv);
   VSA_TRY(hipGetLastError());
   fine_bwd_dq_kernel<D><<<((grid + 7u) / 8u) * 8u, 256, 0, st>>>(
       (const bf16*)a.qp, (const bf16*)a.kp, (const bf16*)a.vp, (const bf16*)a.dofp,
-      a.lse_f, a.delta, a.offs, a.ids, a.topk, a.dqc, a.kc, a.heads, nc, a.H, a.W, scale,
+      a.lse_f, a.delta, a.offs, a.ids, a.topk, a.n_ids, a.dqc, a.kc, a.heads, nc, a.H, a.W, scale,
       (int)grid, (bf16*)a.dq);
   VSA_TRY(hipGetLastError());
 #undef VSA_TRY

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kp, const bf16* __restrict__ vp,
     const float* __restrict__ oc, const bf16* __restrict__ gc, const bf16* __restrict__ gf,
     int nh, int nc, int Hg, int Wg,
-    const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk,
+    const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk, int64_t n_ids,
     float scale_log2, int n_logical, const int32_t* __restrict__ order,
     bf16* __restrict__ out, float* __restrict__ lse_f, float* __restrict__ o_fine) {
   constexpr int KS = D / 16;          // k-steps of S^T over head_dim
@@ -89,9 +89,9 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
   const int bh = blk / nc;
   const int c = blk - bh * nc;
   const int64_t N = (int64_t)nc * 64;
-  int start, n;
-  if (offs) { start = offs[blk]; n = offs[blk + 1] - start; }
-  else { start = blk * topk; n = topk; }
+  int64_t start;
+  int n;
+  list_range(offs, blk, topk, n_ids, &start, &n);
   const int32_t* list = ids + start;
   const int64_t bh_tiles = (int64_t)bh * nc;
   const int b = bh / nh, h = bh - b * nh;
@@ -99,8 +99,9 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
   // Copy the K and V tiles of key cube kc into buffer `buf`.  Both come
   // from contiguous cube-major tiles (each is re-read by about K query
   // cubes, and one contiguous 16 KB block streams better than 64 scattered
-  // token rows).
+  // token rows).  An entry outside [0, nc) reads cube 0 and is skipped.
   auto copy_tile = [&](int kc, int buf) {
+    kc = cube_or_0(kc, nc);
     dma_tile<D>(kp + (bh_tiles + kc) * 64 * D, buf ? k_lds1 : k_lds0, wave, lane);
     dma_tile<D>(vp + (bh_tiles + kc) * 64 * D, buf ? v_lds1 : v_lds0, wave, lane);
   };
@@ -126,6 +127,7 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
 
   for (int it = 0; it < n; ++it) {
     const int buf = it & 1;
+    const bool tile_ok = cube_ok(list[it], nc);
     wait_vmcnt<0>();   // this wave's copies of tile `it` have landed
     __syncthreads();   // all copies of tile `it` visible; buffer buf^1 free
     const u32x4* kb = buf ? k_lds1 : k_lds0;
@@ -150,6 +152,7 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
     // of this tile's arithmetic.
     if (it + 1 < n) copy_tile(list[it + 1], buf ^ 1);
     __builtin_amdgcn_sched_barrier(0);
+    if (!tile_ok) continue;
 
     // S^T (32 keys x 32 queries) = K[32kh..] * Q[32qh..]^T
     f32x16 sacc;
@@ -250,8 +253,8 @@ __global__ __launch_bounds__(64) void fine_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kp, const float* __restrict__ vp,
     const float* __restrict__ oc, const float* __restrict__ gc, const float* __restrict__ gf,
     int nh, int nc, int Hg, int Wg,
-    const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk, float scale,
-    float* __restrict__ out, float* __restrict__ lse_f, float* __restrict__ o_fine) {
+    const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk, int64_t n_ids,
+    float scale, float* __restrict__ out, float* __restrict__ lse_f, float* __restrict__ o_fine) {
   __shared__ float k_lds[64 * D];
   __shared__ float v_lds[D * 64];
   __shared__ float s_lds[64][65];  // this tile's scaled logits, [key][query slot]
@@ -260,9 +263,9 @@ __global__ __launch_bounds__(64) void fine_fwd_f32_kernel(
   const int bh = blk / nc;
   const int c = blk - bh * nc;
   const int64_t N = (int64_t)nc * 64;
-  int start, n;
-  if (offs) { start = offs[blk]; n = offs[blk + 1] - start; }
-  else { start = blk * topk; n = topk; }
+  int64_t start;
+  int n;
+  list_range(offs, blk, topk, n_ids, &start, &n);
 
   float qv[D], acc[D];
   const int b = bh / nh, h = bh - b * nh;
@@ -273,6 +276,7 @@ __global__ __launch_bounds__(64) void fine_fwd_f32_kernel(
   float m_run = -INFINITY, l_run = 0.f;
   for (int it = 0; it < n; ++it) {
     const int kc = ids[start + it];
+    if (!cube_ok(kc, nc)) continue;  // not a key cube: no contribution
     const float* ks = kp + ((int64_t)bh * nc + kc) * 64 * D;
     const float* vs = vp + ((int64_t)bh * nc + kc) * 64 * D;
     __syncthreads();
@@ -322,12 +326,12 @@ hipError_t launch_fine_d(const FineArgs& a, hipStream_t st) {
     fine_fwd_bf16_kernel<D><<<((grid + 7u) / 8u) * 8u, 256, 0, st>>>(
         (const bf16*)a.q, (const bf16*)a.kp, (const bf16*)a.vp, a.oc,
         (const bf16*)a.gc, (const bf16*)a.gf, a.heads, nc, a.H, a.W, a.offs, a.ids, a.topk,
-        scale * kLog2e, (int)grid, a.order, (bf16*)a.out, a.lse_f, a.o_fine);
+        a.n_ids, scale * kLog2e, (int)grid, a.order, (bf16*)a.out, a.lse_f, a.o_fine);
   } else {
     fine_fwd_f32_kernel<D><<<grid, 64, 0, st>>>(
         (const float*)a.q, (const float*)a.kp, (const float*)a.vp, a.oc,
         (const float*)a.gc, (const float*)a.gf, a.heads, nc, a.H, a.W, a.offs, a.ids, a.topk,
-        scale, (float*)a.out, a.lse_f, a.o_fine);
+        a.n_ids, scale, (float*)a.out, a.lse_f, a.o_fine);
   }
   return hipGetLastError();
 }

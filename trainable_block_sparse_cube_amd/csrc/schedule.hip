@@ -21,8 +21,8 @@ constexpr int kOrderThreads = 1024;
 constexpr int kOrderMax = 4096;  // cubes per (b, h) this sort holds (>= the coarse stage's limit)
 
 __global__ __launch_bounds__(kOrderThreads) void order_by_middle_kernel(
-    const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk, int nc, int P,
-    int32_t* __restrict__ order) {
+    const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk, int64_t n_ids,
+    int nc, int P, int32_t* __restrict__ order) {
   __shared__ uint32_t key[kOrderMax];
   const int64_t base = (int64_t)blockIdx.x * nc;
   const int tid = threadIdx.x;
@@ -31,9 +31,8 @@ __global__ __launch_bounds__(kOrderThreads) void order_by_middle_kernel(
     if (i < nc) {
       int64_t start;
       int n;
-      if (offs) { start = offs[base + i]; n = offs[base + i + 1] - (int)start; }
-      else { start = (base + i) * topk; n = topk; }
-      const uint32_t mid = n > 0 ? (uint32_t)ids[start + n / 2] : 0u;
+      list_range(offs, base + i, topk, n_ids, &start, &n);
+      const uint32_t mid = n > 0 ? (uint32_t)cube_or_0(ids[start + n / 2], nc) : 0u;
       kv = (mid << 12) | (uint32_t)i;
     }
     key[i] = kv;
@@ -60,11 +59,12 @@ __global__ __launch_bounds__(kOrderThreads) void order_by_middle_kernel(
 
 int order_max_cubes() { return kOrderMax; }
 
-hipError_t launch_fine_order(const int32_t* offs, const int32_t* ids, int topk, int n_bh, int nc,
-                             int32_t* order, hipStream_t st) {
+hipError_t launch_fine_order(const int32_t* offs, const int32_t* ids, int topk, int64_t n_ids,
+                             int n_bh, int nc, int32_t* order, hipStream_t st) {
   int P = 1;
   while (P < nc) P <<= 1;
-  order_by_middle_kernel<<<(unsigned)n_bh, kOrderThreads, 0, st>>>(offs, ids, topk, nc, P, order);
+  order_by_middle_kernel<<<(unsigned)n_bh, kOrderThreads, 0, st>>>(offs, ids, topk, n_ids, nc, P,
+                                                                    order);
   return hipGetLastError();
 }
 

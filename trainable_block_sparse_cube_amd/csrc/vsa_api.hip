@@ -6,6 +6,8 @@
 
 #include <climits>
 #include <cmath>
+#include <cstdlib>
+#include <cstring>
 
 using namespace vsa;
 
@@ -37,6 +39,7 @@ int check_shape(int B, int heads, int D, int T, int H, int W, int dtype, Shape* 
 }
 
 struct FwdWorkspace {
+  int32_t* check;  // 2 ints: list validation counts (VSA_VALIDATE)
   void *kp, *vp;
   float *qc, *kc, *vc, *oc, *lse_c;
   int32_t* order;  // processing order of the fine stage's query cubes
@@ -51,6 +54,7 @@ size_t fwd_ws_layout(const Shape& s, char* base, FwdWorkspace* w) {
   size_t off = 0;
   auto take = [&](size_t bytes) { char* p = base ? base + off : nullptr; off += bytes; return (void*)p; };
   FwdWorkspace t;
+  t.check = (int32_t*)take(kAlign);
   t.kp = take(tile_bytes); t.vp = take(tile_bytes);
   t.qc = (float*)take(pooled); t.kc = (float*)take(pooled_kv); t.vc = (float*)take(pooled_kv);
   t.oc = (float*)take(pooled); t.lse_c = (float*)take(lse);
@@ -77,6 +81,30 @@ size_t saved_layout(const Shape& s, char* base, Saved* sv) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_HIP; }
 
+// VSA_VALIDATE=1 in the environment (read at every call): entry points
+// that take caller-made key lists check them on the GPU first, wait for the
+// answer and return VSA_ERR_INVALID_ARG, queueing nothing more, if any
+// precondition fails.  Off by default: the check reads the lists once and
+// synchronizes the stream.
+bool validate_mode() {
+  const char* e = std::getenv("VSA_VALIDATE");
+  return e && *e && std::strcmp(e, "0") != 0;
+}
+
+// Runs the list check into `slot` (2 ints of device scratch) and waits for
+// it.  VSA_OK when the lists are well formed.
+int validate_now(const int32_t* offs, const int32_t* ids, int topk, int64_t n_ids, int64_t n_rows,
+                 int nc, int32_t* slot, hipStream_t st) {
+  if (nc > validate_max_cubes() || n_rows > INT_MAX) return VSA_ERR_UNSUPPORTED;
+  if (launch_validate_lists(offs, ids, topk, n_ids, (int)n_rows, nc, slot, st) != hipSuccess)
+    return VSA_ERR_HIP;
+  int32_t counts[2] = {0, 0};
+  if (hipMemcpyAsync(counts, slot, sizeof(counts), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return VSA_ERR_HIP;
+  return counts[0] == 0 && counts[1] == 0 ? VSA_OK : VSA_ERR_INVALID_ARG;
+}
+
 // Mass-rule selection inside a forward: the coarse stage writes per-row
 // lengths and padded lists into the workspace, then they are packed into
 // the caller's CSR buffers, which the fine stage reads.
@@ -95,13 +123,18 @@ size_t mass_ws_bytes(const Shape& s, int k_max) {
 
 // Shared body of vsa_forward, block_sparse_attn_varlen and vsa_forward_mass.
 int forward_impl(const void* q, const void* k, const void* v, const void* gc, const void* gf,
-                 const Shape& s, int topk, const int32_t* offs, const int32_t* ids,
+                 const Shape& s, int topk, const int32_t* offs, const int32_t* ids, int64_t n_ids,
                  int32_t* sel, void* out, void* saved, void* ws, size_t ws_bytes,
                  hipStream_t st, const MassRule* mr = nullptr) {
   FwdWorkspace w;
   const size_t fwd_bytes = fwd_ws_layout(s, nullptr, nullptr);
   if (ws_bytes < fwd_bytes + (mr ? mass_ws_bytes(s, mr->k_max) : 0)) return VSA_ERR_WORKSPACE;
   fwd_ws_layout(s, (char*)ws, &w);
+  if (offs && validate_mode()) {  // caller-made lists
+    const int vs = validate_now(offs, ids, 0, n_ids, (int64_t)s.B * s.heads * s.nc, (int)s.nc,
+                                w.check, st);
+    if (vs != VSA_OK) return vs;
+  }
   float *oc = w.oc, *lse_c = w.lse_c, *lse_f = nullptr, *of = nullptr;
   if (saved) {
     Saved sv;
@@ -135,11 +168,13 @@ int forward_impl(const void* q, const void* k, const void* v, const void* gc, co
     if (e != hipSuccess) return VSA_ERR_HIP;
     offs = mr->offsets;
     ids = mr->ids;
+    n_ids = (int64_t)rows * mr->k_max;  // capacity; the packed lists end at offsets[rows]
   }
+  if (!offs) n_ids = (int64_t)rows * topk;
   FineArgs fa{q, w.kp, w.vp, oc, gc, gf, s.B, s.heads, s.D, s.T, s.H, s.W,
-              offs, offs ? ids : sel, topk, bf, out, lse_f, of};
+              offs, offs ? ids : sel, topk, n_ids, bf, out, lse_f, of};
   if (bf) {  // the MFMA kernel runs the query cubes sorted by their lists' middle entries
-    e = launch_fine_order(fa.offs, fa.ids, topk, s.B * s.heads, (int)s.nc, w.order, st);
+    e = launch_fine_order(fa.offs, fa.ids, topk, n_ids, s.B * s.heads, (int)s.nc, w.order, st);
     if (e != hipSuccess) return VSA_ERR_HIP;
     fa.order = w.order;
   }
@@ -147,6 +182,7 @@ int forward_impl(const void* q, const void* k, const void* v, const void* gc, co
 }
 
 struct BwdWorkspace {
+  int32_t* check;  // 2 ints: list validation counts (VSA_VALIDATE)
   void *qp, *kp, *vp, *dofp;
   float *qc, *kc, *vc, *delta, *doc, *deltac, *S, *dP, *dqc, *dkc, *dvc;
   int32_t *tr_offs, *tr_order, *tr_ids, *tr_tmp;
@@ -161,6 +197,7 @@ size_t bwd_ws_layout(const Shape& s, int64_t n_entries, char* base, BwdWorkspace
   size_t off = 0;
   auto take = [&](size_t bytes) { char* p = base ? base + off : nullptr; off += bytes; return (void*)p; };
   BwdWorkspace t;
+  t.check = (int32_t*)take(kAlign);
   t.qp = take(tile); t.kp = take(tile); t.vp = take(tile); t.dofp = take(tile);
   t.qc = (float*)take(pooled); t.kc = (float*)take(pooled); t.vc = (float*)take(pooled);
   t.delta = (float*)take(per_tok);
@@ -182,22 +219,28 @@ int backward_impl(const void* q, const void* k, const void* v, const void* gc, c
                   void* ws, size_t ws_bytes, hipStream_t st) {
   if (!q || !k || !v || !gc || !gf || !dout || !saved || !ws) return VSA_ERR_INVALID_ARG;
   if (!dq || !dk || !dv || !dgc || !dgf) return VSA_ERR_INVALID_ARG;
-  if (s.dtype != VSA_BF16) return VSA_ERR_UNSUPPORTED;  // bf16 MFMA backward only
   if (ws_bytes < bwd_ws_layout(s, n_entries, nullptr, nullptr)) return VSA_ERR_WORKSPACE;
   BwdWorkspace w;
   bwd_ws_layout(s, n_entries, (char*)ws, &w);
+  if (validate_mode()) {  // the lists always come from the caller here
+    const int vs = validate_now(offs, ids, topk, n_entries, (int64_t)s.B * s.heads * s.nc,
+                                (int)s.nc, w.check, st);
+    if (vs != VSA_OK) return vs;
+  }
   Saved sv;
   saved_layout(s, (char*)const_cast<void*>(saved), &sv);
+  const bool bf = s.dtype == VSA_BF16;
   PermutePoolArgs pa{{{q, k, v}, {w.qp, w.kp, w.vp}, {w.qc, w.kc, w.vc}},
-                     s.B, s.heads, s.D, s.T, s.H, s.W, true};
+                     s.B, s.heads, s.D, s.T, s.H, s.W, bf};
   if (launch_permute_pool(pa, st) != hipSuccess) return VSA_ERR_HIP;
   BackwardArgs ba;
   ba.B = s.B; ba.heads = s.heads; ba.D = s.D; ba.T = s.T; ba.H = s.H; ba.W = s.W;
+  ba.bf16 = bf;
   ba.dout = dout; ba.gc = gc; ba.gf = gf;
   ba.qp = w.qp; ba.kp = w.kp; ba.vp = w.vp;
   ba.qc = w.qc; ba.kc = w.kc; ba.vc = w.vc;
   ba.oc = sv.oc; ba.lse_c = sv.lse_c; ba.lse_f = sv.lse_f; ba.of = sv.of;
-  ba.offs = offs; ba.ids = ids; ba.topk = topk;
+  ba.offs = offs; ba.ids = ids; ba.topk = topk; ba.n_ids = n_entries;
   ba.delta = w.delta; ba.dofp = w.dofp;
   ba.doc = w.doc; ba.deltac = w.deltac; ba.S = w.S; ba.dP = w.dP;
   ba.dqc = w.dqc; ba.dkc = w.dkc; ba.dvc = w.dvc;
@@ -243,7 +286,7 @@ int vsa_forward(const void* q, const void* k, const void* v, const void* gate_c,
   if (!q || !k || !v || !gate_c || !gate_f || !out || !sel_idx || !workspace) return VSA_ERR_INVALID_ARG;
   if (topk < 1 || topk > s.nc) return VSA_ERR_INVALID_ARG;
   if ((int64_t)B * heads * s.nc * topk > INT_MAX) return VSA_ERR_UNSUPPORTED;
-  return forward_impl(q, k, v, gate_c, gate_f, s, topk, nullptr, nullptr, sel_idx, out, saved,
+  return forward_impl(q, k, v, gate_c, gate_f, s, topk, nullptr, nullptr, 0, sel_idx, out, saved,
                       workspace, workspace_bytes, stream);
 }
 
@@ -260,8 +303,8 @@ int block_sparse_attn_varlen(const void* q, const void* k, const void* v,
   if (n_list_entries < 0 || n_list_entries > (int64_t)B * heads * s.nc * s.nc) return VSA_ERR_INVALID_ARG;
   if (n_list_entries > 0 && !kv_ids) return VSA_ERR_INVALID_ARG;
   if (n_list_entries > INT_MAX) return VSA_ERR_UNSUPPORTED;
-  return forward_impl(q, k, v, gate_c, gate_f, s, 0, kv_offsets, kv_ids, nullptr, out, saved,
-                      workspace, workspace_bytes, stream);
+  return forward_impl(q, k, v, gate_c, gate_f, s, 0, kv_offsets, kv_ids, n_list_entries, nullptr,
+                      out, saved, workspace, workspace_bytes, stream);
 }
 
 // Argument checks of the mass rule shared by its entry points.
@@ -293,7 +336,7 @@ int vsa_forward_mass(const void* q, const void* k, const void* v, const void* ga
   st = check_mass(mass, k_min, k_max, s.nc, (int64_t)B * heads * s.nc);
   if (st != VSA_OK) return st;
   const MassRule mr{mass, k_min, k_max, kv_offsets, kv_ids};
-  return forward_impl(q, k, v, gate_c, gate_f, s, 0, nullptr, nullptr, nullptr, out, saved,
+  return forward_impl(q, k, v, gate_c, gate_f, s, 0, nullptr, nullptr, 0, nullptr, out, saved,
                       workspace, workspace_bytes, stream, &mr);
 }
 
@@ -366,9 +409,9 @@ int vsa_coarse_topk(const float* qc, const float* kc, const float* vc,
 int vsa_fine_forward(const void* q, const void* kp, const void* vp, const float* oc,
                      const void* gate_c, const void* gate_f,
                      int B, int heads, int head_dim, int T, int H, int W,
-                     const int32_t* kv_offsets, const int32_t* kv_ids, int topk, int dtype,
-                     void* out, float* lse_f, float* o_fine, const int32_t* order,
-                     hipStream_t stream) {
+                     const int32_t* kv_offsets, const int32_t* kv_ids, int64_t n_list_entries,
+                     int topk, int dtype, void* out, float* lse_f, float* o_fine,
+                     const int32_t* order, hipStream_t stream) {
   Shape s;
   int st = check_shape(B, heads, head_dim, T, H, W, dtype, &s);
   if (st != VSA_OK) return st;
@@ -377,23 +420,49 @@ int vsa_fine_forward(const void* q, const void* kp, const void* vp, const float*
   if (!kv_offsets) {
     if (topk < 1 || topk > s.nc || !kv_ids) return VSA_ERR_INVALID_ARG;
     if ((int64_t)B * heads * s.nc * topk > INT_MAX) return VSA_ERR_UNSUPPORTED;
+    n_list_entries = (int64_t)B * heads * s.nc * topk;
+  } else {
+    if (n_list_entries < 0 || n_list_entries > (int64_t)B * heads * s.nc * s.nc) return VSA_ERR_INVALID_ARG;
+    if (n_list_entries > 0 && !kv_ids) return VSA_ERR_INVALID_ARG;
+    if (n_list_entries > INT_MAX) return VSA_ERR_UNSUPPORTED;
   }
   FineArgs fa{q, kp, vp, oc, gate_c, gate_f, B, heads, head_dim, T, H, W,
-              kv_offsets, kv_ids, topk, dtype == VSA_BF16, out, lse_f, o_fine};
+              kv_offsets, kv_ids, topk, n_list_entries, dtype == VSA_BF16, out, lse_f, o_fine};
   fa.order = order;
   return hip_status(launch_fine_forward(fa, stream));
 }
 
-int vsa_fine_order(const int32_t* kv_offsets, const int32_t* kv_ids, int topk, int B, int heads,
-                   int n_cubes, int32_t* order, hipStream_t stream) {
+int vsa_fine_order(const int32_t* kv_offsets, const int32_t* kv_ids, int64_t n_list_entries,
+                   int topk, int B, int heads, int n_cubes, int32_t* order, hipStream_t stream) {
   if (B < 1 || heads < 1 || n_cubes < 1 || !order) return VSA_ERR_INVALID_ARG;
   if (n_cubes > order_max_cubes() || (int64_t)B * heads > 65535) return VSA_ERR_UNSUPPORTED;
   if ((int64_t)B * heads * n_cubes > INT_MAX / 2) return VSA_ERR_UNSUPPORTED;
   if (!kv_offsets) {
     if (topk < 1 || topk > n_cubes || !kv_ids) return VSA_ERR_INVALID_ARG;
     if ((int64_t)B * heads * n_cubes * topk > INT_MAX) return VSA_ERR_UNSUPPORTED;
+    n_list_entries = (int64_t)B * heads * n_cubes * topk;
+  } else {
+    if (n_list_entries < 0 || n_list_entries > (int64_t)B * heads * n_cubes * n_cubes)
+      return VSA_ERR_INVALID_ARG;
+    if (n_list_entries > 0 && !kv_ids) return VSA_ERR_INVALID_ARG;
+    if (n_list_entries > INT_MAX) return VSA_ERR_UNSUPPORTED;
   }
-  return hip_status(launch_fine_order(kv_offsets, kv_ids, topk, B * heads, n_cubes, order, stream));
+  return hip_status(launch_fine_order(kv_offsets, kv_ids, topk, n_list_entries, B * heads, n_cubes,
+                                      order, stream));
+}
+
+int vsa_validate_lists(const int32_t* kv_offsets, const int32_t* kv_ids, int64_t n_list_entries,
+                       int topk, int n_rows, int n_cubes, int32_t* result, hipStream_t stream) {
+  if (n_rows < 0 || n_cubes < 1 || !result) return VSA_ERR_INVALID_ARG;
+  if (n_cubes > validate_max_cubes()) return VSA_ERR_UNSUPPORTED;
+  if (n_list_entries < 0 || n_list_entries > INT_MAX) return VSA_ERR_INVALID_ARG;
+  if (kv_offsets) {
+    if (n_list_entries > 0 && !kv_ids) return VSA_ERR_INVALID_ARG;
+  } else {
+    if (topk < 1 || !kv_ids || (int64_t)n_rows * topk != n_list_entries) return VSA_ERR_INVALID_ARG;
+  }
+  return hip_status(launch_validate_lists(kv_offsets, kv_ids, topk, n_list_entries, n_rows, n_cubes,
+                                          result, stream));
 }
 
 size_t vsa_backward_workspace_bytes(int B, int heads, int head_dim, int T, int H, int W, int dtype,

@@ -46,6 +46,27 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// ------------------------------------------------------------ key lists
+// Entry range of list `row`: a fixed-length list of `topk` ids (offs null)
+// or CSR offsets, each clamped to the id array [0, n_ids) so that a
+// malformed offset array can never send a read outside it.  The library
+// only promises meaningful results for well-formed lists (non-decreasing
+// offsets from 0 to n_ids, ids in [0, Nc), no repeats within a list); for
+// anything else it promises only that every access stays in bounds.
+__device__ __forceinline__ void list_range(const int32_t* offs, int64_t row, int topk, int64_t n_ids,
+                                           int64_t* start, int* n) {
+  if (!offs) { *start = row * topk; *n = topk; return; }
+  const int64_t s = min(max((int64_t)offs[row], (int64_t)0), n_ids);
+  const int64_t e = min(max((int64_t)offs[row + 1], s), n_ids);
+  *start = s;
+  *n = (int)(e - s);
+}
+
+// A list entry names a key cube only if it lies in [0, nc); kernels read
+// cube 0 in place of any other value and drop its contribution.
+__device__ __forceinline__ bool cube_ok(int id, int nc) { return (unsigned)id < (unsigned)nc; }
+__device__ __forceinline__ int cube_or_0(int id, int nc) { return cube_ok(id, nc) ? id : 0; }
+
 // ------------------------------------------------------------ LDS tiles
 // A cube tile is 64 rows (tokens) x D bf16, row-major, moved as 16-byte
 // chunks (KCH = D/8 per row).  In LDS, logical chunk c of row r sits at

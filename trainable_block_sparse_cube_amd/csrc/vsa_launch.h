@@ -62,6 +62,14 @@ struct CoarseArgs {
 // packed in row order.
 hipError_t launch_pack_lists(const int32_t* counts, const int32_t* padded, int n_rows, int k_max,
                              int32_t* offsets, int32_t* ids, hipStream_t st);
+// Checks of caller-made key lists (CSR offsets, or fixed length `topk`
+// when offs is null) against the fine kernels' preconditions.  Clears
+// result[0..1], then counts into result[0] the offset faults (offs[0] != 0,
+// a decrease, offs[n_rows] != n_ids) and into result[1] the lists holding
+// an id outside [0, nc) or an id twice.  nc <= validate_max_cubes().
+int validate_max_cubes();
+hipError_t launch_validate_lists(const int32_t* offs, const int32_t* ids, int topk, int64_t n_ids,
+                                 int n_rows, int nc, int32_t* result, hipStream_t st);
 // Largest number of cubes the coarse kernel accepts.
 int coarse_max_cubes(int D);
 hipError_t launch_coarse_topk(const CoarseArgs& a, hipStream_t st);
@@ -76,6 +84,7 @@ struct FineArgs {
   const int32_t* offs;  // null: fixed-length lists of `topk`
   const int32_t* ids;
   int topk;
+  int64_t n_ids;        // entries in ids (CSR ranges are clamped to it)
   bool bf16;
   void* out;            // [B, N, heads, D]
   float* lse_f;         // [B, heads, N] cube-major, optional
@@ -86,10 +95,10 @@ hipError_t launch_fine_forward(const FineArgs& a, hipStream_t st);
 // Query cubes of each (b, h) sorted by the middle entry of their key list
 // (cube index on ties), as global ids bh*nc + c, into order[n_bh*nc].
 int order_max_cubes();
-hipError_t launch_fine_order(const int32_t* offs, const int32_t* ids, int topk, int n_bh, int nc,
-                             int32_t* order, hipStream_t st);
+hipError_t launch_fine_order(const int32_t* offs, const int32_t* ids, int topk, int64_t n_ids,
+                             int n_bh, int nc, int32_t* order, hipStream_t st);
 
-// Backward (bf16).  Inputs: raster dout, gates; cube-major tiles qp, kp,
+// Backward (bf16 or fp32).  Inputs: raster dout, gates; cube-major tiles qp, kp,
 // vp from the backward permute; fp32 means; forward state (oc, lse_c,
 // lse_f, of); key lists (offs null: fixed topk).  Scratch: delta [BH,N],
 // dofp tiles, doc [BH,Nc,D], deltac [BH,Nc], S and dP [BH,Nc,Nc],
@@ -97,6 +106,7 @@ hipError_t launch_fine_order(const int32_t* offs, const int32_t* ids, int topk, 
 // tr_tmp (one int per list entry).
 struct BackwardArgs {
   int B, heads, D, T, H, W;
+  bool bf16;  // element type of inputs, tiles and dq/dk/dv: bf16 (MFMA) or fp32 (VALU)
   const void *dout, *gc, *gf;
   const void *qp, *kp, *vp;
   const float *qc, *kc, *vc;
@@ -104,6 +114,7 @@ struct BackwardArgs {
   const int32_t* offs;
   const int32_t* ids;
   int topk;
+  int64_t n_ids;  // entries in ids, tr_ids and tr_tmp
   float* delta;
   void* dofp;
   float *doc, *deltac, *S, *dP, *dqc, *dkc, *dvc;

@@ -79,12 +79,20 @@ def saved_bytes(B, heads, D, grid):
     return _lib.load().vsa_saved_bytes(B, heads, D, *grid)
 
 
-def vsa_forward(q, k, v, gate_c, gate_f, grid, topk, save=False):
-    """Returns (out, sel_idx [B, heads, Nc, topk] int32, saved or None)."""
+def _out(out, q):
+    if out is None:
+        return torch.empty_like(q)
+    _need(out, "out", q.dtype, shape=q.shape)
+    return out
+
+
+def vsa_forward(q, k, v, gate_c, gate_f, grid, topk, save=False, out=None):
+    """Returns (out, sel_idx [B, heads, Nc, topk] int32, saved or None).
+    `out` (optional) is the tensor to write the result into."""
     lib = _lib.load()
     B, N, nh, D, T, H, W, dt = _check_inputs(q, k, v, gate_c, gate_f, grid)
     nc = N // 64
-    out = torch.empty_like(q)
+    out = _out(out, q)
     sel = torch.empty((B, nh, nc, topk), dtype=torch.int32, device=q.device)
     saved = _workspace(lib.vsa_saved_bytes(B, nh, D, T, H, W), q.device) if save else None
     wsb = lib.vsa_forward_workspace_bytes(B, nh, D, T, H, W, dt)
@@ -96,6 +104,29 @@ def vsa_forward(q, k, v, gate_c, gate_f, grid, topk, save=False):
     return out, sel, saved
 
 
+def validate_lists(kv_ids, n_rows, n_cubes, kv_offsets=None, topk=0):
+    """Checks key lists on the GPU (include/vsa.h, vsa_validate_lists) and
+    returns (offset_faults, bad_lists); (0, 0) means well formed.  Reading
+    the answer waits for the current stream."""
+    lib = _lib.load()
+    _need(kv_ids, "kv_ids", torch.int32)
+    if kv_offsets is not None:
+        _need(kv_offsets, "kv_offsets", torch.int32, numel=n_rows + 1)
+    result = torch.empty(2, dtype=torch.int32, device=kv_ids.device)
+    st = lib.vsa_validate_lists(_ptr(kv_offsets), _ptr(kv_ids), int(kv_ids.numel()), int(topk),
+                                int(n_rows), int(n_cubes), _ptr(result), _stream())
+    _lib.check("vsa_validate_lists", st)
+    faults, bad = (int(x) for x in result.tolist())
+    return faults, bad
+
+
+def _require_valid(kv_ids, n_rows, n_cubes, kv_offsets=None, topk=0):
+    faults, bad = validate_lists(kv_ids, n_rows, n_cubes, kv_offsets=kv_offsets, topk=topk)
+    if faults or bad:
+        raise ValueError(f"malformed key lists: {faults} offset fault(s), {bad} list(s) with an id "
+                         f"outside [0, {n_cubes}) or repeated")
+
+
 def _check_lists(kv_offsets, kv_ids, B, nh, nc):
     for name, t in (("kv_offsets", kv_offsets), ("kv_ids", kv_ids)):
         if not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
@@ -104,14 +135,20 @@ def _check_lists(kv_offsets, kv_ids, B, nh, nc):
         raise ValueError("kv_offsets must have B*heads*Nc + 1 entries")
 
 
-def block_sparse_attn_varlen(q, k, v, gate_c, gate_f, grid, kv_offsets, kv_ids, save=False):
+def block_sparse_attn_varlen(q, k, v, gate_c, gate_f, grid, kv_offsets, kv_ids, save=False,
+                             out=None, validate=True):
     """Variable-length key-cube lists (CSR over (b, h, query cube)).
-    Returns (out, saved or None)."""
+    Returns (out, saved or None).  With validate (the default) the lists are
+    checked on the GPU first and a ValueError names what is wrong; that
+    check waits for the stream, so hot loops with known-good lists pass
+    validate=False."""
     lib = _lib.load()
     B, N, nh, D, T, H, W, dt = _check_inputs(q, k, v, gate_c, gate_f, grid)
     nc = N // 64
     _check_lists(kv_offsets, kv_ids, B, nh, nc)
-    out = torch.empty_like(q)
+    if validate:
+        _require_valid(kv_ids, B * nh * nc, nc, kv_offsets=kv_offsets)
+    out = _out(out, q)
     saved = _workspace(lib.vsa_saved_bytes(B, nh, D, T, H, W), q.device) if save else None
     wsb = lib.vsa_forward_workspace_bytes(B, nh, D, T, H, W, dt)
     ws = _workspace(wsb, q.device)
@@ -147,9 +184,10 @@ def vsa_forward_mass(q, k, v, gate_c, gate_f, grid, mass, k_min, k_max, save=Fal
     return out, offs, ids[:int(offs[-1].item())] if trim else ids, saved
 
 
-def vsa_backward(q, k, v, gate_c, gate_f, dout, sel, saved, grid):
+def vsa_backward(q, k, v, gate_c, gate_f, dout, sel, saved, grid, validate=False):
     """Gradients of sum(dout * out) for a forward run with save=True.
-    Returns (dq, dk, dv, dgate_c, dgate_f); gate gradients are fp32."""
+    Returns (dq, dk, dv, dgate_c, dgate_f); gate gradients are fp32.
+    validate checks a caller-made sel first (vsa_forward's own needs none)."""
     lib = _lib.load()
     B, N, nh, D, T, H, W, dt = _check_inputs(q, k, v, gate_c, gate_f, grid)
     _need(dout, "dout", q.dtype, shape=q.shape)
@@ -157,6 +195,8 @@ def vsa_backward(q, k, v, gate_c, gate_f, dout, sel, saved, grid):
     if sel.dim() != 4 or tuple(sel.shape[:3]) != (B, nh, nc):
         raise ValueError("sel must be [B, heads, Nc, topk]")
     _need(sel, "sel", torch.int32)
+    if validate:
+        _require_valid(sel, B * nh * nc, nc, topk=sel.shape[-1])
     _need(saved, "saved", torch.uint8, min_numel=int(lib.vsa_saved_bytes(B, nh, D, T, H, W)))
     topk = sel.shape[-1]
     grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
@@ -171,10 +211,15 @@ def vsa_backward(q, k, v, gate_c, gate_f, dout, sel, saved, grid):
     return tuple(grads)
 
 
-def block_sparse_attn_varlen_backward(q, k, v, gate_c, gate_f, dout, kv_offsets, kv_ids, saved, grid):
+def block_sparse_attn_varlen_backward(q, k, v, gate_c, gate_f, dout, kv_offsets, kv_ids, saved, grid,
+                                      validate=True):
+    """Gradients for a block_sparse_attn_varlen forward run with save=True
+    and the same lists (checked first unless validate is False)."""
     lib = _lib.load()
     B, N, nh, D, T, H, W, dt = _check_inputs(q, k, v, gate_c, gate_f, grid)
     _check_lists(kv_offsets, kv_ids, B, nh, N // 64)
+    if validate:
+        _require_valid(kv_ids, B * nh * (N // 64), N // 64, kv_offsets=kv_offsets)
     _need(dout, "dout", q.dtype, shape=q.shape)
     _need(saved, "saved", torch.uint8, min_numel=int(lib.vsa_saved_bytes(B, nh, D, T, H, W)))
     grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
@@ -305,7 +350,7 @@ def vsa_fine_forward(q, kp, vp, oc, gate_c, gate_f, grid, kv_ids, topk=0, kv_off
         lse = torch.empty((B, nh, N), dtype=torch.float32, device=q.device)
         of = torch.empty((B, nh, N, D), dtype=torch.float32, device=q.device)
     st = lib.vsa_fine_forward(_ptr(q), _ptr(kp), _ptr(vp), _ptr(oc), _ptr(gate_c), _ptr(gate_f),
-                              B, nh, D, *grid, _ptr(kv_offsets), _ptr(kv_ids), topk,
+                              B, nh, D, *grid, _ptr(kv_offsets), _ptr(kv_ids), int(kv_ids.numel()), topk,
                               _DT[q.dtype], _ptr(out), _ptr(lse), _ptr(of), _ptr(order), _stream())
     _lib.check("vsa_fine_forward", st)
     return out, lse, of
@@ -321,26 +366,8 @@ def vsa_fine_order(kv_ids, B, heads, n_cubes, topk=0, kv_offsets=None):
     elif kv_ids.numel() != B * heads * n_cubes * topk:
         raise ValueError("kv_ids must hold B*heads*Nc*topk ids")
     order = torch.empty(B * heads * n_cubes, dtype=torch.int32, device=kv_ids.device)
-    st = lib.vsa_fine_order(_ptr(kv_offsets), _ptr(kv_ids), topk, B, heads, n_cubes, _ptr(order),
+    st = lib.vsa_fine_order(_ptr(kv_offsets), _ptr(kv_ids), int(kv_ids.numel()), topk, B, heads,
+                            n_cubes, _ptr(order),
                             _stream())
     _lib.check("vsa_fine_order", st)
     return order
-
-
-# ------------------------------------------------------- measurement helper
-def probe_tile_gather(kp, vp, kv_ids, topk, depth=8):
-    """include/vsa_probe.h: stream the K and V tiles the fine stage reads for
-    the fixed-length lists kv_ids [B, heads, Nc, topk], with no arithmetic
-    (the fine stage's data-movement floor).  Queued on the current stream."""
-    lib = _lib.load()
-    if kp.dim() != 5 or kp.shape[3] != 64:
-        raise ValueError("kp must be [B, heads, Nc, 64, D]")
-    B, nh, nc, _, D = kp.shape
-    _need(kp, "kp", kp.dtype)
-    _need(vp, "vp", kp.dtype, shape=kp.shape)
-    _need(kv_ids, "kv_ids", torch.int32, numel=B * nh * nc * topk)
-    sink = torch.empty(4096, dtype=torch.uint8, device=kp.device)
-    st = lib.vsa_probe_tile_gather(_ptr(kp), _ptr(vp), B * nh, nc, D, _ptr(kv_ids), topk, depth,
-                                   _ptr(sink), _stream())
-    if st != 0:
-        raise RuntimeError(f"vsa_probe_tile_gather failed with status {st}")
