@@ -102,6 +102,25 @@ int vsa_forward(const void* q, const void* k, const void* v,
                 void* out, int32_t* sel_idx, void* saved,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* vsa_forward_noalloc: vsa_forward for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors as
+ * vsa_forward without the workspace: the workspace lives in a fixed
+ * 128 MiB device array inside the library (one per GPU, held until the
+ * process ends; enough for B*heads = 12 at 16384 tokens, head_dim 128,
+ * bf16).  A shape whose forward workspace (vsa_forward_workspace_bytes)
+ * exceeds 128 MiB returns VSA_ERR_WORKSPACE and queues nothing.  The call
+ * allocates nothing; its first call on a device looks up that device's
+ * copy of the array.  All calls on one GPU share the array, so calls that
+ * overlap in time on one GPU (on different streams, or from different
+ * threads) race and must be serialized by the caller.
+ */
+int vsa_forward_noalloc(const void* q, const void* k, const void* v,
+                        const void* gate_c, const void* gate_f,
+                        int B, int heads, int head_dim, int T, int H, int W,
+                        int topk, int dtype,
+                        void* out, int32_t* sel_idx, void* saved, hipStream_t stream);
+
 /* block_sparse_attn_varlen: as vsa_forward, but step 3 is replaced by a
  * caller-given list of key cubes per query cube ([VSA2-abs]: each query
  * attends a variable number of key-value pairs; the router that would make

@@ -177,6 +177,17 @@ extern "C" hipError_t hipMemcpyAsync(void* dst, const void* src, size_t n, hipMe
   return hipSuccess;
 }
 extern "C" hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
+// The fixed scratch of the allocation-free entry point: in this host build
+// the "device address" of the array is the host array itself, so the stub
+// launches' writes into it are bounds-checked by ASan against its size.
+extern "C" hipError_t hipGetDevice(int* dev) {
+  *dev = 0;
+  return hipSuccess;
+}
+extern "C" hipError_t hipGetSymbolAddress(void** ptr, const void* symbol) {
+  *ptr = const_cast<void*>(symbol);
+  return hipSuccess;
+}
 
 // ------------------------------------------------------------------ driver
 namespace {
@@ -299,6 +310,19 @@ void run_shape(int B, int heads, int D, int T, int H, int W, int dtype, int topk
                                            nullptr) == VSA_ERR_INVALID_ARG);
   g_validate_faults = 0;
   unsetenv("VSA_VALIDATE");
+
+  // the allocation-free forward: same launches into the fixed scratch,
+  // refused (nothing queued) where the workspace would not fit in it
+  const int launches = g_launches;
+  const int st = vsa_forward_noalloc(q, k, v, gc, gf, B, heads, D, T, H, W, topk, dtype, out, sel, saved,
+                                     nullptr);
+  if (fwb <= (size_t(128) << 20)) {
+    EXPECT(st == VSA_OK);
+    EXPECT(g_launches > launches);
+  } else {
+    EXPECT(st == VSA_ERR_WORKSPACE);
+    EXPECT(g_launches == launches);
+  }
 }
 
 void argument_checks() {
@@ -352,6 +376,13 @@ void argument_checks() {
   EXPECT(vsa_fine_order(I, I, 65, 0, 1, 1, 8, I, nullptr) == VSA_ERR_INVALID_ARG);
   EXPECT(vsa_validate_lists(I, I, 10, 0, 4, 5000, I, nullptr) == VSA_ERR_UNSUPPORTED);
   EXPECT(vsa_validate_lists(nullptr, I, 10, 3, 4, 8, I, nullptr) == VSA_ERR_INVALID_ARG);
+  EXPECT(vsa_forward_noalloc(F, F, F, F, F, 1, 2, 64, 8, 8, 8, 9, VSA_BF16, F, I, nullptr, nullptr) ==
+         VSA_ERR_INVALID_ARG);
+  EXPECT(vsa_forward_noalloc(F, F, F, F, F, 1, 2, 64, 8, 8, 8, 2, VSA_BF16, F, nullptr, nullptr, nullptr) ==
+         VSA_ERR_INVALID_ARG);
+  // the 16384-token training shape with B = 2 needs about 215 MB of workspace
+  EXPECT(vsa_forward_noalloc(F, F, F, F, F, 2, 12, 128, 16, 32, 32, 32, VSA_BF16, F, I, nullptr, nullptr) ==
+         VSA_ERR_WORKSPACE);
   EXPECT(g_launches == 0);  // no failing call queued anything
 }
 
@@ -364,6 +395,7 @@ int main() {
       {1, 2, 64, 8, 8, 8, VSA_F32, 2},   {1, 2, 64, 8, 8, 8, VSA_BF16, 3},
       {2, 3, 128, 4, 8, 12, VSA_BF16, 6}, {2, 1, 128, 4, 4, 4, VSA_F32, 1},
       {1, 2, 128, 12, 8, 16, VSA_F32, 24}, {1, 1, 64, 4, 8, 20, VSA_BF16, 10},
+      {1, 12, 128, 16, 32, 32, VSA_BF16, 32},  // the largest workload the fixed scratch holds
   };
   for (const auto& s : shapes) run_shape(s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7]);
   if (failures) {

@@ -19,8 +19,10 @@ ROCM_INCLUDE = "/opt/rocm/include"
                     reason="needs g++ and the HIP headers")
 def test_abi_host_code_under_asan_and_ubsan(tmp_path):
     exe = str(tmp_path / "abi_sanitize")
+    # the two macros that only the HIP compiler defines, for a host-only build
     cmd = ["g++", "-std=c++17", "-g", "-O1", "-fsanitize=address,undefined",
            "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-D__HIP_PLATFORM_AMD__",
+           "-D__align__(n)=__attribute__((aligned(n)))", "-DHIP_SYMBOL(X)=X",
            "-I", ROCM_INCLUDE, "-I", os.path.join(ROOT, "include"),
            "-I", os.path.join(ROOT, "trainable_block_sparse_cube_amd", "csrc"),
            "-x", "c++", SRC[0], "-x", "c++", SRC[1], "-o", exe]

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 using namespace vsa;
 
@@ -249,6 +250,32 @@ int backward_impl(const void* q, const void* k, const void* v, const void* gc, c
   return hip_status(launch_backward(ba, st));
 }
 
+// ------------------------------------------------ fixed device scratch
+// vsa_forward_noalloc runs the forward with its workspace in this array
+// instead of a caller's buffer.  Every GPU the library is loaded on holds
+// its own copy until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: the device address of each
+// GPU's copy is looked up once per device (with that device current) and
+// kept in scratch_ptr, and only that address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+int device_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return VSA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress((void**)&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return VSA_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  return VSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -288,6 +315,26 @@ int vsa_forward(const void* q, const void* k, const void* v, const void* gate_c,
   if ((int64_t)B * heads * s.nc * topk > INT_MAX) return VSA_ERR_UNSUPPORTED;
   return forward_impl(q, k, v, gate_c, gate_f, s, topk, nullptr, nullptr, 0, sel_idx, out, saved,
                       workspace, workspace_bytes, stream);
+}
+
+int vsa_forward_noalloc(const void* q, const void* k, const void* v, const void* gate_c,
+                        const void* gate_f, int B, int heads, int head_dim, int T, int H, int W,
+                        int topk, int dtype, void* out, int32_t* sel_idx, void* saved,
+                        hipStream_t stream) {
+  Shape s;
+  int st = check_shape(B, heads, head_dim, T, H, W, dtype, &s);
+  if (st != VSA_OK) return st;
+  if (!q || !k || !v || !gate_c || !gate_f || !out || !sel_idx) return VSA_ERR_INVALID_ARG;
+  if (topk < 1 || topk > s.nc) return VSA_ERR_INVALID_ARG;
+  if ((int64_t)B * heads * s.nc * topk > INT_MAX) return VSA_ERR_UNSUPPORTED;
+  if (fwd_ws_layout(s, nullptr, nullptr) > kNoAllocScratchBytes) return VSA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = device_scratch(&ws);
+  if (st != VSA_OK) return st;
+  // Nothing in the forward's workspace has to start at zero: every stage
+  // writes what the next one reads.
+  return forward_impl(q, k, v, gate_c, gate_f, s, topk, nullptr, nullptr, 0, sel_idx, out, saved, ws,
+                      kNoAllocScratchBytes, stream);
 }
 
 int block_sparse_attn_varlen(const void* q, const void* k, const void* v,
