@@ -78,6 +78,7 @@ def parse():
                    help="also time top-K 16, the 16K and 70400-token workloads, varlen, the mass rule "
                         "and smooth inputs")
     p.add_argument("--no-dense", action="store_true", help="skip the dense reference (about 0.1 s of GPU time)")
+    p.add_argument("--no-backward", action="store_true", help="skip the training-workload backward")
     return p.parse_args()
 
 
@@ -250,7 +251,8 @@ def main():
         },
     }
     del kp, vp, fout, q, k, v, gc, gf, out
-    res["backward_train16k"] = backward_case(vsa, torch, stream, a)
+    if not a.no_backward:
+        res["backward_train16k"] = backward_case(vsa, torch, stream, a)
     if not a.no_dense:
         res["dense_reference"] = dense_case(vsa, torch, stream, ms_step, fine_tflops)
     if a.copy_calibration:
