@@ -783,19 +783,6 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(
 // pair's products are formed as in the oracle's formulas, in a fixed order,
 // so results are deterministic.
 
-// Copy `rows` rows of D floats from src (contiguous) into dst with row
-// pitch `pitch` floats, by the 256 threads of the workgroup.
-template <int D>
-__device__ __forceinline__ void copy_rows_f32(const float* __restrict__ src, float* dst, int rows, int pitch) {
-  constexpr int V = D / 4;  // float4 per row
-  for (int i = threadIdx.x; i < rows * V; i += 256) {
-    const int r = i / V, c4 = i - r * V;
-    const f32x4 x = *reinterpret_cast<const f32x4*>(src + (int64_t)r * D + 4 * c4);
-    float* d = dst + r * pitch + 4 * c4;
-    d[0] = x[0]; d[1] = x[1]; d[2] = x[2]; d[3] = x[3];
-  }
-}
-
 // dQ of one query cube: for each selected key cube, two halves of 32 keys.
 //   phase A: thread (query i = t % 64, keys j = t / 64 + 4e, e < 8):
 //            s = q_i.k_j, dP = dOf_i.v_j, P = exp(s s - lse_i),

@@ -29,8 +29,8 @@
 // cubes sweeping similar key ranges share an XCD's L2 at the same time),
 // or in natural order.
 //
-// fp32 kernel: plain VALU, one wave per query cube, one lane per query
-// token; it serves the fp32 path, where no reduced precision is allowed.
+// fp32 kernel: plain VALU, one 256-thread workgroup per query cube; it
+// serves the fp32 path, where no reduced precision is allowed.
 #include "vsa_device.h"
 #include "vsa_launch.h"
 
@@ -248,73 +248,101 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
         l_tot > 0.f ? (m_max + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
+// fp32: one workgroup of 256 threads per query cube, plain fp32 vector
+// arithmetic.  The cube's 64 query rows sit in LDS (rows padded by one float
+// so that lanes reading one column of different rows hit distinct banks);
+// each selected key tile is taken in two halves of 32 keys:
+//   phase A: thread (query i = t % 64, keys j = t / 64 + 4e, e < 8) forms
+//            s_ij = scale * q_i.k_j into an LDS row block;
+//   phase B: thread (query i, dims d = t / 64 + 4m) updates the running
+//            max, rescales, and accumulates exp(s_ij - max) v_j[d].
+// The four threads of a query row keep identical softmax statistics.
 template <int D>
-__global__ __launch_bounds__(64) void fine_fwd_f32_kernel(
+__global__ __launch_bounds__(256) void fine_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kp, const float* __restrict__ vp,
     const float* __restrict__ oc, const float* __restrict__ gc, const float* __restrict__ gf,
     int nh, int nc, int Hg, int Wg,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk, int64_t n_ids,
     float scale, float* __restrict__ out, float* __restrict__ lse_f, float* __restrict__ o_fine) {
-  __shared__ float k_lds[64 * D];
-  __shared__ float v_lds[D * 64];
-  __shared__ float s_lds[64][65];  // this tile's scaled logits, [key][query slot]
-  const int slot = threadIdx.x;
+  constexpr int P1 = D + 1;
+  __shared__ float qs[64 * P1];
+  __shared__ float ks[32 * D], vs[32 * D];
+  __shared__ float sm[64 * 33];
+  const int tid = threadIdx.x, i = tid & 63, w = tid >> 6;
   const int blk = blockIdx.x;
   const int bh = blk / nc;
   const int c = blk - bh * nc;
   const int64_t N = (int64_t)nc * 64;
+  const int b = bh / nh, h = bh - b * nh;
+  const int64_t bh_tiles = (int64_t)bh * nc;
   int64_t start;
   int n;
   list_range(offs, blk, topk, n_ids, &start, &n);
 
-  float qv[D], acc[D];
-  const int b = bh / nh, h = bh - b * nh;
-  const int64_t tok_stride = (int64_t)nh * D;
-  const float* qrow = q + ((int64_t)b * N + raster_token(c, slot, Hg, Wg)) * tok_stride + (int64_t)h * D;
+  // the cube's 64 query rows, gathered from raster order
+  for (int e = tid; e < 64 * (D / 4); e += 256) {
+    const int r = e / (D / 4), c4 = e - r * (D / 4);
+    const int64_t tok = raster_token(c, r, Hg, Wg);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(q + (((int64_t)b * N + tok) * nh + h) * D + 4 * c4);
+    float* d = qs + r * P1 + 4 * c4;
+    d[0] = x[0]; d[1] = x[1]; d[2] = x[2]; d[3] = x[3];
+  }
+  float acc[D / 4];
 #pragma unroll
-  for (int d = 0; d < D; ++d) { qv[d] = qrow[d]; acc[d] = 0.f; }
+  for (int m = 0; m < D / 4; ++m) acc[m] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   for (int it = 0; it < n; ++it) {
     const int kc = ids[start + it];
     if (!cube_ok(kc, nc)) continue;  // not a key cube: no contribution
-    const float* ks = kp + ((int64_t)bh * nc + kc) * 64 * D;
-    const float* vs = vp + ((int64_t)bh * nc + kc) * 64 * D;
-    __syncthreads();
-    for (int i = slot; i < 64 * D; i += 64) { k_lds[i] = ks[i]; v_lds[i] = vs[i]; }
-    __syncthreads();
-    float mx = -INFINITY;
-    for (int j = 0; j < 64; ++j) {
-      float s = 0.f;
+    for (int half = 0; half < 2; ++half) {
+      __syncthreads();  // previous phase B done with ks, vs, sm (and qs written)
+      const int64_t row0 = (bh_tiles + kc) * 64 + 32 * half;
+      copy_rows_f32<D>(kp + row0 * D, ks, 32, D);
+      copy_rows_f32<D>(vp + row0 * D, vs, 32, D);
+      __syncthreads();
+      float sv[8];
 #pragma unroll
-      for (int d = 0; d < D; ++d) s = fmaf(qv[d], k_lds[j * D + d], s);
-      s_lds[j][slot] = s * scale;
-      mx = fmaxf(mx, s * scale);
-    }
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = expf(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
+      for (int e = 0; e < 8; ++e) sv[e] = 0.f;
+#pragma unroll 8
+      for (int d = 0; d < D; ++d) {
+        const float qd = qs[i * P1 + d];
 #pragma unroll
-    for (int d = 0; d < D; ++d) acc[d] *= alpha;
-    for (int j = 0; j < 64; ++j) {
-      const float w = expf(s_lds[j][slot] - m_new);
-      l_run += w;
+        for (int e = 0; e < 8; ++e) sv[e] = fmaf(qd, ks[(w + 4 * e) * D + d], sv[e]);
+      }
 #pragma unroll
-      for (int d = 0; d < D; ++d) acc[d] = fmaf(w, v_lds[j * D + d], acc[d]);
+      for (int e = 0; e < 8; ++e) sm[i * 33 + w + 4 * e] = sv[e] * scale;
+      __syncthreads();
+      float mx = m_run;
+      for (int j = 0; j < 32; ++j) mx = fmaxf(mx, sm[i * 33 + j]);
+      const float alpha = m_run == -INFINITY ? 0.f : expf(m_run - mx);
+      m_run = mx;
+      l_run *= alpha;
+#pragma unroll
+      for (int m = 0; m < D / 4; ++m) acc[m] *= alpha;
+#pragma unroll 4
+      for (int j = 0; j < 32; ++j) {
+        const float p = expf(sm[i * 33 + j] - m_run);
+        l_run += p;
+#pragma unroll
+        for (int m = 0; m < D / 4; ++m) acc[m] = fmaf(p, vs[j * D + w + 4 * m], acc[m]);
+      }
     }
   }
   const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-  const int tok = raster_token(c, slot, Hg, Wg);
+  const int tok = raster_token(c, i, Hg, Wg);
   const int64_t gidx = ((int64_t)b * N + tok) * nh + h;
   const float g_c = gc[gidx], g_f = gf[gidx];
-  const float* ocrow = oc + ((int64_t)bh * nc + c) * D;
-  float* ofrow = o_fine ? o_fine + ((int64_t)bh * N + (int64_t)c * 64 + slot) * D : nullptr;
-  for (int d = 0; d < D; ++d) {
-    const float of = acc[d] * inv;
+  const float* ocrow = oc + (bh_tiles + c) * D;
+  float* ofrow = o_fine ? o_fine + ((int64_t)bh * N + (int64_t)c * 64 + i) * D : nullptr;
+#pragma unroll
+  for (int m = 0; m < D / 4; ++m) {
+    const int d = w + 4 * m;
+    const float of = acc[m] * inv;
     out[gidx * D + d] = fmaf(g_c, ocrow[d], g_f * of);
     if (ofrow) ofrow[d] = of;
   }
-  if (lse_f) lse_f[(int64_t)bh * N + (int64_t)c * 64 + slot] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
+  if (lse_f && w == 0)
+    lse_f[(int64_t)bh * N + (int64_t)c * 64 + i] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
 }
 
 template <int D>
@@ -328,7 +356,7 @@ hipError_t launch_fine_d(const FineArgs& a, hipStream_t st) {
         (const bf16*)a.gc, (const bf16*)a.gf, a.heads, nc, a.H, a.W, a.offs, a.ids, a.topk,
         a.n_ids, scale * kLog2e, (int)grid, a.order, (bf16*)a.out, a.lse_f, a.o_fine);
   } else {
-    fine_fwd_f32_kernel<D><<<grid, 64, 0, st>>>(
+    fine_fwd_f32_kernel<D><<<grid, 256, 0, st>>>(
         (const float*)a.q, (const float*)a.kp, (const float*)a.vp, a.oc,
         (const float*)a.gc, (const float*)a.gf, a.heads, nc, a.H, a.W, a.offs, a.ids, a.topk,
         a.n_ids, scale, (float*)a.out, a.lse_f, a.o_fine);

@@ -67,6 +67,21 @@ __device__ __forceinline__ void list_range(const int32_t* offs, int64_t row, int
 __device__ __forceinline__ bool cube_ok(int id, int nc) { return (unsigned)id < (unsigned)nc; }
 __device__ __forceinline__ int cube_or_0(int id, int nc) { return cube_ok(id, nc) ? id : 0; }
 
+// ------------------------------------------------------------ fp32 tiles
+// Copy `rows` rows of D floats from src (contiguous) into dst with row
+// pitch `pitch` floats, by the 256 threads of the workgroup (the fp32
+// kernels; a pitch of D + 1 puts a column's rows on distinct banks).
+template <int D>
+__device__ __forceinline__ void copy_rows_f32(const float* __restrict__ src, float* dst, int rows, int pitch) {
+  constexpr int V = D / 4;  // float4 per row
+  for (int i = threadIdx.x; i < rows * V; i += 256) {
+    const int r = i / V, c4 = i - r * V;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(src + (int64_t)r * D + 4 * c4);
+    float* d = dst + r * pitch + 4 * c4;
+    d[0] = x[0]; d[1] = x[1]; d[2] = x[2]; d[3] = x[3];
+  }
+}
+
 // ------------------------------------------------------------ LDS tiles
 // A cube tile is 64 rows (tokens) x D bf16, row-major, moved as 16-byte
 // chunks (KCH = D/8 per row).  In LDS, logical chunk c of row r sits at
