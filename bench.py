@@ -40,12 +40,21 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 FINE_SRC = os.path.join(ROOT, "trainable_block_sparse_cube_amd", "csrc", "fine_fwd.hip")
+DEVICE_H = os.path.join(ROOT, "trainable_block_sparse_cube_amd", "csrc", "vsa_device.h")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "fine_fwd_bf16_long61k_k32_pmc.txt")
 
 
 def fine_source_hash():
-    with open(FINE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of what the bf16 fine kernel is built from: fine_fwd.hip without
+    the fp32 kernel's function text, plus the device helper header."""
+    src = open(FINE_SRC).read()
+    head = "template <int D>\n__global__ __launch_bounds__(256) void fine_fwd_f32_kernel("
+    i = src.index(head)
+    j = src.index("\n}\n", i) + 3
+    h = hashlib.sha256((src[:i] + src[j:]).encode())
+    with open(DEVICE_H, "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_counters():
