@@ -271,9 +271,12 @@ int vsa_pack_lists(const int32_t* counts, const int32_t* ids_padded, int n_rows,
  * ids (topk ignored).  lse_f [B,heads,N] and
  * o_fine [B,heads,N,D] (fp32, cube-major) are written only if non-NULL
  * (both or neither).  order (optional, NULL = natural order): a permutation
- * of the B*heads*Nc query cubes (global ids (b*heads + h)*Nc + c, each
- * (b, h)'s cubes kept together) giving the order in which the bf16 kernel
- * runs them, as written by vsa_fine_order; it changes no result. */
+ * of the B*heads*Nc query cubes (global ids (b*heads + h)*Nc + c) giving
+ * the order in which the bf16 kernel runs them, as written by
+ * vsa_fine_order; it changes no result.  An entry outside [0, B*heads*Nc)
+ * runs nothing, so an order that is not a permutation leaves the rows of
+ * the cubes it misses unwritten (and computes repeated cubes twice, with
+ * the same result). */
 int vsa_fine_forward(const void* q, const void* kp, const void* vp,
                      const float* oc, const void* gate_c, const void* gate_f,
                      int B, int heads, int head_dim, int T, int H, int W,

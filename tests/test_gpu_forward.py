@@ -332,6 +332,42 @@ def test_fine_order_sorts_by_middle_entry_and_changes_nothing():
     np.testing.assert_array_equal(order.cpu().numpy(), want)
 
 
+def test_fine_order_entries_out_of_range_run_nothing():
+    """An order entry outside [0, B*heads*Nc) runs no cube (the kernel's own
+    range check): those cubes' rows keep what the output held, every other
+    row equals the natural-order result."""
+    vsa = _vsa()
+    B, nh, D, grid, K = 1, 2, 128, (8, 12, 16), 5  # 24 cubes per head
+    nc = 24
+    inp = make_inputs(B, nh, D, grid, dtype="bf16", seed=63)
+    q, k, v, gc, gf = (dev(inp[n], BF16) for n in ("q", "k", "v", "gc", "gf"))
+    _, kp, vp, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, grid, with_q_tiles=False)
+    oc, _, sel = vsa.vsa_coarse_topk(qc, kc, vc, K, input_dtype=BF16)
+    ref, _, _ = vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, grid, sel, topk=K)
+    order = torch.arange(B * nh * nc, dtype=torch.int32, device="cuda")
+    dropped = [3, nc + 7]
+    order[dropped[0]] = -1
+    order[dropped[1]] = B * nh * nc
+    out = torch.full_like(q, float("nan"))
+    vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, grid, sel, topk=K, out=out, order=order)
+    torch.cuda.synchronize()
+    # token rows of each dropped cube (raster order), for its head
+    T, H, W = grid
+    cube_rows = {}
+    for g in dropped:
+        h, c = divmod(g, nc)
+        W4, H4 = W // 4, H // 4
+        ct, cy, cx = c // (H4 * W4), (c // W4) % H4, c % W4
+        toks = [((4 * ct + s // 16) * H + 4 * cy + (s // 4) % 4) * W + 4 * cx + s % 4 for s in range(64)]
+        cube_rows[g] = (h, toks)
+    o, r = out.float().cpu(), ref.float().cpu()
+    mask = torch.zeros(o.shape[:3], dtype=torch.bool)
+    for g, (h, toks) in cube_rows.items():
+        mask[0, toks, h] = True
+    assert torch.isnan(o[mask]).all()
+    assert torch.equal(o[~mask], r[~mask])
+
+
 def test_forward_is_deterministic():
     vsa = _vsa()
     grid = (8, 16, 16)

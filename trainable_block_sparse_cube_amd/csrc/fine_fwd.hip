@@ -86,6 +86,7 @@ __global__ __launch_bounds__(256, 2) void fine_fwd_bf16_kernel(
   const int lblk = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
   if (lblk >= n_logical) return;
   const int blk = order ? order[lblk] : lblk;
+  if ((unsigned)blk >= (unsigned)n_logical) return;  // an order entry out of range runs nothing
   const int bh = blk / nc;
   const int c = blk - bh * nc;
   const int64_t N = (int64_t)nc * 64;

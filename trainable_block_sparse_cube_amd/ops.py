@@ -9,6 +9,8 @@ q, k, v, out: [B, N, heads, D]; gates: [B, N, heads]; N = T*H*W.
 """
 from __future__ import annotations
 
+import contextlib
+
 import torch
 
 from . import _lib
@@ -16,8 +18,13 @@ from . import _lib
 _DT = {torch.float32: _lib.VSA_F32, torch.bfloat16: _lib.VSA_BF16}
 
 
-def _stream():
-    return torch.cuda.current_stream().cuda_stream
+@contextlib.contextmanager
+def _on(t):
+    """Runs the enclosed library call with t's GPU as the current device and
+    yields that device's current stream: the kernels launch where the
+    tensors live, whichever device the caller has current."""
+    with torch.cuda.device(t.device):
+        yield torch.cuda.current_stream(t.device).cuda_stream
 
 
 def _ptr(t):
@@ -34,6 +41,8 @@ def _check_inputs(q, k, v, gate_c, gate_f, grid):
             raise ValueError(f"{name} must be contiguous")
         if t.dtype != q.dtype:
             raise TypeError(f"{name} has dtype {t.dtype}, expected {q.dtype}")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must share one [B, N, heads, D] shape")
     B, N, nh, D = q.shape
@@ -45,13 +54,16 @@ def _check_inputs(q, k, v, gate_c, gate_f, grid):
     return B, N, nh, D, T, H, W, _DT[q.dtype]
 
 
-def _need(t, name, dtype, shape=None, numel=None, min_numel=None):
-    """A tensor handed to the C ABI as a raw pointer: on the GPU, dense, of
-    the element type (and shape or size) the call assumes."""
+def _need(t, name, dtype, shape=None, numel=None, min_numel=None, device=None):
+    """A tensor handed to the C ABI as a raw pointer: on the GPU (on
+    `device` when given), dense, of the element type (and shape or size) the
+    call assumes."""
     if t is None:
         raise ValueError(f"{name} is required")
     if not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     if t.dtype != dtype:
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
@@ -66,7 +78,7 @@ def _check_qkv(q, k, v, grid):
     if q.dtype not in _DT:
         raise TypeError(f"unsupported dtype {q.dtype}")
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _need(t, name, q.dtype, shape=q.shape)
+        _need(t, name, q.dtype, shape=q.shape, device=q.device)
     if q.dim() != 4 or q.shape[1] != grid[0] * grid[1] * grid[2]:
         raise ValueError(f"q must be [B, N, heads, D] with N = {grid[0] * grid[1] * grid[2]}")
 
@@ -82,7 +94,7 @@ def saved_bytes(B, heads, D, grid):
 def _out(out, q):
     if out is None:
         return torch.empty_like(q)
-    _need(out, "out", q.dtype, shape=q.shape)
+    _need(out, "out", q.dtype, shape=q.shape, device=q.device)
     return out
 
 
@@ -97,9 +109,10 @@ def vsa_forward(q, k, v, gate_c, gate_f, grid, topk, save=False, out=None):
     saved = _workspace(lib.vsa_saved_bytes(B, nh, D, T, H, W), q.device) if save else None
     wsb = lib.vsa_forward_workspace_bytes(B, nh, D, T, H, W, dt)
     ws = _workspace(wsb, q.device)
-    st = lib.vsa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(gate_c), _ptr(gate_f),
-                         B, nh, D, T, H, W, topk, dt, _ptr(out), _ptr(sel), _ptr(saved),
-                         _ptr(ws), wsb, _stream())
+    with _on(q) as stream:
+        st = lib.vsa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(gate_c), _ptr(gate_f),
+                             B, nh, D, T, H, W, topk, dt, _ptr(out), _ptr(sel), _ptr(saved),
+                             _ptr(ws), wsb, stream)
     _lib.check("vsa_forward", st)
     return out, sel, saved
 
@@ -109,12 +122,13 @@ def validate_lists(kv_ids, n_rows, n_cubes, kv_offsets=None, topk=0):
     returns (offset_faults, bad_lists); (0, 0) means well formed.  Reading
     the answer waits for the current stream."""
     lib = _lib.load()
-    _need(kv_ids, "kv_ids", torch.int32)
+    _need(kv_ids, "kv_ids", torch.int32, device=kv_ids.device)
     if kv_offsets is not None:
-        _need(kv_offsets, "kv_offsets", torch.int32, numel=n_rows + 1)
+        _need(kv_offsets, "kv_offsets", torch.int32, numel=n_rows + 1, device=kv_ids.device)
     result = torch.empty(2, dtype=torch.int32, device=kv_ids.device)
-    st = lib.vsa_validate_lists(_ptr(kv_offsets), _ptr(kv_ids), int(kv_ids.numel()), int(topk),
-                                int(n_rows), int(n_cubes), _ptr(result), _stream())
+    with _on(kv_ids) as stream:
+        st = lib.vsa_validate_lists(_ptr(kv_offsets), _ptr(kv_ids), int(kv_ids.numel()), int(topk),
+                                    int(n_rows), int(n_cubes), _ptr(result), stream)
     _lib.check("vsa_validate_lists", st)
     faults, bad = (int(x) for x in result.tolist())
     return faults, bad
@@ -131,6 +145,8 @@ def _check_lists(kv_offsets, kv_ids, B, nh, nc):
     for name, t in (("kv_offsets", kv_offsets), ("kv_ids", kv_ids)):
         if not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous int32 GPU tensor")
+    if kv_ids.device != kv_offsets.device:
+        raise ValueError("kv_offsets and kv_ids must be on one device")
     if kv_offsets.shape != (B * nh * nc + 1,):
         raise ValueError("kv_offsets must have B*heads*Nc + 1 entries")
 
@@ -152,10 +168,11 @@ def block_sparse_attn_varlen(q, k, v, gate_c, gate_f, grid, kv_offsets, kv_ids, 
     saved = _workspace(lib.vsa_saved_bytes(B, nh, D, T, H, W), q.device) if save else None
     wsb = lib.vsa_forward_workspace_bytes(B, nh, D, T, H, W, dt)
     ws = _workspace(wsb, q.device)
-    st = lib.block_sparse_attn_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(gate_c), _ptr(gate_f),
-                                      B, nh, D, T, H, W, _ptr(kv_offsets), _ptr(kv_ids),
-                                      int(kv_ids.numel()), dt, _ptr(out), _ptr(saved),
-                                      _ptr(ws), wsb, _stream())
+    with _on(q) as stream:
+        st = lib.block_sparse_attn_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(gate_c), _ptr(gate_f),
+                                          B, nh, D, T, H, W, _ptr(kv_offsets), _ptr(kv_ids),
+                                          int(kv_ids.numel()), dt, _ptr(out), _ptr(saved),
+                                          _ptr(ws), wsb, stream)
     _lib.check("block_sparse_attn_varlen", st)
     return out, saved
 
@@ -177,9 +194,10 @@ def vsa_forward_mass(q, k, v, gate_c, gate_f, grid, mass, k_min, k_max, save=Fal
     saved = _workspace(lib.vsa_saved_bytes(B, nh, D, T, H, W), q.device) if save else None
     wsb = lib.vsa_forward_mass_workspace_bytes(B, nh, D, T, H, W, dt, int(k_max))
     ws = _workspace(wsb, q.device)
-    st = lib.vsa_forward_mass(_ptr(q), _ptr(k), _ptr(v), _ptr(gate_c), _ptr(gate_f),
-                              B, nh, D, T, H, W, float(mass), int(k_min), int(k_max), dt,
-                              _ptr(out), _ptr(offs), _ptr(ids), _ptr(saved), _ptr(ws), wsb, _stream())
+    with _on(q) as stream:
+        st = lib.vsa_forward_mass(_ptr(q), _ptr(k), _ptr(v), _ptr(gate_c), _ptr(gate_f),
+                                  B, nh, D, T, H, W, float(mass), int(k_min), int(k_max), dt,
+                                  _ptr(out), _ptr(offs), _ptr(ids), _ptr(saved), _ptr(ws), wsb, stream)
     _lib.check("vsa_forward_mass", st)
     return out, offs, ids[:int(offs[-1].item())] if trim else ids, saved
 
@@ -190,11 +208,11 @@ def vsa_backward(q, k, v, gate_c, gate_f, dout, sel, saved, grid, validate=False
     validate checks a caller-made sel first (vsa_forward's own needs none)."""
     lib = _lib.load()
     B, N, nh, D, T, H, W, dt = _check_inputs(q, k, v, gate_c, gate_f, grid)
-    _need(dout, "dout", q.dtype, shape=q.shape)
+    _need(dout, "dout", q.dtype, shape=q.shape, device=q.device)
     nc = N // 64
     if sel.dim() != 4 or tuple(sel.shape[:3]) != (B, nh, nc):
         raise ValueError("sel must be [B, heads, Nc, topk]")
-    _need(sel, "sel", torch.int32)
+    _need(sel, "sel", torch.int32, device=q.device)
     if validate:
         _require_valid(sel, B * nh * nc, nc, topk=sel.shape[-1])
     _need(saved, "saved", torch.uint8, min_numel=int(lib.vsa_saved_bytes(B, nh, D, T, H, W)))
@@ -204,9 +222,10 @@ def vsa_backward(q, k, v, gate_c, gate_f, dout, sel, saved, grid, validate=False
              torch.empty(gate_f.shape, dtype=torch.float32, device=q.device)]
     wsb = lib.vsa_backward_workspace_bytes(B, nh, D, T, H, W, dt, int(sel.numel()))
     ws = _workspace(wsb, q.device)
-    st = lib.vsa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(gate_c), _ptr(gate_f), _ptr(dout),
-                          _ptr(sel), _ptr(saved), B, nh, D, T, H, W, topk, dt,
-                          *[_ptr(g) for g in grads], _ptr(ws), wsb, _stream())
+    with _on(q) as stream:
+        st = lib.vsa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(gate_c), _ptr(gate_f), _ptr(dout),
+                              _ptr(sel), _ptr(saved), B, nh, D, T, H, W, topk, dt,
+                              *[_ptr(g) for g in grads], _ptr(ws), wsb, stream)
     _lib.check("vsa_backward", st)
     return tuple(grads)
 
@@ -220,7 +239,7 @@ def block_sparse_attn_varlen_backward(q, k, v, gate_c, gate_f, dout, kv_offsets,
     _check_lists(kv_offsets, kv_ids, B, nh, N // 64)
     if validate:
         _require_valid(kv_ids, B * nh * (N // 64), N // 64, kv_offsets=kv_offsets)
-    _need(dout, "dout", q.dtype, shape=q.shape)
+    _need(dout, "dout", q.dtype, shape=q.shape, device=q.device)
     _need(saved, "saved", torch.uint8, min_numel=int(lib.vsa_saved_bytes(B, nh, D, T, H, W)))
     grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
              torch.empty(gate_c.shape, dtype=torch.float32, device=q.device),
@@ -228,10 +247,11 @@ def block_sparse_attn_varlen_backward(q, k, v, gate_c, gate_f, dout, kv_offsets,
     n = int(kv_ids.numel())
     wsb = lib.vsa_backward_workspace_bytes(B, nh, D, T, H, W, dt, n)
     ws = _workspace(wsb, q.device)
-    st = lib.block_sparse_attn_varlen_backward(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(gate_c), _ptr(gate_f), _ptr(dout),
-        _ptr(kv_offsets), _ptr(kv_ids), n, _ptr(saved), B, nh, D, T, H, W, dt,
-        *[_ptr(g) for g in grads], _ptr(ws), wsb, _stream())
+    with _on(q) as stream:
+        st = lib.block_sparse_attn_varlen_backward(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(gate_c), _ptr(gate_f), _ptr(dout),
+            _ptr(kv_offsets), _ptr(kv_ids), n, _ptr(saved), B, nh, D, T, H, W, dt,
+            *[_ptr(g) for g in grads], _ptr(ws), wsb, stream)
     _lib.check("block_sparse_attn_varlen_backward", st)
     return tuple(grads)
 
@@ -249,8 +269,9 @@ def vsa_cube_permute_pool(q, k, v, grid, with_q_tiles=True):
     kp = torch.empty((B, nh, nc, 64, D), dtype=q.dtype, device=q.device)
     vp = torch.empty((B, nh, nc, 64, D), dtype=q.dtype, device=q.device)
     pooled = [torch.empty((B, nh, nc, D), dtype=torch.float32, device=q.device) for _ in range(3)]
-    st = lib.vsa_cube_permute_pool(_ptr(q), _ptr(k), _ptr(v), B, nh, D, *grid, dt,
-                                   _ptr(qp), _ptr(kp), _ptr(vp), *[_ptr(p) for p in pooled], _stream())
+    with _on(q) as stream:
+        st = lib.vsa_cube_permute_pool(_ptr(q), _ptr(k), _ptr(v), B, nh, D, *grid, dt,
+                                       _ptr(qp), _ptr(kp), _ptr(vp), *[_ptr(p) for p in pooled], stream)
     _lib.check("vsa_cube_permute_pool", st)
     return (qp, kp, vp, *pooled)
 
@@ -264,8 +285,9 @@ def vsa_cube_max_pool(q, k, v, grid):
     T, H, W = grid
     nc = N // 64
     pooled = [torch.empty((B, nh, nc, D), dtype=torch.float32, device=q.device) for _ in range(3)]
-    st = lib.vsa_cube_max_pool(_ptr(q), _ptr(k), _ptr(v), B, nh, D, T, H, W, _DT[q.dtype],
-                               *[_ptr(t) for t in pooled], _stream())
+    with _on(q) as stream:
+        st = lib.vsa_cube_max_pool(_ptr(q), _ptr(k), _ptr(v), B, nh, D, T, H, W, _DT[q.dtype],
+                                   *[_ptr(t) for t in pooled], stream)
     _lib.check("vsa_cube_max_pool", st)
     return tuple(pooled)
 
@@ -277,13 +299,14 @@ def vsa_coarse_topk(qc, kc, vc, topk, input_dtype=torch.float32):
     (as the forward does for such inputs)."""
     lib = _lib.load()
     for name, t in (("qc", qc), ("kc", kc), ("vc", vc)):
-        _need(t, name, torch.float32, shape=qc.shape)
+        _need(t, name, torch.float32, shape=qc.shape, device=qc.device)
     B, nh, nc, D = qc.shape
     oc = torch.empty_like(qc)
     lse = torch.empty((B, nh, nc), dtype=torch.float32, device=qc.device)
     sel = torch.empty((B, nh, nc, topk), dtype=torch.int32, device=qc.device) if topk > 0 else None
-    st = lib.vsa_coarse_topk(_ptr(qc), _ptr(kc), _ptr(vc), B, nh, D, nc, topk,
-                             _DT[input_dtype], _ptr(oc), _ptr(lse), _ptr(sel), _stream())
+    with _on(qc) as stream:
+        st = lib.vsa_coarse_topk(_ptr(qc), _ptr(kc), _ptr(vc), B, nh, D, nc, topk,
+                                 _DT[input_dtype], _ptr(oc), _ptr(lse), _ptr(sel), stream)
     _lib.check("vsa_coarse_topk", st)
     return oc, lse, sel
 
@@ -294,15 +317,16 @@ def vsa_coarse_select_mass(qc, kc, vc, mass, k_min, k_max, input_dtype=torch.flo
     is ids[..., :counts[r]] (ascending)."""
     lib = _lib.load()
     for name, t in (("qc", qc), ("kc", kc), ("vc", vc)):
-        _need(t, name, torch.float32, shape=qc.shape)
+        _need(t, name, torch.float32, shape=qc.shape, device=qc.device)
     B, nh, nc, D = qc.shape
     oc = torch.empty_like(qc)
     lse = torch.empty((B, nh, nc), dtype=torch.float32, device=qc.device)
     counts = torch.empty((B, nh, nc), dtype=torch.int32, device=qc.device)
     ids = torch.zeros((B, nh, nc, max(int(k_max), 1)), dtype=torch.int32, device=qc.device)
-    st = lib.vsa_coarse_select_mass(_ptr(qc), _ptr(kc), _ptr(vc), B, nh, D, nc, float(mass),
-                                    int(k_min), int(k_max), _DT[input_dtype], _ptr(oc), _ptr(lse),
-                                    _ptr(counts), _ptr(ids), _stream())
+    with _on(qc) as stream:
+        st = lib.vsa_coarse_select_mass(_ptr(qc), _ptr(kc), _ptr(vc), B, nh, D, nc, float(mass),
+                                        int(k_min), int(k_max), _DT[input_dtype], _ptr(oc), _ptr(lse),
+                                        _ptr(counts), _ptr(ids), stream)
     _lib.check("vsa_coarse_select_mass", st)
     return oc, lse, counts, ids
 
@@ -313,12 +337,13 @@ def pack_lists(counts, ids_padded):
     lib = _lib.load()
     k_max = ids_padded.shape[-1]
     n_rows = counts.numel()
-    _need(counts, "counts", torch.int32)
-    _need(ids_padded, "ids_padded", torch.int32, numel=n_rows * k_max)
+    _need(counts, "counts", torch.int32, device=counts.device)
+    _need(ids_padded, "ids_padded", torch.int32, numel=n_rows * k_max, device=counts.device)
     offs = torch.empty(n_rows + 1, dtype=torch.int32, device=counts.device)
     ids = torch.empty(max(n_rows * k_max, 1), dtype=torch.int32, device=counts.device)
-    st = lib.vsa_pack_lists(_ptr(counts), _ptr(ids_padded), n_rows, k_max, _ptr(offs), _ptr(ids),
-                            _stream())
+    with _on(counts) as stream:
+        st = lib.vsa_pack_lists(_ptr(counts), _ptr(ids_padded), n_rows, k_max, _ptr(offs), _ptr(ids),
+                                stream)
     _lib.check("vsa_pack_lists", st)
     return offs, ids
 
@@ -331,27 +356,28 @@ def vsa_fine_forward(q, kp, vp, oc, gate_c, gate_f, grid, kv_ids, topk=0, kv_off
     lib = _lib.load()
     B, N, nh, D, T, H, W, dt = _check_inputs(q, q, q, gate_c, gate_f, grid)
     nc = N // 64
-    _need(kp, "kp", q.dtype, shape=(B, nh, nc, 64, D))
-    _need(vp, "vp", q.dtype, shape=(B, nh, nc, 64, D))
-    _need(oc, "oc", torch.float32, shape=(B, nh, nc, D))
-    _need(kv_ids, "kv_ids", torch.int32)
+    _need(kp, "kp", q.dtype, shape=(B, nh, nc, 64, D), device=q.device)
+    _need(vp, "vp", q.dtype, shape=(B, nh, nc, 64, D), device=q.device)
+    _need(oc, "oc", torch.float32, shape=(B, nh, nc, D), device=q.device)
+    _need(kv_ids, "kv_ids", torch.int32, device=q.device)
     if kv_offsets is not None:
-        _need(kv_offsets, "kv_offsets", torch.int32, numel=B * nh * nc + 1)
+        _need(kv_offsets, "kv_offsets", torch.int32, numel=B * nh * nc + 1, device=q.device)
     elif kv_ids.numel() != B * nh * nc * topk:
         raise ValueError("kv_ids must hold B*heads*Nc*topk ids")
     if order is not None:
-        _need(order, "order", torch.int32, numel=B * nh * nc)
+        _need(order, "order", torch.int32, numel=B * nh * nc, device=q.device)
     if out is None:
         out = torch.empty_like(q)
     else:
-        _need(out, "out", q.dtype, shape=q.shape)
+        _need(out, "out", q.dtype, shape=q.shape, device=q.device)
     lse = of = None
     if save:
         lse = torch.empty((B, nh, N), dtype=torch.float32, device=q.device)
         of = torch.empty((B, nh, N, D), dtype=torch.float32, device=q.device)
-    st = lib.vsa_fine_forward(_ptr(q), _ptr(kp), _ptr(vp), _ptr(oc), _ptr(gate_c), _ptr(gate_f),
-                              B, nh, D, *grid, _ptr(kv_offsets), _ptr(kv_ids), int(kv_ids.numel()), topk,
-                              _DT[q.dtype], _ptr(out), _ptr(lse), _ptr(of), _ptr(order), _stream())
+    with _on(q) as stream:
+        st = lib.vsa_fine_forward(_ptr(q), _ptr(kp), _ptr(vp), _ptr(oc), _ptr(gate_c), _ptr(gate_f),
+                                  B, nh, D, *grid, _ptr(kv_offsets), _ptr(kv_ids), int(kv_ids.numel()), topk,
+                                  _DT[q.dtype], _ptr(out), _ptr(lse), _ptr(of), _ptr(order), stream)
     _lib.check("vsa_fine_forward", st)
     return out, lse, of
 
@@ -360,14 +386,14 @@ def vsa_fine_order(kv_ids, B, heads, n_cubes, topk=0, kv_offsets=None):
     """Processing order for the fine stage (each (b, h)'s query cubes sorted
     by the middle entry of their list).  Returns int32 [B * heads * Nc]."""
     lib = _lib.load()
-    _need(kv_ids, "kv_ids", torch.int32)
+    _need(kv_ids, "kv_ids", torch.int32, device=kv_ids.device)
     if kv_offsets is not None:
-        _need(kv_offsets, "kv_offsets", torch.int32, numel=B * heads * n_cubes + 1)
+        _need(kv_offsets, "kv_offsets", torch.int32, numel=B * heads * n_cubes + 1, device=kv_ids.device)
     elif kv_ids.numel() != B * heads * n_cubes * topk:
         raise ValueError("kv_ids must hold B*heads*Nc*topk ids")
     order = torch.empty(B * heads * n_cubes, dtype=torch.int32, device=kv_ids.device)
-    st = lib.vsa_fine_order(_ptr(kv_offsets), _ptr(kv_ids), int(kv_ids.numel()), topk, B, heads,
-                            n_cubes, _ptr(order),
-                            _stream())
+    with _on(kv_ids) as stream:
+        st = lib.vsa_fine_order(_ptr(kv_offsets), _ptr(kv_ids), int(kv_ids.numel()), topk, B, heads,
+                                n_cubes, _ptr(order), stream)
     _lib.check("vsa_fine_order", st)
     return order
