@@ -65,7 +65,10 @@ __global__ __launch_bounds__(256) void permute_pool_kernel(PermutePoolPtrs p, in
     __builtin_memcpy(vals, &raw, 16);
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] = MAXP ? fmaxf(acc[e], to_f32(vals[e])) : acc[e] + to_f32(vals[e]);
-    if (nat) *reinterpret_cast<u32x4*>(nat + tile + (int64_t)s * D + ch * EPC) = raw;
+    // Non-temporal store too: the tile is read back by the fine stage only
+    // after every tile is written, far beyond what the L2 keeps (the permute
+    // measured 0.171 against 0.183 ms at 61440 tokens and 12 heads).
+    if (nat) __builtin_nontemporal_store(raw, reinterpret_cast<u32x4*>(nat + tile + (int64_t)s * D + ch * EPC));
   }
 
   if (pooled) {
