@@ -14,9 +14,10 @@
 //                   Delta = dOf.O_fine, dOf = g_f dO (bf16 cube tile),
 //                   dOc = sum over the cube of g_c dO and Delta_c = dOc.Oc
 //   gemm_f32 / coarse_softmax_grad
-//                   coarse backward on the means: S, dP by fp32 MFMA GEMMs,
-//                   P = exp(S - lse_c), dS = P (dP - Delta_c), then
-//                   dQc = s dS Kc, dKc = s dS^T Qc, dVc = P^T dOc
+//                   coarse backward on the means: S, dP by fp32 MFMA GEMMs
+//                   (one launch), P = exp(S - lse_c), dS = P (dP - Delta_c),
+//                   then dQc = s dS Kc, and dKc = s dS^T Qc with
+//                   dVc = P^T dOc (one launch)
 //   transpose_scatter / transpose_rank
 //                   for every key cube, the ascending list of query cubes
 //                   that selected it (counting sort per (b, h), then a rank
@@ -191,6 +192,15 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
 // ---------------------------------------------------------------- coarse
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
+// Up to two products of one shape per launch (operands of product p in
+// GemmPair slot p; blockIdx.z = p * batch + z).
+struct GemmPair {
+  const float* A[2];
+  const float* B[2];
+  float* C[2];
+  float alpha[2];
+};
+
 // C[z] = alpha * op(A[z]) * op(B[z]) for z < batch, fp32, row-major.
 // op(A) is M x K (TA: A stored K x M); op(B) is K x N (TB: B stored N x K).
 // 64 x 64 output tile per workgroup, v_mfma_f32_16x16x4f32, each wave owns a
@@ -200,13 +210,17 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 // is multiplied, so their latency overlaps the MFMAs.
 template <bool TA, bool TB>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(
-    const float* __restrict__ A, int lda, int64_t sA, const float* __restrict__ B, int ldb, int64_t sB,
-    float* __restrict__ C, int ldc, int64_t sC, int M, int N, int K, float alpha) {
+    GemmPair g, int batch, int lda, int64_t sA, int ldb, int64_t sB, int ldc, int64_t sC, int M, int N,
+    int K) {
   constexpr int KC = 32;
   __shared__ float As[KC][64 + 4];
   __shared__ float Bs[KC][64 + 4];
-  const int z = blockIdx.z;
-  A += z * sA; B += z * sB; C += z * sC;
+  const int pr = (int)blockIdx.z >= batch ? 1 : 0;
+  const int z = (int)blockIdx.z - pr * batch;
+  const float* __restrict__ A = g.A[pr] + z * sA;
+  const float* __restrict__ B = g.B[pr] + z * sB;
+  float* __restrict__ C = g.C[pr] + z * sC;
+  const float alpha = g.alpha[pr];
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, lg = lane >> 4;
@@ -946,12 +960,17 @@ __global__ __launch_bounds__(256) void fine_bwd_dkdv_f32_kernel(
   }
 }
 
+// n_prod (1 or 2) batched products of one shape in one launch.
 template <bool TA, bool TB>
-hipError_t gemm(const float* A, int lda, int64_t sA, const float* B, int ldb, int64_t sB,
-                float* C, int ldc, int64_t sC, int M, int N, int K, float alpha, int batch,
-                hipStream_t st) {
-  dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64), (unsigned)batch);
-  gemm_f32_kernel<TA, TB><<<grid, 256, 0, st>>>(A, lda, sA, B, ldb, sB, C, ldc, sC, M, N, K, alpha);
+hipError_t gemm(const GemmPair& g, int n_prod, int lda, int64_t sA, int ldb, int64_t sB, int ldc,
+                int64_t sC, int M, int N, int K, int batch, hipStream_t st) {
+  if (n_prod == 2 && 2 * batch > 65535) {  // past the grid's z limit: one launch per product
+    const GemmPair second{{g.A[1], nullptr}, {g.B[1], nullptr}, {g.C[1], nullptr}, {g.alpha[1], 0.f}};
+    const hipError_t e = gemm<TA, TB>(g, 1, lda, sA, ldb, sB, ldc, sC, M, N, K, batch, st);
+    return e != hipSuccess ? e : gemm<TA, TB>(second, 1, lda, sA, ldb, sB, ldc, sC, M, N, K, batch, st);
+  }
+  dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64), (unsigned)(n_prod * batch));
+  gemm_f32_kernel<TA, TB><<<grid, 256, 0, st>>>(g, batch, lda, sA, ldb, sB, ldc, sC, M, N, K);
   return hipGetLastError();
 }
 
@@ -974,14 +993,17 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t st) {
   VSA_TRY(hipGetLastError());
   // coarse backward on the cube means
   const int64_t sq = (int64_t)nc * D, ss = (int64_t)nc * nc;
-  VSA_TRY((gemm<false, true>(a.qc, D, sq, a.kc, D, sq, a.S, nc, ss, nc, nc, D, scale, BH, st)));
-  VSA_TRY((gemm<false, true>(a.doc, D, sq, a.vc, D, sq, a.dP, nc, ss, nc, nc, D, 1.0f, BH, st)));
+  // S = s Qc Kc^T and dP = dOc Vc^T in one launch
+  VSA_TRY((gemm<false, true>(GemmPair{{a.qc, a.doc}, {a.kc, a.vc}, {a.S, a.dP}, {scale, 1.0f}}, 2,
+                             D, sq, D, sq, nc, ss, nc, nc, D, BH, st)));
   const int64_t rows = (int64_t)BH * nc;
   coarse_softmax_grad_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(a.S, a.dP, a.lse_c, a.deltac, nc, rows);
   VSA_TRY(hipGetLastError());
-  VSA_TRY((gemm<false, false>(a.dP, nc, ss, a.kc, D, sq, a.dqc, D, sq, nc, D, nc, scale, BH, st)));
-  VSA_TRY((gemm<true, false>(a.dP, nc, ss, a.qc, D, sq, a.dkc, D, sq, nc, D, nc, scale, BH, st)));
-  VSA_TRY((gemm<true, false>(a.S, nc, ss, a.doc, D, sq, a.dvc, D, sq, nc, D, nc, 1.0f, BH, st)));
+  // dQc = s dS Kc; then dKc = s dS^T Qc and dVc = P^T dOc in one launch
+  VSA_TRY((gemm<false, false>(GemmPair{{a.dP, nullptr}, {a.kc, nullptr}, {a.dqc, nullptr}, {scale, 0.f}},
+                              1, nc, ss, D, sq, D, sq, nc, D, nc, BH, st)));
+  VSA_TRY((gemm<true, false>(GemmPair{{a.dP, a.S}, {a.qc, a.doc}, {a.dkc, a.dvc}, {scale, 1.0f}}, 2,
+                             nc, ss, D, sq, D, sq, nc, D, nc, BH, st)));
   // transposed selection
   transpose_scatter_kernel<<<(unsigned)BH, 256, sizeof(int32_t) * (4 * nc + 4), st>>>(
       a.offs, a.ids, a.topk, a.n_ids, nc, a.tr_offs, a.tr_order, a.tr_tmp);
