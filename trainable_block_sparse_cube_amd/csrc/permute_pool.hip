@@ -20,7 +20,7 @@
 
 namespace vsa {
 
-template <typename T, int D, bool MAXP>
+template <typename T, int D, bool MAXP, bool NT>
 __global__ __launch_bounds__(256) void permute_pool_kernel(PermutePoolPtrs p, int nh, int Tg, int Hg, int Wg,
                                                            bool packed_kv) {
   constexpr int EPC = 16 / sizeof(T);     // elements per 16-byte chunk
@@ -65,10 +65,13 @@ __global__ __launch_bounds__(256) void permute_pool_kernel(PermutePoolPtrs p, in
     __builtin_memcpy(vals, &raw, 16);
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] = MAXP ? fmaxf(acc[e], to_f32(vals[e])) : acc[e] + to_f32(vals[e]);
-    // Non-temporal store too: the tile is read back by the fine stage only
-    // after every tile is written, far beyond what the L2 keeps (the permute
-    // measured 0.171 against 0.183 ms at 61440 tokens and 12 heads).
-    if (nat) __builtin_nontemporal_store(raw, reinterpret_cast<u32x4*>(nat + tile + (int64_t)s * D + ch * EPC));
+    // Tiles that together overflow the last-level cache (MALL) are written
+    // with non-temporal stores, the others with plain ones (see the launch).
+    if (nat) {
+      u32x4* dst = reinterpret_cast<u32x4*>(nat + tile + (int64_t)s * D + ch * EPC);
+      if constexpr (NT) __builtin_nontemporal_store(raw, dst);
+      else *dst = raw;
+    }
   }
 
   if (pooled) {
@@ -107,6 +110,13 @@ __global__ __launch_bounds__(256) void permute_pool_kernel(PermutePoolPtrs p, in
   }
 }
 
+// Tile bytes a launch writes above which the stores bypass the caches: the
+// 256 MB MALL of MI355X.  Measured on the permute stage alone: 61440 tokens,
+// 12 heads, K and V tiles (378 MB): 0.174 ms non-temporal against 0.185
+// plain; 16384 tokens (100 and 200 MB): 0.051 against 0.043 and 0.092
+// against 0.079 ms; 300 MB (Q, K and V at B = 2): a tie.
+constexpr double kNonTemporalTileBytes = 256.0 * 1024 * 1024;
+
 template <typename T, int D>
 static hipError_t launch_pp(const PermutePoolArgs& a, hipStream_t st) {
   const int nc = (a.T / 4) * (a.H / 4) * (a.W / 4);
@@ -114,10 +124,15 @@ static hipError_t launch_pp(const PermutePoolArgs& a, hipStream_t st) {
   if (a.max_pool) {
     PermutePoolPtrs p = a.p;
     p.nat[0] = p.nat[1] = p.nat[2] = nullptr;  // pooled values only
-    permute_pool_kernel<T, D, true><<<grid, 256, 0, st>>>(p, a.heads, a.T, a.H, a.W, false);
-  } else {
-    permute_pool_kernel<T, D, false><<<grid, 256, 0, st>>>(a.p, a.heads, a.T, a.H, a.W, a.packed_kv);
+    permute_pool_kernel<T, D, true, false><<<grid, 256, 0, st>>>(p, a.heads, a.T, a.H, a.W, false);
+    return hipGetLastError();
   }
+  const int n_tiles = (a.p.nat[0] != nullptr) + (a.p.nat[1] != nullptr) + (a.p.nat[2] != nullptr);
+  const double tile_bytes = (double)n_tiles * a.B * a.heads * nc * kCubeTokens * D * sizeof(T);
+  if (tile_bytes > kNonTemporalTileBytes)
+    permute_pool_kernel<T, D, false, true><<<grid, 256, 0, st>>>(a.p, a.heads, a.T, a.H, a.W, a.packed_kv);
+  else
+    permute_pool_kernel<T, D, false, false><<<grid, 256, 0, st>>>(a.p, a.heads, a.T, a.H, a.W, a.packed_kv);
   return hipGetLastError();
 }
 
