@@ -259,7 +259,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* gc, c
 // kept in scratch_ptr, and only that address is handed to kernels.
 constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
 constexpr int kMaxDevices = 64;
-__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 std::mutex scratch_mu;
 void* scratch_ptr[kMaxDevices] = {};
 
