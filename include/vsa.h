@@ -188,8 +188,10 @@ int vsa_forward_mass(const void* q, const void* k, const void* v,
  * cores with fp32 accumulation; VSA_F32 uses fp32 arithmetic throughout
  * (plain vector code, for accuracy rather than speed).  workspace:
  * vsa_backward_workspace_bytes with n_list_entries = B*heads*Nc*topk
- * (resp. the varlen total).  With VSA_VALIDATE=1 the key lists (sel_idx
- * included) are checked first as in vsa_validate_lists.
+ * (resp. the varlen total); for bf16 it includes one 8 KB dS tile per list
+ * entry (the dK/dV pass stores dS for the dQ pass), e.g. 1.6 GB at B = 2,
+ * 12 heads, 16384 tokens, top-K 32.  With VSA_VALIDATE=1 the key lists
+ * (sel_idx included) are checked first as in vsa_validate_lists.
  */
 int vsa_backward(const void* q, const void* k, const void* v,
                  const void* gate_c, const void* gate_f, const void* dout,

@@ -23,13 +23,16 @@
 //                   that selected it (counting sort per (b, h), then a rank
 //                   sort of each list, one wave per list)
 //   fine_bwd_dkdv   key-stationary: one workgroup per key cube accumulates
-//                   dK and dV over the query cubes that selected it
+//                   dK and dV over the query cubes that selected it, and
+//                   (bf16) stores each pair's dS tile
 //   fine_bwd_dq     query-stationary: one workgroup per query cube
-//                   accumulates dQ over its selected key cubes
+//                   accumulates dQ over its selected key cubes (bf16: from
+//                   the stored dS tiles, one product per pair)
 // The last two write raster-order gradients with the coarse share added.
-// Both stream their per-pair tiles (Q and dOf, resp. K and V; 16 KB each
-// at D = 128, natural [token][D] layout) with global->LDS copies, double
-// buffered, and take every transposed operand from transposing LDS reads.
+// Both stream their per-pair tiles (Q and dOf, resp. K and the 8 KB dS
+// tile, or K and V for fp32; 16 KB each at D = 128, natural row-major
+// layout) with global->LDS copies, double buffered, and take every
+// transposed operand from transposing LDS reads.
 // Each wave raises its issue priority for its two MFMA bursts per tile
 // (s_setprio 1, back to 0 for the softmax arithmetic), so a SIMD's matrix
 // unit is fed first while the other resident wave runs its VALU work; the
@@ -343,7 +346,8 @@ __device__ void block_exclusive_scan(const int32_t* in, int n, int32_t* out, int
 
 // transpose_scatter: one workgroup per (b, h): counts (LDS atomics), an
 // exclusive scan into tr_offs, then a scatter of the query cube ids into
-// `tmp`, each list in arbitrary order.  It also writes tr_order, the key
+// `tmp`, each list in arbitrary order, and (tmp_pos non-null) of each
+// entry's index in `ids` into tmp_pos at the same slot.  It also writes tr_order, the key
 // cubes of (b, h) by list length, longest first: the dK/dV kernel takes
 // them in that order, so that the longest lists start first and the
 // workgroups running together have lists of similar length (their sweeps
@@ -351,7 +355,8 @@ __device__ void block_exclusive_scan(const int32_t* in, int n, int32_t* out, int
 // among equal lengths is arbitrary; results do not depend on it.
 __global__ __launch_bounds__(256) void transpose_scatter_kernel(
     const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk, int64_t n_ids,
-    int nc, int32_t* __restrict__ tr_offs, int32_t* __restrict__ tr_order, int32_t* __restrict__ tmp) {
+    int nc, int32_t* __restrict__ tr_offs, int32_t* __restrict__ tr_order, int32_t* __restrict__ tmp,
+    int32_t* __restrict__ tmp_pos) {
   // LDS: cnt [nc] (counts, then cursors), start [nc + 1], hist [nc + 1],
   // hpos [nc + 2]
   extern __shared__ int32_t cnt[];
@@ -413,7 +418,10 @@ __global__ __launch_bounds__(256) void transpose_scatter_kernel(
           // rows of well-formed offsets tile [base, base + total) exactly;
           // others may not, and what would not fit is dropped
           const int pos = atomicAdd(&cnt[jj[u]], 1);
-          if (pos < total) tmp[base + pos] = c;
+          if (pos < total) {
+            tmp[base + pos] = c;
+            if (tmp_pos) tmp_pos[base + pos] = (int32_t)(e + u);
+          }
         }
     }
   }
@@ -423,10 +431,12 @@ __global__ __launch_bounds__(256) void transpose_scatter_kernel(
 // lane counts the entries that precede its own, smaller values first and
 // equal values by position (a query cube that lists a key cube twice
 // appears twice), through readlane broadcasts.  Ranks are therefore
-// distinct and every slot of the list is written.
+// distinct and every slot of the list is written.  With tr_pos, each
+// entry's index in `ids` moves along with it.
 __global__ __launch_bounds__(256) void transpose_rank_kernel(
-    const int32_t* __restrict__ tr_offs, const int32_t* __restrict__ tmp, int64_t n_lists,
-    int64_t n_ids, int32_t* __restrict__ tr_ids) {
+    const int32_t* __restrict__ tr_offs, const int32_t* __restrict__ tmp,
+    const int32_t* __restrict__ tmp_pos, int64_t n_lists, int64_t n_ids,
+    int32_t* __restrict__ tr_ids, int32_t* __restrict__ tr_pos) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= n_lists) return;
@@ -446,7 +456,10 @@ __global__ __launch_bounds__(256) void transpose_rank_kernel(
         rank += w < v || (w == v && k0 + i < idx);
       }
     }
-    if (idx < n) tr_ids[s0 + rank] = v;
+    if (idx < n) {
+      tr_ids[s0 + rank] = v;
+      if (tr_pos) tr_pos[s0 + rank] = tmp_pos[s0 + idx];
+    }
   }
 }
 
@@ -466,9 +479,9 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(
     const bf16* __restrict__ qp, const bf16* __restrict__ kp, const bf16* __restrict__ vp,
     const bf16* __restrict__ dofp, const float* __restrict__ lse_f, const float* __restrict__ delta,
     const int32_t* __restrict__ tr_offs, const int32_t* __restrict__ tr_order,
-    const int32_t* __restrict__ tr_ids, int64_t n_ids, const float* __restrict__ dkc,
-    const float* __restrict__ dvc, int nh, int nc, int Hg, int Wg, float scale, int n_logical,
-    bf16* __restrict__ dk, bf16* __restrict__ dv) {
+    const int32_t* __restrict__ tr_ids, const int32_t* __restrict__ tr_pos, int64_t n_ids,
+    const float* __restrict__ dkc, const float* __restrict__ dvc, int nh, int nc, int Hg, int Wg,
+    float scale, int n_logical, bf16* __restrict__ dk, bf16* __restrict__ dv, bf16* __restrict__ ds) {
   constexpr int KS = D / 16, MD = D / 32, TILE_CH = 64 * D / 8;
   // Tile parity buffers: separate arrays picked at run time, so that the
   // compiler adds no waits of its own for the global->LDS copies.
@@ -576,6 +589,21 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(
         dsB[r >> 3][r & 7] = (bf16)(p * (da[r] - d4[i]));
       }
     }
+    // this wave's dS block, kept for the dQ pass: the pair's 64 x 64 tile
+    // (entry tr_pos of the key lists) as dS^T, rows = keys, row-major; this
+    // lane's key row, queries 32qh + 8a + 4hf .. +4 per 8-byte store
+    {
+      const int64_t ent = tr_pos[e0 + it];
+      if ((uint64_t)ent < (uint64_t)n_ids) {
+        bf16* drow = ds + ent * 4096 + (int64_t)(32 * kh + ql) * 64 + 32 * qh + 4 * hf;
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const bf16x8& src = dsB[a4 >> 1];
+          const int e = 4 * (a4 & 1);
+          *reinterpret_cast<bf16x4*>(drow + 8 * a4) = bf16x4{src[e], src[e + 1], src[e + 2], src[e + 3]};
+        }
+      }
+    }
 #pragma unroll
     for (int g = 0; g < 2; ++g) xch[wave][g][lane] = qh ? pB[g] : dsB[g];
     lds_barrier();
@@ -618,141 +646,99 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dkdv_kernel(
     }
 }
 
-// dQ of one query cube.  4 waves; wave w: key half kh = w & 1 of every
-// selected key tile, query half qh = w >> 1 (queries 32qh .. +32):
-//   S^T = K Q^T, dP^T = V dOf^T    (m = 32 keys, n = 32 queries, k = d)
-//   dS^T = P^T (dP^T - Delta)
+// dQ of one query cube from the dS tiles the dK/dV pass stored (one 64 x 64
+// bf16 tile per list entry, as dS^T: rows = keys).  4 waves; wave w: key
+// half kh = w & 1 of every selected key tile, query half qh = w >> 1:
 //   dQ^T += K^T dS^T               (m = d, n = queries, k = 32 keys)
-// K^T is read transposed from the natural K tile.  The exact dS sums to
-// zero over each query's keys, so sum_j dS_j c adds nothing for any fixed
-// vector c; the computed dS does not quite (Delta comes from the forward's
-// output, whose weights were rounded to bf16), and that residue times the
-// keys' large shared component (cubes with a common mean) would dominate
-// dQ.  So dQ = sum_j dS_j K_j - (sum_j dS_j) c0, with c0 the mean of the
-// first listed key cube and both sums in fp32; dS enters the product as a
-// bf16 pair (hi + lo, both MFMA operands) so that its own rounding leaves no
-// such residue.  The two key halves are summed at the end.
+// with K^T and dS^T both read transposed from their natural tiles, which
+// stream in together (global->LDS, double buffered).  As in the dK/dV
+// pass's products, dS enters as its bf16 rounding r; the exact dS rows sum
+// to zero over each query's keys, so dQ = sum_j r_j K_j - (sum_j r_j) c0,
+// with c0 the mean of the first listed key cube and the sum of the rounded
+// values taken in fp32, removes the rounding residue along the keys'
+// shared component and leaves errors of the size of r - dS times K - c0.
 template <int D>
-__global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(
-    const bf16* __restrict__ qp, const bf16* __restrict__ kp, const bf16* __restrict__ vp,
-    const bf16* __restrict__ dofp, const float* __restrict__ lse_f, const float* __restrict__ delta,
+__global__ __launch_bounds__(256, 2) void fine_bwd_dq_ds_kernel(
+    const bf16* __restrict__ kp, const bf16* __restrict__ ds,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk, int64_t n_ids,
     const float* __restrict__ dqc, const float* __restrict__ kc_mean,
     int nh, int nc, int Hg, int Wg, float scale, int n_logical, bf16* __restrict__ dq) {
-  constexpr int KS = D / 16, MD = D / 32, TILE_CH = 64 * D / 8;
+  constexpr int MD = D / 32, TILE_CH = 64 * D / 8, DS_CH = 64 * 64 / 8;
   __shared__ __align__(256) u32x4 k_lds0[TILE_CH];
   __shared__ __align__(256) u32x4 k_lds1[TILE_CH];
-  __shared__ __align__(16) u32x4 v_lds0[TILE_CH];
-  __shared__ __align__(16) u32x4 v_lds1[TILE_CH];
+  __shared__ __align__(256) u32x4 s_lds0[DS_CH];
+  __shared__ __align__(256) u32x4 s_lds1[DS_CH];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ql = lane & 31, hf = lane >> 5;
   const int kh = wave & 1, qh = wave >> 1;
-  // Logical block (b*nh + h)*nc + query cube, XCD-contiguous as in the
-  // forward fine kernel (hardware block i runs on XCD i % 8); the grid is
-  // padded to a multiple of 8.
+  // XCD-contiguous logical numbering as in the forward fine kernel
   const int per = (n_logical + 7) >> 3;
   const int blk = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
   if (blk >= n_logical) return;
   const int bh = blk / nc, c = blk - bh * nc;
   const int64_t N = (int64_t)nc * 64;
   const int64_t bh_tiles = (int64_t)bh * nc;
-  const float scale_log2 = scale * kLog2e;
   int64_t start;
   int n;
   list_range(offs, blk, topk, n_ids, &start, &n);
   const int32_t* list = ids + start;
-
   const int slot = 32 * qh + ql;
-  bf16x8 qB[KS], oB[KS];
-  {
-    const int64_t row = (bh_tiles + c) * 64 + slot;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      qB[s] = *reinterpret_cast<const bf16x8*>(qp + row * D + (D / 2) * hf + 8 * s);
-      oB[s] = *reinterpret_cast<const bf16x8*>(dofp + row * D + (D / 2) * hf + 8 * s);
-    }
-  }
-  const float lse2 = lse_f[(int64_t)bh * N + (int64_t)c * 64 + slot] * kLog2e;
-  const float del = delta[(int64_t)bh * N + (int64_t)c * 64 + slot];
+
   f32x16 acc[MD];
 #pragma unroll
   for (int m = 0; m < MD; ++m)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
-  float ssum = 0.f;  // this lane's share of sum_j dS_j
+  float ssum = 0.f;  // this lane's share of sum_j r_j
 
-  // An entry outside [0, nc) reads cube 0 and is skipped.
-  auto copy_tile = [&](int kc, int buf) {
+  // Entry `e` of the lists (key cube kc): its K tile and its dS tile.  An
+  // id outside [0, nc) reads cube 0 and is skipped.
+  auto copy_tile = [&](int64_t e, int kc, int buf) {
     kc = cube_or_0(kc, nc);
     dma_tile<D>(kp + (bh_tiles + kc) * 64 * D, buf ? k_lds1 : k_lds0, wave, lane);
-    dma_tile<D>(vp + (bh_tiles + kc) * 64 * D, buf ? v_lds1 : v_lds0, wave, lane);
+    dma_tile<64>(ds + e * 4096, buf ? s_lds1 : s_lds0, wave, lane);
   };
-  if (n > 0) copy_tile(list[0], 0);
-  const int krow = 32 * kh + ql;
-  // transposed reads of K rows 32kh .. 32kh + 31
+  if (n > 0) copy_tile(start, list[0], 0);
+  // transposed reads of rows (keys) 32kh .. 32kh + 31: of the K tile, column
+  // blocks 0 .. MD-1; of the dS^T tile, column block qh (queries 32qh ..)
   const uint32_t tr_lo = tr_offset<D>(lane, 0) + 32 * kh * D * 2;
   const uint32_t tr_hi = tr_offset<D>(lane, 1) + 32 * kh * D * 2;
+  const uint32_t sr_lo = tr_offset<64>(lane, 0) + 32 * kh * 64 * 2;
+  const uint32_t sr_hi = tr_offset<64>(lane, 1) + 32 * kh * 64 * 2;
 
   for (int it = 0; it < n; ++it) {
     const int buf = it & 1;
     const bool tile_ok = cube_ok(list[it], nc);
     wait_vmcnt<0>();
     __syncthreads();
-    if (it + 1 < n) copy_tile(list[it + 1], buf ^ 1);
+    if (it + 1 < n) copy_tile(start + it + 1, list[it + 1], buf ^ 1);
     if (!tile_ok) continue;
-    const u32x4* kb = buf ? k_lds1 : k_lds0;
-    const u32x4* vb = buf ? v_lds1 : v_lds0;
-
-    bf16x8 ka[KS], va[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      ka[s] = tile_row8<D>(kb, krow, KS * hf + s);
-      va[s] = tile_row8<D>(vb, krow, KS * hf + s);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16 sa, da;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { sa[r] = 0.f; da[r] = 0.f; }
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qB[s], sa, 0, 0, 0);
-      da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s], oB[s], da, 0, 0, 0);
-    }
-    // K^T operands (m = d, k = keys), read while the MFMAs above run
-    const uint32_t kbase = lds_addr(kb);
+    const uint32_t kbase = lds_addr(buf ? k_lds1 : k_lds0);
+    const uint32_t sbase = lds_addr(buf ? s_lds1 : s_lds0);
     bf16x8 ta[MD][2];
     tile_tr8_asm_cols<D, MD>(ta, kbase + tr_lo, kbase + tr_hi);
-    __builtin_amdgcn_s_setprio(0);
-    // this lane: query column ql, key rows 32kh + 8(r/4) + 4hf + r%4
-    bf16x8 hiB[2], loB[2];
+    bf16x8 dB[2];
+    tile_tr8_asm<64, 2>(dB, (sbase + sr_lo) ^ ((uint32_t)qh << 6), (sbase + sr_hi) ^ ((uint32_t)qh << 6));
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(sa[r], scale_log2, -lse2));
-      const float ds = p * (da[r] - del);
-      ssum += ds;
-      const bf16 hi = (bf16)ds;
-      hiB[r >> 3][r & 7] = hi;
-      loB[r >> 3][r & 7] = (bf16)(ds - (float)hi);
-    }
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ssum += (float)dB[g][e];
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int m = 0; m < MD; ++m)
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[m][g], hiB[g], acc[m], 0, 0, 0);
-        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[m][g], loB[g], acc[m], 0, 0, 0);
-      }
+      for (int g = 0; g < 2; ++g)
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[m][g], dB[g], acc[m], 0, 0, 0);
     __builtin_amdgcn_s_setprio(0);
   }
 
   ssum += swap_halves(ssum);  // over this wave's 32 keys of every tile
-  // Sum the key halves: the kh = 1 wave hands its dQ^T and dS sum to the
+  // Sum the key halves: the kh = 1 wave hands its dQ^T and r sum to the
   // kh = 0 wave of the same query half through LDS.
   __syncthreads();  // all tile reads done; the buffers are free
   float* xo = reinterpret_cast<float*>(qh ? k_lds1 : k_lds0);  // 32 q x D floats
-  float* xs = reinterpret_cast<float*>(qh ? v_lds1 : v_lds0);  // 32 q
+  float* xs = reinterpret_cast<float*>(qh ? s_lds1 : s_lds0);  // 32 q
   if (kh == 1) {
 #pragma unroll
     for (int m = 0; m < MD; ++m)
@@ -786,16 +772,6 @@ __global__ __launch_bounds__(256, 2) void fine_bwd_dq_kernel(
       *reinterpret_cast<bf16x4*>(dq + gidx * D + d0) = o;
     }
 }
-
-// ---------------------------------------------------------------- fp32
-// fp32 inputs: the same two fine kernels in plain fp32 VALU arithmetic (no
-// reduced precision anywhere), one workgroup of 256 threads per query cube
-// (dQ) or per key cube (dK, dV).  Tiles sit in LDS as fp32 rows; a row that
-// lanes read at different rows of the same column is padded by one float,
-// so those reads fall on distinct banks.  Work is split into 32-row halves
-// of the streamed tile so that everything fits in LDS at D = 128.  Each
-// pair's products are formed as in the oracle's formulas, in a fixed order,
-// so results are deterministic.
 
 // dQ of one query cube: for each selected key cube, two halves of 32 keys.
 //   phase A: thread (query i = t % 64, keys j = t / 64 + 4e, e < 8):
@@ -1006,11 +982,11 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t st) {
                              nc, ss, D, sq, D, sq, nc, D, nc, BH, st)));
   // transposed selection
   transpose_scatter_kernel<<<(unsigned)BH, 256, sizeof(int32_t) * (4 * nc + 4), st>>>(
-      a.offs, a.ids, a.topk, a.n_ids, nc, a.tr_offs, a.tr_order, a.tr_tmp);
+      a.offs, a.ids, a.topk, a.n_ids, nc, a.tr_offs, a.tr_order, a.tr_tmp, a.bf16 ? a.tr_tmp_pos : nullptr);
   VSA_TRY(hipGetLastError());
   const int64_t n_lists = (int64_t)BH * nc;
-  transpose_rank_kernel<<<(unsigned)((n_lists + 3) / 4), 256, 0, st>>>(a.tr_offs, a.tr_tmp, n_lists,
-                                                                       a.n_ids, a.tr_ids);
+  transpose_rank_kernel<<<(unsigned)((n_lists + 3) / 4), 256, 0, st>>>(
+      a.tr_offs, a.tr_tmp, a.tr_tmp_pos, n_lists, a.n_ids, a.tr_ids, a.bf16 ? a.tr_pos : nullptr);
   VSA_TRY(hipGetLastError());
   const unsigned grid = (unsigned)(BH * nc);
   if (!a.bf16) {
@@ -1029,13 +1005,12 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t st) {
   }
   fine_bwd_dkdv_kernel<D><<<((grid + 7u) / 8u) * 8u, 256, 0, st>>>(
       (const bf16*)a.qp, (const bf16*)a.kp, (const bf16*)a.vp, (const bf16*)a.dofp,
-      a.lse_f, a.delta, a.tr_offs, a.tr_order, a.tr_ids, a.n_ids, a.dkc, a.dvc, a.heads, nc, a.H, a.W,
-      scale, (int)grid, (bf16*)a.dk, (bf16*)a.dv);
+      a.lse_f, a.delta, a.tr_offs, a.tr_order, a.tr_ids, a.tr_pos, a.n_ids, a.dkc, a.dvc, a.heads, nc,
+      a.H, a.W, scale, (int)grid, (bf16*)a.dk, (bf16*)a.dv, (bf16*)a.ds);
   VSA_TRY(hipGetLastError());
-  fine_bwd_dq_kernel<D><<<((grid + 7u) / 8u) * 8u, 256, 0, st>>>(
-      (const bf16*)a.qp, (const bf16*)a.kp, (const bf16*)a.vp, (const bf16*)a.dofp,
-      a.lse_f, a.delta, a.offs, a.ids, a.topk, a.n_ids, a.dqc, a.kc, a.heads, nc, a.H, a.W, scale,
-      (int)grid, (bf16*)a.dq);
+  fine_bwd_dq_ds_kernel<D><<<((grid + 7u) / 8u) * 8u, 256, 0, st>>>(
+      (const bf16*)a.kp, (const bf16*)a.ds, a.offs, a.ids, a.topk, a.n_ids, a.dqc, a.kc, a.heads, nc,
+      a.H, a.W, scale, (int)grid, (bf16*)a.dq);
   VSA_TRY(hipGetLastError());
 #undef VSA_TRY
   return hipSuccess;

@@ -15,6 +15,7 @@ using namespace vsa;
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr size_t kDsTileBytes = 64 * 64 * 2;  // one bf16 dS tile (64 queries x 64 keys)
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Shape {
@@ -186,7 +187,8 @@ struct BwdWorkspace {
   int32_t* check;  // 2 ints: list validation counts (VSA_VALIDATE)
   void *qp, *kp, *vp, *dofp;
   float *qc, *kc, *vc, *delta, *doc, *deltac, *S, *dP, *dqc, *dkc, *dvc;
-  int32_t *tr_offs, *tr_order, *tr_ids, *tr_tmp;
+  int32_t *tr_offs, *tr_order, *tr_ids, *tr_tmp, *tr_pos, *tr_tmp_pos;
+  void* ds;  // bf16: the dS tile of every (query cube, selected key cube) entry
 };
 
 size_t bwd_ws_layout(const Shape& s, int64_t n_entries, char* base, BwdWorkspace* w) {
@@ -207,8 +209,16 @@ size_t bwd_ws_layout(const Shape& s, int64_t n_entries, char* base, BwdWorkspace
   t.dqc = (float*)take(pooled); t.dkc = (float*)take(pooled); t.dvc = (float*)take(pooled);
   t.tr_offs = (int32_t*)take(align_up(((size_t)s.B * s.heads * s.nc + 1) * sizeof(int32_t)));
   t.tr_order = (int32_t*)take(align_up((size_t)s.B * s.heads * s.nc * sizeof(int32_t)));
-  t.tr_ids = (int32_t*)take(align_up((size_t)(n_entries > 0 ? n_entries : 1) * sizeof(int32_t)));
-  t.tr_tmp = (int32_t*)take(align_up((size_t)(n_entries > 0 ? n_entries : 1) * sizeof(int32_t)));
+  const size_t per_entry = align_up((size_t)(n_entries > 0 ? n_entries : 1) * sizeof(int32_t));
+  t.tr_ids = (int32_t*)take(per_entry);
+  t.tr_tmp = (int32_t*)take(per_entry);
+  t.tr_pos = t.tr_tmp_pos = nullptr;
+  t.ds = nullptr;
+  if (s.dtype == VSA_BF16) {
+    t.tr_pos = (int32_t*)take(per_entry);
+    t.tr_tmp_pos = (int32_t*)take(per_entry);
+    t.ds = take(align_up((size_t)(n_entries > 0 ? n_entries : 1) * kDsTileBytes));
+  }
   if (w) *w = t;
   return off;
 }
@@ -246,6 +256,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* gc, c
   ba.doc = w.doc; ba.deltac = w.deltac; ba.S = w.S; ba.dP = w.dP;
   ba.dqc = w.dqc; ba.dkc = w.dkc; ba.dvc = w.dvc;
   ba.tr_offs = w.tr_offs; ba.tr_order = w.tr_order; ba.tr_ids = w.tr_ids; ba.tr_tmp = w.tr_tmp;
+  ba.tr_pos = w.tr_pos; ba.tr_tmp_pos = w.tr_tmp_pos; ba.ds = w.ds;
   ba.dq = dq; ba.dk = dk; ba.dv = dv; ba.dgc = dgc; ba.dgf = dgf;
   return hip_status(launch_backward(ba, st));
 }

@@ -114,11 +114,13 @@ struct BackwardArgs {
   const int32_t* offs;
   const int32_t* ids;
   int topk;
-  int64_t n_ids;  // entries in ids, tr_ids and tr_tmp
+  int64_t n_ids;  // entries in ids, tr_ids, tr_tmp, tr_pos and tr_tmp_pos
   float* delta;
   void* dofp;
   float *doc, *deltac, *S, *dP, *dqc, *dkc, *dvc;
   int32_t *tr_offs, *tr_order, *tr_ids, *tr_tmp;
+  int32_t *tr_pos, *tr_tmp_pos;  // per transposed entry: its index in ids (bf16 path)
+  void* ds;                      // bf16 path: one 64 x 64 dS tile per entry of ids
   void *dq, *dk, *dv, *dgc, *dgf;
 };
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t st);
