@@ -96,6 +96,39 @@ def test_varlen_backward_small_including_empty_lists():
         assert_close(host64(g), ref[name], BF16, name)
 
 
+def test_varlen_backward_with_shuffled_lists():
+    """The order inside a key list is free: with every list shuffled, dK, dV
+    and the gate gradients (accumulated over the transposed lists, in query
+    cube order) come out bitwise the same, and dQ (accumulated in list
+    order, from the dS tile stored for each list entry) still matches the
+    oracle.  Pins the entry-to-tile mapping of the dQ pass."""
+    vsa = _vsa()
+    B, nh, D, grid = 2, 2, 128, (8, 12, 16)  # 24 cubes
+    inp = make_inputs(B, nh, D, grid, dtype="bf16", seed=37, with_dout=True, varlen=(1, 24))
+    offs_np, ids_np = inp["kv_offsets"], inp["kv_ids"]
+    rng = np.random.default_rng(38)
+    shuffled = ids_np.copy()
+    for a, b in zip(offs_np[:-1], offs_np[1:]):
+        shuffled[a:b] = rng.permutation(shuffled[a:b])
+    assert not np.array_equal(shuffled, ids_np)
+    offs = torch.from_numpy(offs_np).cuda()
+    q, k, v, gc, gf, do = (dev(inp[n], BF16) for n in ("q", "k", "v", "gc", "gf", "dout"))
+    # one forward state for both (the forward's own rounding follows list order)
+    _, saved = vsa.block_sparse_attn_varlen(q, k, v, gc, gf, grid, offs, torch.from_numpy(ids_np).cuda(),
+                                            save=True)
+    runs = []
+    for ids_host in (ids_np, shuffled):
+        ids = torch.from_numpy(ids_host).cuda()
+        runs.append(vsa.block_sparse_attn_varlen_backward(q, k, v, gc, gf, do, offs, ids, saved, grid))
+    torch.cuda.synchronize()
+    for i, name in enumerate(GRADS):
+        if name != "dq":
+            assert torch.equal(runs[0][i], runs[1][i]), name
+    lists = oracle.lists_from_csr(offs_np, ids_np, B, nh, 24)
+    ref = oracle.backward(inp["q"], inp["k"], inp["v"], inp["gc"], inp["gf"], inp["dout"], grid, lists)
+    assert_close(host64(runs[1][0]), ref["dq"], BF16, "dq, shuffled lists")
+
+
 def test_backward_training_workload_whole_tensor():
     """train16k: B=2, 12 heads, head_dim 128, 16x32x32 grid, top-K 32.
     All five gradients over the whole tensors against oracle.backward under
