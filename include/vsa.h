@@ -76,10 +76,13 @@ size_t vsa_forward_workspace_bytes(int B, int heads, int head_dim,
 size_t vsa_backward_workspace_bytes(int B, int heads, int head_dim,
                                     int T, int H, int W, int dtype,
                                     int64_t n_list_entries);
-/* Size of the forward->backward state ("saved"): fp32 coarse output
- * [B,heads,Nc,D], coarse log-sum-exp [B,heads,Nc], fine log-sum-exp
- * [B,heads,N] and fine output [B,heads,N,D] (cube-major token order). */
-size_t vsa_saved_bytes(int B, int heads, int head_dim, int T, int H, int W);
+/* Size of the forward->backward state ("saved") for element type dtype:
+ * fp32 coarse output [B,heads,Nc,D], coarse log-sum-exp [B,heads,Nc], fine
+ * log-sum-exp [B,heads,N] and fine output [B,heads,N,D] (cube-major token
+ * order), the forward's K and V cube tiles [B,heads,Nc,64,D] (dtype) and
+ * the fp32 cube means of Q, K and V [B,heads,Nc,D].  The backward reads K
+ * and V only from here.  Opaque to the caller; 0 for an invalid shape. */
+size_t vsa_saved_bytes(int B, int heads, int head_dim, int T, int H, int W, int dtype);
 
 /* ---------------------------------------------------------------- forward
  * vsa_forward: the whole operator ([VSA-sum, Approach]; [VSA-abs]).
@@ -182,7 +185,10 @@ int vsa_forward_mass(const void* q, const void* k, const void* v,
  * ([VSA-abs]: one operator trained end-to-end).  The selection is held
  * fixed (no gradient through the discrete choice); the coarse stage carries
  * gradient to the pooled tensors, which spread it evenly over each cube's
- * 64 tokens.  sel_idx / kv lists must be the ones the forward used.
+ * 64 tokens.  sel_idx / kv lists must be the ones the forward used, and
+ * q and `saved` must come from that same forward: K and V enter only
+ * through the tiles and means the forward left in `saved` (k and v must
+ * still be non-NULL, and are not read).
  * Outputs dq, dk, dv [B,N,heads,D] (dtype) and dgate_c, dgate_f [B,N,heads]
  * (fp32) are overwritten.  VSA_BF16 runs the products on the bf16 matrix
  * cores with fp32 accumulation; VSA_F32 uses fp32 arithmetic throughout

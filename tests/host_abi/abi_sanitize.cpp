@@ -226,7 +226,7 @@ void run_shape(int B, int heads, int D, int T, int H, int W, int dtype, int topk
   const size_t raster = (size_t)(B * N * heads * D) * elt, gates = (size_t)(B * N * heads) * elt;
   void *q = m.get(raster), *k = m.get(raster), *v = m.get(raster), *dout = m.get(raster);
   void *gc = m.get(gates), *gf = m.get(gates), *out = m.get(raster);
-  const size_t svb = vsa_saved_bytes(B, heads, D, T, H, W);
+  const size_t svb = vsa_saved_bytes(B, heads, D, T, H, W, dtype);
   const size_t fwb = vsa_forward_workspace_bytes(B, heads, D, T, H, W, dtype);
   EXPECT(svb > 0 && fwb > 0);
   void *saved = m.get(svb), *ws = m.get(fwb);

@@ -61,8 +61,13 @@ def test_workspace_sizes(lib):
     N, nc = T * H * W, T * H * W // 64
     fw = lib.vsa_forward_workspace_bytes(B, nh, D, T, H, W, _lib.VSA_BF16)
     assert fw >= 2 * B * nh * N * D * 2 + 4 * B * nh * nc * D * 4
-    sv = lib.vsa_saved_bytes(B, nh, D, T, H, W)
-    assert sv >= 4 * (B * nh * nc * D + B * nh * nc + B * nh * N + B * nh * N * D)
+    sv = lib.vsa_saved_bytes(B, nh, D, T, H, W, _lib.VSA_BF16)
+    # coarse output, both log-sum-exps, fine output; K and V tiles; three means
+    assert sv >= 4 * (B * nh * nc * D + B * nh * nc + B * nh * N + B * nh * N * D) \
+        + 2 * 2 * B * nh * N * D + 3 * 4 * B * nh * nc * D
+    sv32 = lib.vsa_saved_bytes(B, nh, D, T, H, W, _lib.VSA_F32)
+    assert sv32 >= sv + 2 * 2 * B * nh * N * D
+    assert lib.vsa_saved_bytes(B, nh, D, T, H, W, 7) == 0
     bw = lib.vsa_backward_workspace_bytes(B, nh, D, T, H, W, _lib.VSA_BF16, B * nh * nc * 32)
     assert bw > fw
     # the coarse stage holds at most 3584 cubes (8 rows of logits in LDS,

@@ -78,6 +78,23 @@ def test_backward_is_deterministic():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
+def test_backward_takes_k_and_v_from_the_saved_state(dtype):
+    """K and V enter the backward only through the tiles and cube means the
+    forward left in its saved state: other k and v tensors handed to the
+    backward change nothing."""
+    vsa = _vsa()
+    grid = (8, 8, 16)
+    inp = make_inputs(1, 2, 64, grid, dtype="bf16" if dtype == BF16 else "f32", seed=77, with_dout=True)
+    q, k, v, gc, gf, do = (dev(inp[n], dtype) for n in ("q", "k", "v", "gc", "gf", "dout"))
+    out, sel, saved = vsa.vsa_forward(q, k, v, gc, gf, grid, 4, save=True)
+    g1 = vsa.vsa_backward(q, k, v, gc, gf, do, sel, saved, grid)
+    g2 = vsa.vsa_backward(q, torch.randn_like(k), torch.zeros_like(v), gc, gf, do, sel, saved, grid)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
 def test_varlen_backward_small_including_empty_lists():
     vsa = _vsa()
     B, nh, D, grid = 1, 2, 128, (8, 8, 12)

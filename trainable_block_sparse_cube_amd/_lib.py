@@ -22,7 +22,7 @@ SIGNATURES = {
     "vsa_status_string": (ctypes.c_char_p, [_i]),
     "vsa_forward_workspace_bytes": (_sz, [_i] * 7),
     "vsa_backward_workspace_bytes": (_sz, [_i] * 7 + [_i64]),
-    "vsa_saved_bytes": (_sz, [_i] * 6),
+    "vsa_saved_bytes": (_sz, [_i] * 7),
     "vsa_forward": (_i, [_p] * 5 + [_i] * 8 + [_p, _p, _p, _p, _sz, _p]),
     "vsa_forward_noalloc": (_i, [_p] * 5 + [_i] * 8 + [_p, _p, _p, _p]),
     "block_sparse_attn_varlen": (_i, [_p] * 5 + [_i] * 6 + [_p, _p, _i64, _i, _p, _p, _p, _sz, _p]),

@@ -94,12 +94,14 @@ __global__ __launch_bounds__(256) void permute_pool_kernel(PermutePoolPtrs p, in
     const bool pk = packed_kv && which > 0;
     const int ncp = packed_keys(nc);
     float* base = pooled + (int64_t)(b * nh + h) * (pk ? ncp : nc) * D;
+    float* plain = p.plain[which] ? p.plain[which] + ((int64_t)(b * nh + h) * nc + c) * D : nullptr;
     for (int d = tid; d < D; d += 256) {
       const float r = MAXP ? fmaxf(fmaxf(red[0][d], red[1][d]), fmaxf(red[2][d], red[3][d]))
                            : ((red[0][d] + red[1][d]) + (red[2][d] + red[3][d])) * (1.0f / kCubeTokens);
       if (!pk) base[(int64_t)c * D + d] = r;
       else if (which == 1) base[packed_k_index(c, d, D)] = r;
       else base[packed_v_index(c, d, D)] = r;
+      if (plain) plain[d] = r;
     }
     if (pk && c == nc - 1) {  // zero the padding keys of this (b, h)
       for (int i = tid; i < (ncp - nc) * D; i += 256) {
@@ -120,14 +122,16 @@ constexpr double kNonTemporalTileBytes = 256.0 * 1024 * 1024;
 template <typename T, int D>
 static hipError_t launch_pp(const PermutePoolArgs& a, hipStream_t st) {
   const int nc = (a.T / 4) * (a.H / 4) * (a.W / 4);
-  dim3 grid((unsigned)(a.B * nc * a.heads), 3);
+  dim3 grid((unsigned)(a.B * nc * a.heads), (unsigned)a.n_tensors);
   if (a.max_pool) {
     PermutePoolPtrs p = a.p;
     p.nat[0] = p.nat[1] = p.nat[2] = nullptr;  // pooled values only
+    p.plain[0] = p.plain[1] = p.plain[2] = nullptr;
     permute_pool_kernel<T, D, true, false><<<grid, 256, 0, st>>>(p, a.heads, a.T, a.H, a.W, false);
     return hipGetLastError();
   }
-  const int n_tiles = (a.p.nat[0] != nullptr) + (a.p.nat[1] != nullptr) + (a.p.nat[2] != nullptr);
+  int n_tiles = 0;
+  for (int i = 0; i < a.n_tensors; ++i) n_tiles += a.p.nat[i] != nullptr;
   const double tile_bytes = (double)n_tiles * a.B * a.heads * nc * kCubeTokens * D * sizeof(T);
   if (tile_bytes > kNonTemporalTileBytes)
     permute_pool_kernel<T, D, false, true><<<grid, 256, 0, st>>>(a.p, a.heads, a.T, a.H, a.W, a.packed_kv);

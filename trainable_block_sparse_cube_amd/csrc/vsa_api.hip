@@ -65,18 +65,32 @@ size_t fwd_ws_layout(const Shape& s, char* base, FwdWorkspace* w) {
   return off;
 }
 
+// Forward -> backward state.  Besides the forward's outputs that the
+// backward needs (coarse output and log-sum-exp, fine log-sum-exp and fine
+// output), the forward leaves its K and V cube tiles and the plain fp32
+// cube means of Q, K and V here, so that the backward's permute only has
+// to make Q tiles.
 struct Saved {
   float *oc, *lse_c, *lse_f, *of;
+  void *kp, *vp;
+  float *qc, *kc, *vc;
 };
 
 size_t saved_layout(const Shape& s, char* base, Saved* sv) {
   size_t off = 0;
-  auto take = [&](size_t bytes) { char* p = base ? base + off : nullptr; off += align_up(bytes); return (float*)p; };
+  auto take = [&](size_t bytes) { char* p = base ? base + off : nullptr; off += align_up(bytes); return (void*)p; };
+  const size_t pooled = (size_t)s.B * s.heads * s.nc * s.D * sizeof(float);
+  const size_t tile = (size_t)s.B * s.heads * s.N * s.D * s.elt;
   Saved t;
-  t.oc = take((size_t)s.B * s.heads * s.nc * s.D * sizeof(float));
-  t.lse_c = take((size_t)s.B * s.heads * s.nc * sizeof(float));
-  t.lse_f = take((size_t)s.B * s.heads * s.N * sizeof(float));
-  t.of = take((size_t)s.B * s.heads * s.N * s.D * sizeof(float));
+  t.oc = (float*)take(pooled);
+  t.lse_c = (float*)take((size_t)s.B * s.heads * s.nc * sizeof(float));
+  t.lse_f = (float*)take((size_t)s.B * s.heads * s.N * sizeof(float));
+  t.of = (float*)take((size_t)s.B * s.heads * s.N * s.D * sizeof(float));
+  t.kp = take(tile);
+  t.vp = take(tile);
+  t.qc = (float*)take(pooled);
+  t.kc = (float*)take(pooled);
+  t.vc = (float*)take(pooled);
   if (sv) *sv = t;
   return off;
 }
@@ -137,21 +151,27 @@ int forward_impl(const void* q, const void* k, const void* v, const void* gc, co
                                 w.check, st);
     if (vs != VSA_OK) return vs;
   }
+  const bool bf = s.dtype == VSA_BF16;
   float *oc = w.oc, *lse_c = w.lse_c, *lse_f = nullptr, *of = nullptr;
-  if (saved) {
+  void *kp = w.kp, *vp = w.vp;
+  float *qc = w.qc, *kc = w.kc, *vc = w.vc;
+  float *plain_k = nullptr, *plain_v = nullptr;
+  if (saved) {  // tiles and means go where the backward will read them
     Saved sv;
     saved_layout(s, (char*)saved, &sv);
     oc = sv.oc; lse_c = sv.lse_c; lse_f = sv.lse_f; of = sv.of;
+    kp = sv.kp; vp = sv.vp; qc = sv.qc;
+    if (bf) { plain_k = sv.kc; plain_v = sv.vc; }  // the coarse stage reads the packed copies
+    else { kc = sv.kc; vc = sv.vc; }
   }
-  const bool bf = s.dtype == VSA_BF16;
   // The fine stage reads Q in place; K and V are copied into cube tiles.
   // bf16: pooled K and V go straight into the coarse kernel's operand order.
-  PermutePoolArgs pa{{{q, k, v}, {nullptr, w.kp, w.vp}, {w.qc, w.kc, w.vc}},
+  PermutePoolArgs pa{{{q, k, v}, {nullptr, kp, vp}, {qc, kc, vc}, {nullptr, plain_k, plain_v}},
                      s.B, s.heads, s.D, s.T, s.H, s.W, bf};
   pa.packed_kv = bf;
   hipError_t e = launch_permute_pool(pa, st);
   if (e != hipSuccess) return VSA_ERR_HIP;
-  CoarseArgs ca{w.qc, w.kc, w.vc, s.B, s.heads, s.D, (int)s.nc, offs ? 0 : topk, oc, lse_c, sel, bf};
+  CoarseArgs ca{qc, kc, vc, s.B, s.heads, s.D, (int)s.nc, offs ? 0 : topk, oc, lse_c, sel, bf};
   ca.packed = bf;
   const int rows = (int)((int64_t)s.B * s.heads * s.nc);
   int32_t* counts = nullptr;
@@ -173,7 +193,7 @@ int forward_impl(const void* q, const void* k, const void* v, const void* gc, co
     n_ids = (int64_t)rows * mr->k_max;  // capacity; the packed lists end at offsets[rows]
   }
   if (!offs) n_ids = (int64_t)rows * topk;
-  FineArgs fa{q, w.kp, w.vp, oc, gc, gf, s.B, s.heads, s.D, s.T, s.H, s.W,
+  FineArgs fa{q, kp, vp, oc, gc, gf, s.B, s.heads, s.D, s.T, s.H, s.W,
               offs, offs ? ids : sel, topk, n_ids, bf, out, lse_f, of};
   if (bf) {  // the MFMA kernel runs the query cubes sorted by their lists' middle entries
     e = launch_fine_order(fa.offs, fa.ids, topk, n_ids, s.B * s.heads, (int)s.nc, w.order, st);
@@ -185,8 +205,8 @@ int forward_impl(const void* q, const void* k, const void* v, const void* gc, co
 
 struct BwdWorkspace {
   int32_t* check;  // 2 ints: list validation counts (VSA_VALIDATE)
-  void *qp, *kp, *vp, *dofp;
-  float *qc, *kc, *vc, *delta, *doc, *deltac, *S, *dP, *dqc, *dkc, *dvc;
+  void *qp, *dofp;
+  float *delta, *doc, *deltac, *S, *dP, *dqc, *dkc, *dvc;
   int32_t *tr_offs, *tr_order, *tr_ids, *tr_tmp, *tr_pos, *tr_tmp_pos;
   void* ds;  // bf16: the dS tile of every (query cube, selected key cube) entry
 };
@@ -201,8 +221,7 @@ size_t bwd_ws_layout(const Shape& s, int64_t n_entries, char* base, BwdWorkspace
   auto take = [&](size_t bytes) { char* p = base ? base + off : nullptr; off += bytes; return (void*)p; };
   BwdWorkspace t;
   t.check = (int32_t*)take(kAlign);
-  t.qp = take(tile); t.kp = take(tile); t.vp = take(tile); t.dofp = take(tile);
-  t.qc = (float*)take(pooled); t.kc = (float*)take(pooled); t.vc = (float*)take(pooled);
+  t.qp = take(tile); t.dofp = take(tile);
   t.delta = (float*)take(per_tok);
   t.doc = (float*)take(pooled); t.deltac = (float*)take(per_cube);
   t.S = (float*)take(sq); t.dP = (float*)take(sq);
@@ -241,15 +260,18 @@ int backward_impl(const void* q, const void* k, const void* v, const void* gc, c
   Saved sv;
   saved_layout(s, (char*)const_cast<void*>(saved), &sv);
   const bool bf = s.dtype == VSA_BF16;
-  PermutePoolArgs pa{{{q, k, v}, {w.qp, w.kp, w.vp}, {w.qc, w.kc, w.vc}},
+  // Q tiles only: the K and V tiles and all three cube means are the
+  // forward's, kept in `saved`.
+  PermutePoolArgs pa{{{q, nullptr, nullptr}, {w.qp, nullptr, nullptr}, {nullptr, nullptr, nullptr}},
                      s.B, s.heads, s.D, s.T, s.H, s.W, bf};
+  pa.n_tensors = 1;
   if (launch_permute_pool(pa, st) != hipSuccess) return VSA_ERR_HIP;
   BackwardArgs ba;
   ba.B = s.B; ba.heads = s.heads; ba.D = s.D; ba.T = s.T; ba.H = s.H; ba.W = s.W;
   ba.bf16 = bf;
   ba.dout = dout; ba.gc = gc; ba.gf = gf;
-  ba.qp = w.qp; ba.kp = w.kp; ba.vp = w.vp;
-  ba.qc = w.qc; ba.kc = w.kc; ba.vc = w.vc;
+  ba.qp = w.qp; ba.kp = sv.kp; ba.vp = sv.vp;
+  ba.qc = sv.qc; ba.kc = sv.kc; ba.vc = sv.vc;
   ba.oc = sv.oc; ba.lse_c = sv.lse_c; ba.lse_f = sv.lse_f; ba.of = sv.of;
   ba.offs = offs; ba.ids = ids; ba.topk = topk; ba.n_ids = n_entries;
   ba.delta = w.delta; ba.dofp = w.dofp;
@@ -308,9 +330,9 @@ size_t vsa_forward_workspace_bytes(int B, int heads, int head_dim, int T, int H,
   return fwd_ws_layout(s, nullptr, nullptr);
 }
 
-size_t vsa_saved_bytes(int B, int heads, int head_dim, int T, int H, int W) {
+size_t vsa_saved_bytes(int B, int heads, int head_dim, int T, int H, int W, int dtype) {
   Shape s;
-  if (check_shape(B, heads, head_dim, T, H, W, VSA_F32, &s) != VSA_OK) return 0;
+  if (check_shape(B, heads, head_dim, T, H, W, dtype, &s) != VSA_OK) return 0;
   return saved_layout(s, nullptr, nullptr);
 }
 

@@ -13,6 +13,7 @@ struct PermutePoolPtrs {
   const void* src[3];
   void* nat[3];
   float* pooled[3];
+  float* plain[3] = {nullptr, nullptr, nullptr};  // optional second copy of the means, plain layout
 };
 // Operand-ordered ("packed") pooled K and V for the coarse kernel's bf16
 // path: each wave load of an MFMA operand block is one contiguous run.
@@ -40,6 +41,7 @@ struct PermutePoolArgs {
   bool bf16;
   bool max_pool = false;   // per-channel max instead of the mean; no tiles written
   bool packed_kv = false;  // pooled K and V in the packed layouts (pitch packed_keys(nc))
+  int n_tensors = 3;       // tensors 0 .. n_tensors - 1 of (q, k, v) are processed
 };
 hipError_t launch_permute_pool(const PermutePoolArgs& a, hipStream_t st);
 

@@ -87,8 +87,10 @@ def _workspace(nbytes, device):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
-def saved_bytes(B, heads, D, grid):
-    return _lib.load().vsa_saved_bytes(B, heads, D, *grid)
+def saved_bytes(B, heads, D, grid, dtype=torch.bfloat16):
+    if dtype not in _DT:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return _lib.load().vsa_saved_bytes(B, heads, D, *grid, _DT[dtype])
 
 
 def _out(out, q):
@@ -106,7 +108,7 @@ def vsa_forward(q, k, v, gate_c, gate_f, grid, topk, save=False, out=None):
     nc = N // 64
     out = _out(out, q)
     sel = torch.empty((B, nh, nc, topk), dtype=torch.int32, device=q.device)
-    saved = _workspace(lib.vsa_saved_bytes(B, nh, D, T, H, W), q.device) if save else None
+    saved = _workspace(lib.vsa_saved_bytes(B, nh, D, T, H, W, dt), q.device) if save else None
     wsb = lib.vsa_forward_workspace_bytes(B, nh, D, T, H, W, dt)
     ws = _workspace(wsb, q.device)
     with _on(q) as stream:
@@ -165,7 +167,7 @@ def block_sparse_attn_varlen(q, k, v, gate_c, gate_f, grid, kv_offsets, kv_ids, 
     if validate:
         _require_valid(kv_ids, B * nh * nc, nc, kv_offsets=kv_offsets)
     out = _out(out, q)
-    saved = _workspace(lib.vsa_saved_bytes(B, nh, D, T, H, W), q.device) if save else None
+    saved = _workspace(lib.vsa_saved_bytes(B, nh, D, T, H, W, dt), q.device) if save else None
     wsb = lib.vsa_forward_workspace_bytes(B, nh, D, T, H, W, dt)
     ws = _workspace(wsb, q.device)
     with _on(q) as stream:
@@ -191,7 +193,7 @@ def vsa_forward_mass(q, k, v, gate_c, gate_f, grid, mass, k_min, k_max, save=Fal
     out = torch.empty_like(q)
     offs = torch.empty(B * nh * nc + 1, dtype=torch.int32, device=q.device)
     ids = torch.empty(B * nh * nc * max(int(k_max), 1), dtype=torch.int32, device=q.device)
-    saved = _workspace(lib.vsa_saved_bytes(B, nh, D, T, H, W), q.device) if save else None
+    saved = _workspace(lib.vsa_saved_bytes(B, nh, D, T, H, W, dt), q.device) if save else None
     wsb = lib.vsa_forward_mass_workspace_bytes(B, nh, D, T, H, W, dt, int(k_max))
     ws = _workspace(wsb, q.device)
     with _on(q) as stream:
@@ -215,7 +217,7 @@ def vsa_backward(q, k, v, gate_c, gate_f, dout, sel, saved, grid, validate=False
     _need(sel, "sel", torch.int32, device=q.device)
     if validate:
         _require_valid(sel, B * nh * nc, nc, topk=sel.shape[-1])
-    _need(saved, "saved", torch.uint8, min_numel=int(lib.vsa_saved_bytes(B, nh, D, T, H, W)))
+    _need(saved, "saved", torch.uint8, min_numel=int(lib.vsa_saved_bytes(B, nh, D, T, H, W, dt)))
     topk = sel.shape[-1]
     grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
              torch.empty(gate_c.shape, dtype=torch.float32, device=q.device),
@@ -240,7 +242,7 @@ def block_sparse_attn_varlen_backward(q, k, v, gate_c, gate_f, dout, kv_offsets,
     if validate:
         _require_valid(kv_ids, B * nh * (N // 64), N // 64, kv_offsets=kv_offsets)
     _need(dout, "dout", q.dtype, shape=q.shape, device=q.device)
-    _need(saved, "saved", torch.uint8, min_numel=int(lib.vsa_saved_bytes(B, nh, D, T, H, W)))
+    _need(saved, "saved", torch.uint8, min_numel=int(lib.vsa_saved_bytes(B, nh, D, T, H, W, dt)))
     grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
              torch.empty(gate_c.shape, dtype=torch.float32, device=q.device),
              torch.empty(gate_f.shape, dtype=torch.float32, device=q.device)]
