@@ -8,7 +8,10 @@
 // raster layout), writes them as one contiguous cube-major tile, and reduces
 // the 64 rows to their fp32 mean with wavefront shuffles plus a 4-way LDS
 // combine.  The forward writes the K and V tiles (the fine stage reads Q in
-// place); the backward writes Q, K and V tiles.  The forward's bf16 path
+// place); the backward writes Q tiles only (it reads the K and V tiles and
+// the cube means the forward left in its saved state, which the forward
+// writes as a second, plain-layout copy of the K and V means when its own
+// copy is packed).  The forward's bf16 path
 // stores the pooled K and V in the coarse kernel's operand order (packed
 // layouts, zero-padded keys).  A second instance takes
 // the per-channel maximum instead of the mean and writes no tiles: the

@@ -100,8 +100,9 @@ int order_max_cubes();
 hipError_t launch_fine_order(const int32_t* offs, const int32_t* ids, int topk, int64_t n_ids,
                              int n_bh, int nc, int32_t* order, hipStream_t st);
 
-// Backward (bf16 or fp32).  Inputs: raster dout, gates; cube-major tiles qp, kp,
-// vp from the backward permute; fp32 means; forward state (oc, lse_c,
+// Backward (bf16 or fp32).  Inputs: raster dout, gates; cube-major tiles: qp
+// from the backward's permute, kp, vp from the forward's saved state; fp32
+// means (saved state); forward state (oc, lse_c,
 // lse_f, of); key lists (offs null: fixed topk).  Scratch: delta [BH,N],
 // dofp tiles, doc [BH,Nc,D], deltac [BH,Nc], S and dP [BH,Nc,Nc],
 // dqc/dkc/dvc [BH,Nc,D], tr_offs [BH*Nc+1], tr_order [BH*Nc], tr_ids and
