@@ -330,6 +330,20 @@ def test_fine_order_sorts_by_middle_entry_and_changes_nothing():
     mids = mids.reshape(B * nh, nc)
     want = np.concatenate([bh * nc + np.lexsort((np.arange(nc), mids[bh])) for bh in range(B * nh)])
     np.testing.assert_array_equal(order.cpu().numpy(), want)
+    # larger (b, h) blocks, drawn directly: random sorted lists up to the
+    # sort's 4096-cube limit, and identical lists (one bucket of every cube)
+    rng = np.random.default_rng(64)
+    for n_bh, nc, K, same in ((3, 512, 16, False), (2, 4096, 32, False), (2, 960, 32, True)):
+        if same:
+            lists = np.broadcast_to(np.arange(K, dtype=np.int32), (n_bh * nc, K))
+        else:
+            lists = np.sort(np.stack([rng.choice(nc, K, replace=False) for _ in range(n_bh * nc)]), axis=1)
+        lists = np.ascontiguousarray(lists, dtype=np.int32)
+        order = vsa.vsa_fine_order(torch.from_numpy(lists).cuda(), 1, n_bh, nc, topk=K)
+        torch.cuda.synchronize()
+        mid = lists.reshape(n_bh, nc, K)[:, :, K // 2]
+        want = np.concatenate([bh * nc + np.lexsort((np.arange(nc), mid[bh])) for bh in range(n_bh)])
+        np.testing.assert_array_equal(order.cpu().numpy(), want)
 
 
 def test_fine_order_entries_out_of_range_run_nothing():

@@ -6,10 +6,15 @@
 // lists have similar middle entries sweep similar key ranges at the same
 // time, so when such cubes run side by side on one XCD more of their tile
 // reads hit its L2.  This kernel sorts each (batch, head)'s query cubes by
-// the middle entry of their list (cube index breaking ties): one workgroup
-// per (b, h), a bitonic sort of (middle id << 12 | cube) keys in LDS.  The
-// result only reorders work: every query cube's own arithmetic, hence the
-// output, is unchanged.
+// the middle entry of their list, cube index breaking ties: one workgroup
+// per (b, h), a stable least-significant-digit radix sort of the 12-bit
+// middle entries in two passes of 6 bits, starting from cube order.  In a
+// pass every wave ranks its 64 entries among those with the same digit
+// (peer masks from six ballots), the per-(digit, tile, wave) counts are
+// scanned in (digit, tile, wave) order, and each entry moves to its
+// digit's offset plus its rank, which keeps equal digits in input order.
+// The result only reorders work: every query cube's own arithmetic, hence
+// the output, is unchanged.
 #include "vsa_device.h"
 #include "vsa_launch.h"
 
@@ -18,41 +23,90 @@ namespace vsa {
 namespace {
 
 constexpr int kOrderThreads = 1024;
-constexpr int kOrderMax = 4096;  // cubes per (b, h) this sort holds (>= the coarse stage's limit)
+constexpr int kOrderWaves = kOrderThreads / 64;
+constexpr int kOrderMax = 4096;                        // cubes per (b, h) this sort holds
+constexpr int kOrderTiles = kOrderMax / kOrderThreads;  // entries per thread
+constexpr int kDigitBits = 6;                          // two passes cover ids < 4096
+constexpr int kDigits = 1 << kDigitBits;
+constexpr int kBins = kDigits * kOrderTiles * kOrderWaves;
+static_assert(2 * kDigitBits >= 12 && kOrderMax <= 4096, "two passes of the 12-bit ids");
+static_assert(kBins % kOrderThreads == 0, "scan layout");
 
 __global__ __launch_bounds__(kOrderThreads) void order_by_middle_kernel(
     const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk, int64_t n_ids,
-    int nc, int P, int32_t* __restrict__ order) {
-  __shared__ uint32_t key[kOrderMax];
+    int nc, int32_t* __restrict__ order) {
+  __shared__ uint16_t mid_of[kOrderMax];  // middle entry of each cube's list
+  __shared__ uint16_t seq[2][kOrderMax];  // cubes in the current / next order
+  __shared__ int32_t bins[kBins];         // counts per (digit, tile, wave), then their offsets
+  __shared__ int32_t wsum[kOrderWaves];
   const int64_t base = (int64_t)blockIdx.x * nc;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < P; i += kOrderThreads) {
-    uint32_t kv = 0xFFFFFFFFu;  // padding sorts last
-    if (i < nc) {
-      int64_t start;
-      int n;
-      list_range(offs, base + i, topk, n_ids, &start, &n);
-      const uint32_t mid = n > 0 ? (uint32_t)cube_or_0(ids[start + n / 2], nc) : 0u;
-      kv = (mid << 12) | (uint32_t)i;
-    }
-    key[i] = kv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  for (int c = tid; c < nc; c += kOrderThreads) {
+    int64_t start;
+    int n;
+    list_range(offs, base + c, topk, n_ids, &start, &n);
+    mid_of[c] = (uint16_t)(n > 0 ? cube_or_0(ids[start + n / 2], nc) : 0);  // an empty list counts as 0
+    seq[0][c] = (uint16_t)c;
   }
-  __syncthreads();
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < P; i += kOrderThreads) {
-        const int l = i ^ j;
-        if (l > i) {
-          const uint32_t a = key[i], b = key[l];
-          const bool ascending = (i & k) == 0;
-          if ((a > b) == ascending) { key[i] = b; key[l] = a; }
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int pass = 0; pass < 2; ++pass) {
+    const uint16_t* src = seq[pass];
+    uint16_t* dst = seq[pass ^ 1];
+    for (int i = tid; i < kBins; i += kOrderThreads) bins[i] = 0;
+    __syncthreads();
+    int digit[kOrderTiles], rank[kOrderTiles];
+#pragma unroll
+    for (int u = 0; u < kOrderTiles; ++u) {
+      const int idx = u * kOrderThreads + tid;
+      const bool live = idx < nc;
+      const int d = live ? (mid_of[src[idx]] >> (kDigitBits * pass)) & (kDigits - 1) : 0;
+      uint64_t peers = __ballot(live);
+#pragma unroll
+      for (int b = 0; b < kDigitBits; ++b) {
+        const uint64_t m = __ballot((d >> b) & 1);
+        peers &= ((d >> b) & 1) ? m : ~m;
+      }
+      digit[u] = d;
+      rank[u] = __popcll(peers & below);
+      if (live && rank[u] == 0) bins[(d * kOrderTiles + u) * kOrderWaves + wave] = __popcll(peers);
+    }
+    __syncthreads();
+    // exclusive scan of bins in (digit, tile, wave) order: thread t owns a run
+    {
+      constexpr int L = kBins / kOrderThreads;
+      int v[L], s = 0;
+#pragma unroll
+      for (int i = 0; i < L; ++i) { v[i] = bins[tid * L + i]; s += v[i]; }
+      int x = s;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+      }
+      if (lane == 63) wsum[wave] = x;
+      __syncthreads();
+      if (wave == 0) {
+        int w = lane < kOrderWaves ? wsum[lane] : 0;
+        for (int o = 1; o < kOrderWaves; o <<= 1) {
+          const int y = __shfl_up(w, o);
+          if (lane >= o) w += y;
         }
+        if (lane < kOrderWaves) wsum[lane] = w;
       }
       __syncthreads();
+      int prefix = x - s + (wave > 0 ? wsum[wave - 1] : 0);
+#pragma unroll
+      for (int i = 0; i < L; ++i) { bins[tid * L + i] = prefix; prefix += v[i]; }
     }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kOrderTiles; ++u) {
+      const int idx = u * kOrderThreads + tid;
+      if (idx < nc) dst[bins[(digit[u] * kOrderTiles + u) * kOrderWaves + wave] + rank[u]] = src[idx];
+    }
+    __syncthreads();
   }
-  for (int i = tid; i < nc; i += kOrderThreads)
-    order[base + i] = (int32_t)(base + (key[i] & 0xFFFu));
+  for (int i = tid; i < nc; i += kOrderThreads) order[base + i] = (int32_t)(base + seq[0][i]);
 }
 
 }  // namespace
@@ -61,10 +115,7 @@ int order_max_cubes() { return kOrderMax; }
 
 hipError_t launch_fine_order(const int32_t* offs, const int32_t* ids, int topk, int64_t n_ids,
                              int n_bh, int nc, int32_t* order, hipStream_t st) {
-  int P = 1;
-  while (P < nc) P <<= 1;
-  order_by_middle_kernel<<<(unsigned)n_bh, kOrderThreads, 0, st>>>(offs, ids, topk, n_ids, nc, P,
-                                                                    order);
+  order_by_middle_kernel<<<(unsigned)n_bh, kOrderThreads, 0, st>>>(offs, ids, topk, n_ids, nc, order);
   return hipGetLastError();
 }
 
