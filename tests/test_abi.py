@@ -88,6 +88,19 @@ def fwd(lib, T=8, H=8, W=8, D=64, topk=2, dtype=_lib.VSA_BF16, null_out=False, w
                            None if null_out else FAKE, FAKE, None, ws, ws_bytes, None)
 
 
+def test_saved_state_size_follows_the_element_type():
+    """The forward keeps its K and V tiles in the saved state, so its size
+    grows with the element size (host only: no GPU work)."""
+    import torch
+    from trainable_block_sparse_cube_amd import ops
+    B, nh, D, grid = 1, 2, 64, (8, 8, 8)
+    N = 8 * 8 * 8
+    bf, f32 = ops.saved_bytes(B, nh, D, grid, torch.bfloat16), ops.saved_bytes(B, nh, D, grid, torch.float32)
+    assert f32 - bf >= 2 * 2 * B * nh * N * D  # two tiles, 2 more bytes per element
+    with pytest.raises(TypeError):
+        ops.saved_bytes(B, nh, D, grid, torch.float16)
+
+
 def test_forward_rejects_bad_arguments(lib):
     assert fwd(lib, T=6) == INVALID          # grid not made of 4x4x4 cubes
     assert fwd(lib, H=0) == INVALID
