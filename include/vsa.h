@@ -296,7 +296,8 @@ int vsa_fine_forward(const void* q, const void* kp, const void* vp,
 /* Processing order for the fine stage: each (b, h)'s query cubes sorted by
  * the middle entry (index n/2) of their key list, cube index on ties, as
  * global ids into order [B*heads*Nc] (int32).  Lists as in
- * vsa_fine_forward; an empty list counts as middle entry 0.  With ascending
+ * vsa_fine_forward; an empty list, or a middle entry outside [0, Nc),
+ * counts as middle entry 0.  With ascending
  * lists, cubes whose lists are centred alike then run side by side and
  * share more tile reads through the L2.  The forward entry points use it
  * for bf16 inputs.  Nc <= 4096. */
