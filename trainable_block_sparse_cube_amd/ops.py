@@ -259,6 +259,72 @@ def block_sparse_attn_varlen_backward(q, k, v, gate_c, gate_f, dout, kv_offsets,
 
 
 # ------------------------------------------------------------ stage calls
+def _wants_grad(*ts):
+    return torch.is_grad_enabled() and any(t.requires_grad for t in ts)
+
+
+class _VSAFunction(torch.autograd.Function):
+    """vsa_forward with its saved state, and vsa_backward as the gradient."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, gate_c, gate_f, grid, topk):
+        out, sel, saved = vsa_forward(q, k, v, gate_c, gate_f, grid, topk, save=True)
+        ctx.save_for_backward(q, k, v, gate_c, gate_f, sel, saved)
+        ctx.grid = tuple(grid)
+        ctx.mark_non_differentiable(sel)
+        return out, sel
+
+    @staticmethod
+    def backward(ctx, dout, _dsel):
+        q, k, v, gc, gf, sel, saved = ctx.saved_tensors
+        dq, dk, dv, dgc, dgf = vsa_backward(q, k, v, gc, gf, dout.contiguous(), sel, saved, ctx.grid)
+        return dq, dk, dv, dgc.to(gc.dtype), dgf.to(gf.dtype), None, None
+
+
+def vsa_attention(q, k, v, gate_c, gate_f, grid, topk):
+    """The operator as one differentiable call: returns (out, sel_idx).
+    When autograd records it, the forward keeps its saved state and the
+    backward runs vsa_backward; otherwise it is vsa_forward without saved
+    state.  No gradient flows through the selection.  Gate gradients come
+    back in the gates' dtype (autograd wants the input's dtype), i.e. the
+    fp32 gradients of vsa_backward rounded once."""
+    if _wants_grad(q, k, v, gate_c, gate_f):
+        return _VSAFunction.apply(q, k, v, gate_c, gate_f, tuple(grid), topk)
+    out, sel, _ = vsa_forward(q, k, v, gate_c, gate_f, grid, topk)
+    return out, sel
+
+
+class _VarlenFunction(torch.autograd.Function):
+    """block_sparse_attn_varlen with its saved state, and the varlen
+    backward as the gradient (the lists were checked by the forward call
+    or vouched for by the caller)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, gate_c, gate_f, grid, kv_offsets, kv_ids, validate):
+        out, saved = block_sparse_attn_varlen(q, k, v, gate_c, gate_f, grid, kv_offsets, kv_ids,
+                                              save=True, validate=validate)
+        ctx.save_for_backward(q, k, v, gate_c, gate_f, kv_offsets, kv_ids, saved)
+        ctx.grid = tuple(grid)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, gc, gf, offs, ids, saved = ctx.saved_tensors
+        dq, dk, dv, dgc, dgf = block_sparse_attn_varlen_backward(
+            q, k, v, gc, gf, dout.contiguous(), offs, ids, saved, ctx.grid, validate=False)
+        return dq, dk, dv, dgc.to(gc.dtype), dgf.to(gf.dtype), None, None, None, None
+
+
+def block_sparse_attn_varlen_attention(q, k, v, gate_c, gate_f, grid, kv_offsets, kv_ids,
+                                       validate=True):
+    """Differentiable form of block_sparse_attn_varlen (same lists, same
+    validate switch); gate gradients as in vsa_attention.  Returns out."""
+    if _wants_grad(q, k, v, gate_c, gate_f):
+        return _VarlenFunction.apply(q, k, v, gate_c, gate_f, tuple(grid), kv_offsets, kv_ids, validate)
+    return block_sparse_attn_varlen(q, k, v, gate_c, gate_f, grid, kv_offsets, kv_ids,
+                                    validate=validate)[0]
+
+
 def vsa_cube_permute_pool(q, k, v, grid, with_q_tiles=True):
     """Returns (qp, kp, vp, qc, kc, vc) in the library's cube-major layouts
     (qp is None when with_q_tiles is False, as in the forward)."""
