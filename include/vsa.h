@@ -114,7 +114,8 @@ int vsa_forward(const void* q, const void* k, const void* v,
  * bf16).  A shape whose forward workspace (vsa_forward_workspace_bytes)
  * exceeds 128 MiB returns VSA_ERR_WORKSPACE and queues nothing.  The call
  * allocates nothing; its first call on a device looks up that device's
- * copy of the array.  All calls on one GPU share the array, so calls that
+ * copy of the array (the device `stream` runs on, or the current device
+ * for the null stream).  All calls on one GPU share the array, so calls that
  * overlap in time on one GPU (on different streams, or from different
  * threads) race and must be serialized by the caller.
  */

@@ -184,6 +184,11 @@ extern "C" hipError_t hipGetDevice(int* dev) {
   *dev = 0;
   return hipSuccess;
 }
+extern "C" hipError_t hipSetDevice(int dev) { return dev == 0 ? hipSuccess : hipErrorInvalidDevice; }
+extern "C" hipError_t hipStreamGetDevice(hipStream_t, hipDevice_t* dev) {
+  *dev = 0;
+  return hipSuccess;
+}
 extern "C" hipError_t hipGetSymbolAddress(void** ptr, const void* symbol) {
   *ptr = const_cast<void*>(symbol);
   return hipSuccess;

@@ -296,13 +296,24 @@ static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 std::mutex scratch_mu;
 void* scratch_ptr[kMaxDevices] = {};
 
-int device_scratch(void** ptr) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return VSA_ERR_HIP;
+// The copy on the GPU that `st` runs on (the current device for the null
+// stream); its address is looked up with that device current.
+int device_scratch(hipStream_t st, void** ptr) {
+  int cur = -1, dev = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return VSA_ERR_HIP;
+  if (st) {
+    if (hipStreamGetDevice(st, &dev) != hipSuccess) return VSA_ERR_HIP;
+  } else {
+    dev = cur;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return VSA_ERR_HIP;
   std::lock_guard<std::mutex> lock(scratch_mu);
   if (!scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return VSA_ERR_HIP;
     void* p = nullptr;
-    if (hipGetSymbolAddress((void**)&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return VSA_ERR_HIP;
+    const hipError_t e = hipGetSymbolAddress((void**)&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return VSA_ERR_HIP;
+    if (e != hipSuccess || !p) return VSA_ERR_HIP;
     scratch_ptr[dev] = p;
   }
   *ptr = scratch_ptr[dev];
@@ -362,7 +373,7 @@ int vsa_forward_noalloc(const void* q, const void* k, const void* v, const void*
   if ((int64_t)B * heads * s.nc * topk > INT_MAX) return VSA_ERR_UNSUPPORTED;
   if (fwd_ws_layout(s, nullptr, nullptr) > kNoAllocScratchBytes) return VSA_ERR_WORKSPACE;
   void* ws = nullptr;
-  st = device_scratch(&ws);
+  st = device_scratch(stream, &ws);
   if (st != VSA_OK) return st;
   // Nothing in the forward's workspace has to start at zero: every stage
   // writes what the next one reads.
