@@ -30,7 +30,9 @@
  *    4 ([VSA-sum, Limitations]).  Nc = N / 64 cubes, at most 3584 per
  *    (batch, head) (VSA_ERR_UNSUPPORTED beyond: the coarse stage keeps
  *    blocks of logit rows in LDS and the row it ranks in registers);
- *    B*heads at most 65535.
+ *    B*heads at most 65535, and B*heads*Nc at most 2^24 - 8 (one
+ *    workgroup of 256 threads per (batch, head, cube) in 1-D grids; about
+ *    275 GB per bf16 tensor at D = 128, so beyond one GPU's memory anyway).
  *  - Token order is raster, token (t, y, x) at (t*H + y)*W + x.
  *    q, k, v, out, dout, dq, dk, dv: [B, N, heads, D].
  *    gate_c, gate_f: [B, N, heads] (one scalar per token and head,

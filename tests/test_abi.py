@@ -114,6 +114,12 @@ def test_forward_rejects_bad_arguments(lib):
     # B * heads is a grid dimension: at most 65535 (batch, head) pairs
     assert lib.vsa_forward(FAKE, FAKE, FAKE, FAKE, FAKE, 256, 256, 64, 8, 8, 8, 2, _lib.VSA_BF16,
                            FAKE, FAKE, None, FAKE, 1 << 40, None) == UNSUPPORTED
+    # (batch, head, cube) units: at most 2^24 - 8 (1-D grids of 256-thread
+    # workgroups); 65535 pairs of 256 cubes pass, of 257 do not
+    assert lib.vsa_forward_workspace_bytes(1, 65535, 64, 4, 16, 256, _lib.VSA_BF16) > 0
+    assert lib.vsa_forward_workspace_bytes(1, 65535, 64, 4, 4, 4 * 257, _lib.VSA_BF16) == 0
+    assert lib.vsa_forward(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 65535, 64, 4, 4, 4 * 257, 2, _lib.VSA_BF16,
+                           FAKE, FAKE, None, FAKE, 1 << 60, None) == UNSUPPORTED
 
 
 def test_varlen_and_backward_reject_bad_arguments(lib):

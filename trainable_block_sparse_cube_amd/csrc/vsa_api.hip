@@ -15,6 +15,10 @@ using namespace vsa;
 namespace {
 
 constexpr size_t kAlign = 256;
+// (batch, head, cube) units at most: kernels with one 256-thread workgroup
+// per unit launch 1-D grids (rounded up to a multiple of 8 workgroups)
+// whose work-item count must stay below 2^32.
+constexpr int64_t kMaxCubeUnits = (int64_t(1) << 24) - 8;
 constexpr size_t kDsTileBytes = 64 * 64 * 2;  // one bf16 dS tile (64 queries x 64 keys)
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
@@ -33,7 +37,7 @@ int check_shape(int B, int heads, int D, int T, int H, int W, int dtype, Shape* 
   const int64_t N = (int64_t)T * H * W;
   const int64_t nc = N / 64;
   if ((int64_t)B * heads > 65535) return VSA_ERR_UNSUPPORTED;  // grid y dimension
-  if (N > INT_MAX / 2 || (int64_t)B * heads * nc > INT_MAX / 2 || (int64_t)B * N * heads > INT_MAX)
+  if (N > INT_MAX / 2 || (int64_t)B * heads * nc > kMaxCubeUnits || (int64_t)B * N * heads > INT_MAX)
     return VSA_ERR_UNSUPPORTED;
   if (nc > coarse_max_cubes(D)) return VSA_ERR_UNSUPPORTED;
   *s = Shape{B, heads, D, T, H, W, dtype, N, nc, dtype == VSA_BF16 ? 2u : 4u};
@@ -440,7 +444,7 @@ int vsa_coarse_select_mass(const float* qc, const float* kc, const float* vc, in
   if (head_dim != 64 && head_dim != 128) return VSA_ERR_UNSUPPORTED;
   if (n_cubes > coarse_max_cubes(head_dim) || (int64_t)B * heads > 65535) return VSA_ERR_UNSUPPORTED;
   if (!qc || !kc || !vc || !oc || !lse_c || !counts || !ids) return VSA_ERR_INVALID_ARG;
-  if ((int64_t)B * heads * n_cubes > INT_MAX / 2) return VSA_ERR_UNSUPPORTED;
+  if ((int64_t)B * heads * n_cubes > kMaxCubeUnits) return VSA_ERR_UNSUPPORTED;
   const int st = check_mass(mass, k_min, k_max, n_cubes, (int64_t)B * heads * n_cubes);
   if (st != VSA_OK) return st;
   CoarseArgs ca{qc, kc, vc, B, heads, head_dim, n_cubes, 0, oc, lse_c, ids, dtype == VSA_BF16};
@@ -491,7 +495,7 @@ int vsa_coarse_topk(const float* qc, const float* kc, const float* vc,
   if (n_cubes > coarse_max_cubes(head_dim) || (int64_t)B * heads > 65535) return VSA_ERR_UNSUPPORTED;
   if (topk < 0 || topk > n_cubes) return VSA_ERR_INVALID_ARG;
   if (!qc || !kc || !vc || !oc || !lse_c || (topk > 0 && !sel_idx)) return VSA_ERR_INVALID_ARG;
-  if ((int64_t)B * heads * n_cubes > INT_MAX / 2 || (int64_t)B * heads * n_cubes * topk > INT_MAX)
+  if ((int64_t)B * heads * n_cubes > kMaxCubeUnits || (int64_t)B * heads * n_cubes * topk > INT_MAX)
     return VSA_ERR_UNSUPPORTED;
   CoarseArgs ca{qc, kc, vc, B, heads, head_dim, n_cubes, topk, oc, lse_c, sel_idx, dtype == VSA_BF16};
   return hip_status(launch_coarse_topk(ca, stream));
@@ -527,7 +531,7 @@ int vsa_fine_order(const int32_t* kv_offsets, const int32_t* kv_ids, int64_t n_l
                    int topk, int B, int heads, int n_cubes, int32_t* order, hipStream_t stream) {
   if (B < 1 || heads < 1 || n_cubes < 1 || !order) return VSA_ERR_INVALID_ARG;
   if (n_cubes > order_max_cubes() || (int64_t)B * heads > 65535) return VSA_ERR_UNSUPPORTED;
-  if ((int64_t)B * heads * n_cubes > INT_MAX / 2) return VSA_ERR_UNSUPPORTED;
+  if ((int64_t)B * heads * n_cubes > kMaxCubeUnits) return VSA_ERR_UNSUPPORTED;
   if (!kv_offsets) {
     if (topk < 1 || topk > n_cubes || !kv_ids) return VSA_ERR_INVALID_ARG;
     if ((int64_t)B * heads * n_cubes * topk > INT_MAX) return VSA_ERR_UNSUPPORTED;
