@@ -12,7 +12,9 @@ launched on, in the sorted processing order the forward gives it, and in
 natural order for comparison) for the roofline entry, next to its compute
 ceiling on the same data: the fine kernel on a shared selection (every query
 cube picks the same key cubes, so every tile is an L2 hit).  The same line
-carries the coarse stage's share of the step, the backward of the training
+carries the coarse stage's share of the step, the same shape with smooth
+(video-like) cube means, whose neighbouring query cubes select overlapping
+key cubes, the backward of the training
 workload (B=2, 12 heads, 16x32x32, top-K 32) after its forward, and a dense
 reference: the fine kernel with every key cube selected, whose MFU the
 sparse fine stage is compared with.
@@ -88,6 +90,7 @@ def parse():
                         "and smooth inputs")
     p.add_argument("--no-dense", action="store_true", help="skip the dense reference (about 0.1 s of GPU time)")
     p.add_argument("--no-backward", action="store_true", help="skip the training-workload backward")
+    p.add_argument("--no-smooth", action="store_true", help="skip the smooth (video-like) selection case")
     return p.parse_args()
 
 
@@ -260,6 +263,8 @@ def main():
         },
     }
     del kp, vp, fout, q, k, v, gc, gf, out
+    if not a.no_smooth:
+        res["smooth_selections"] = smooth_case(vsa, torch, stream, a)
     if not a.no_backward:
         res["backward_train16k"] = backward_case(vsa, torch, stream, a)
     if not a.no_dense:
@@ -296,28 +301,6 @@ def extra(a, vsa, torch, stream):
         return {"ms": ms, "TFLOPs": fl / (ms * 1e-3) / 1e12, "coarse_topk_ms": ms_c,
                 "coarse_share": ms_c / ms}
 
-    # the headline shape with spatially smooth cube means (neighbouring query
-    # cubes select overlapping key cubes, as in video); context, not the metric
-    w = WORKLOADS["long61k_smooth"]
-    inp = workload_inputs(w, with_varlen=False)
-    q, k, v, gc, gf = (dev(inp[n]) for n in ("q", "k", "v", "gc", "gf"))
-    _, kp, vp, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, w.grid, with_q_tiles=False)
-    oc, _, sel = vsa.vsa_coarse_topk(qc, kc, vc, 32, input_dtype=torch.bfloat16)
-    fout = torch.empty_like(q)
-    order_s = vsa.vsa_fine_order(sel, w.B, w.heads, w.n_cubes, topk=32)
-    ms_fine_s = timed(lambda: vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, w.grid, sel, topk=32, out=fout,
-                                                   order=order_s), steps, warm, stream)
-    ms_fwd_s = timed(lambda: vsa.vsa_forward(q, k, v, gc, gf, w.grid, 32), steps, warm, stream)
-    s_np = sel[0, 0].cpu().numpy()
-    f_s = fine_flops(w.B, w.heads, w.N, 32, w.head_dim)
-    ext["long61k_smooth_k32"] = {
-        "forward_ms": ms_fwd_s,
-        "forward_TFLOPs": (f_s + coarse_flops(w.B, w.heads, w.n_cubes, w.head_dim)) / (ms_fwd_s * 1e-3) / 1e12,
-        "fine_ms": ms_fine_s, "fine_TFLOPs": f_s / (ms_fine_s * 1e-3) / 1e12,
-        "mean_shared_ids_with_next_cube": float(sum(len(set(s_np[c]) & set(s_np[c + 1]))
-                                                   for c in range(len(s_np) - 1)) / (len(s_np) - 1))}
-    del q, k, v, gc, gf, kp, vp, fout, inp
-
     # the stand-in variable-length rule (mass 0.2 of the coarse probability,
     # lists clamped to [8, 64]) on the headline shape
     w = WORKLOADS["long61k"]
@@ -353,6 +336,36 @@ def extra(a, vsa, torch, stream):
     del q, k, v, gc, gf, offs, ids, inp
 
     return ext
+
+
+def smooth_case(vsa, torch, stream, a):
+    """The headline shape with spatially smooth cube means: neighbouring
+    query cubes select overlapping key cubes, as in video.  Context beside
+    the random-selection headline, not the metric."""
+    from workloads import WORKLOADS, coarse_flops, fine_flops, workload_inputs
+    dev = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda().contiguous()
+    steps, warm = max(3, a.steps // 2), 2
+    w = WORKLOADS["long61k_smooth"]
+    inp = workload_inputs(w, with_varlen=False)
+    q, k, v, gc, gf = (dev(inp[n]) for n in ("q", "k", "v", "gc", "gf"))
+    del inp
+    _, kp, vp, qc, kc, vc = vsa.vsa_cube_permute_pool(q, k, v, w.grid, with_q_tiles=False)
+    oc, _, sel = vsa.vsa_coarse_topk(qc, kc, vc, 32, input_dtype=torch.bfloat16)
+    fout = torch.empty_like(q)
+    order_s = vsa.vsa_fine_order(sel, w.B, w.heads, w.n_cubes, topk=32)
+    ms_fine_s = timed(lambda: vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, w.grid, sel, topk=32, out=fout,
+                                                   order=order_s), steps, warm, stream)
+    ms_fwd_s = timed(lambda: vsa.vsa_forward(q, k, v, gc, gf, w.grid, 32), steps, warm, stream)
+    s_np = sel[0, 0].cpu().numpy()
+    f_s = fine_flops(w.B, w.heads, w.N, 32, w.head_dim)
+    return {
+        "workload": "long61k with smooth cube means (video-like selections), top-K 32",
+        "forward_ms": ms_fwd_s,
+        "forward_TFLOPs": (f_s + coarse_flops(w.B, w.heads, w.n_cubes, w.head_dim)) / (ms_fwd_s * 1e-3) / 1e12,
+        "fine_ms": ms_fine_s, "fine_TFLOPs": f_s / (ms_fine_s * 1e-3) / 1e12,
+        "fine_frac_of_peak": f_s / (ms_fine_s * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "mean_shared_ids_with_next_cube": float(sum(len(set(s_np[c]) & set(s_np[c + 1]))
+                                                   for c in range(len(s_np) - 1)) / (len(s_np) - 1))}
 
 
 def backward_case(vsa, torch, stream, a):
