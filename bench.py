@@ -185,7 +185,7 @@ def main():
                   a.steps, a.warmup, stream)
     ms_coarse = timed(lambda: vsa.vsa_coarse_topk(qc, kc, vc, K, input_dtype=torch.bfloat16), a.steps, a.warmup, stream)
     # the processing order the forward gives the fine kernel (query cubes
-    # sorted by their lists' middle entries), and the fine kernel with it
+    # sorted by where their lists' quarter points lie), and the fine kernel with it
     order = vsa.vsa_fine_order(sel2, w.B, w.heads, w.n_cubes, topk=K)
     ms_order = timed(lambda: vsa.vsa_fine_order(sel2, w.B, w.heads, w.n_cubes, topk=K), a.steps, a.warmup, stream)
     fout = torch.empty_like(q)

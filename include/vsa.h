@@ -297,11 +297,13 @@ int vsa_fine_forward(const void* q, const void* kp, const void* vp,
                      const int32_t* order, hipStream_t stream);
 
 /* Processing order for the fine stage: each (b, h)'s query cubes sorted by
- * the middle entry (index n/2) of their key list, cube index on ties, as
- * global ids into order [B*heads*Nc] (int32).  Lists as in
- * vsa_fine_forward; an empty list, or a middle entry outside [0, Nc),
- * counts as middle entry 0.  With ascending
- * lists, cubes whose lists are centred alike then run side by side and
+ * a key made from the entries at indices n/4 and 3n/4 of their key list of
+ * n: each entry e becomes the 9-bit coordinate floor(e * 512 / Nc), and the
+ * key interleaves the two (bit j of the first at bit 2j + 1, of the second
+ * at bit 2j); cube index breaks ties.  Written as global ids into order
+ * [B*heads*Nc] (int32).  Lists as in vsa_fine_forward; an empty list has
+ * key 0, and an entry outside [0, Nc) counts as 0.  With ascending lists,
+ * cubes whose lists cover similar key ranges then run side by side and
  * share more tile reads through the L2.  The forward entry points use it
  * for bf16 inputs.  Nc <= 4096. */
 int vsa_fine_order(const int32_t* kv_offsets, const int32_t* kv_ids,

@@ -300,11 +300,41 @@ def test_varlen_with_topk_lists_reproduces_vsa_forward():
     assert_close(host64(out3), host64(out), BF16, "shuffled lists")
 
 
-def test_fine_order_sorts_by_middle_entry_and_changes_nothing():
+def _order_key(p1, p3, nc):
+    """The processing order's sort key: the list entries at a quarter and
+    at three quarters, each scaled to 9 bits (id * 512 // Nc), as a Morton
+    code with the first point's bits above the second's."""
+    x = (np.asarray(p1, dtype=np.int64) << 9) // nc
+    y = (np.asarray(p3, dtype=np.int64) << 9) // nc
+    key = np.zeros_like(x)
+    for j in range(9):
+        key |= ((x >> j) & 1) << (2 * j + 1)
+        key |= ((y >> j) & 1) << (2 * j)
+    return key
+
+
+def _want_order(keys):
+    """keys [n_bh, nc]: ascending key, cube index on ties, as global ids."""
+    n_bh, nc = keys.shape
+    return np.concatenate([bh * nc + np.lexsort((np.arange(nc), keys[bh])) for bh in range(n_bh)])
+
+
+def test_order_key_model():
+    """The test's model of the sort key on hand-worked values (Nc = 512, so
+    ids are their own 9-bit coordinates): the first point's bits land on
+    the odd positions."""
+    assert _order_key([1], [0], 512)[0] == 0b10
+    assert _order_key([0], [1], 512)[0] == 0b01
+    assert _order_key([3], [5], 512)[0] == 0b11011  # x = 0b011 on bits 1, 3; y = 0b101 on bits 0, 4
+    assert _order_key([511], [511], 512)[0] == (1 << 18) - 1
+    assert _order_key([959], [480], 960)[0] == _order_key([511], [256], 512)[0]  # 959 * 512 // 960 = 511
+
+
+def test_fine_order_sorts_by_quartile_entries_and_changes_nothing():
     """The fine stage's processing order: each (b, h)'s query cubes sorted by
-    the middle entry of their list, cube index on ties (exact), for fixed
-    and CSR lists with empty ones; running in that order leaves the output
-    bitwise unchanged."""
+    the Morton code of their lists' entries at indices n/4 and 3n/4, cube
+    index on ties (exact), for fixed and CSR lists with empty ones; running
+    in that order leaves the output bitwise unchanged."""
     vsa = _vsa()
     B, nh, D, grid, K = 2, 3, 128, (8, 12, 16), 5  # 24 cubes
     nc = 24
@@ -314,26 +344,27 @@ def test_fine_order_sorts_by_middle_entry_and_changes_nothing():
     oc, _, sel = vsa.vsa_coarse_topk(qc, kc, vc, K, input_dtype=BF16)
     order = vsa.vsa_fine_order(sel, B, nh, nc, topk=K)
     torch.cuda.synchronize()
-    mid = sel.cpu().numpy().reshape(B * nh, nc, K)[:, :, K // 2]
-    want = np.concatenate([bh * nc + np.lexsort((np.arange(nc), mid[bh])) for bh in range(B * nh)])
-    np.testing.assert_array_equal(order.cpu().numpy(), want)
+    s3 = sel.cpu().numpy().reshape(B * nh, nc, K)
+    np.testing.assert_array_equal(order.cpu().numpy(),
+                                  _want_order(_order_key(s3[:, :, K // 4], s3[:, :, (3 * K) // 4], nc)))
     out0, _, _ = vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, grid, sel, topk=K)
     out1, _, _ = vsa.vsa_fine_forward(q, kp, vp, oc, gc, gf, grid, sel, topk=K, order=order)
     torch.cuda.synchronize()
     assert torch.equal(out0, out1)
     offs, ids = inp["kv_offsets"], inp["kv_ids"]
-    assert (np.diff(offs) == 0).any()
+    assert (np.diff(offs) == 0).any() and (np.diff(offs) == 1).any()
     order = vsa.vsa_fine_order(torch.from_numpy(ids).cuda(), B, nh, nc,
                                kv_offsets=torch.from_numpy(offs).cuda())
     torch.cuda.synchronize()
-    mids = np.array([ids[a + (b - a) // 2] if b > a else 0 for a, b in zip(offs[:-1], offs[1:])])
-    mids = mids.reshape(B * nh, nc)
-    want = np.concatenate([bh * nc + np.lexsort((np.arange(nc), mids[bh])) for bh in range(B * nh)])
-    np.testing.assert_array_equal(order.cpu().numpy(), want)
+    n = np.diff(offs)
+    p1 = np.where(n > 0, ids[np.minimum(offs[:-1] + n // 4, len(ids) - 1)], 0)
+    p3 = np.where(n > 0, ids[np.minimum(offs[:-1] + (3 * n) // 4, len(ids) - 1)], 0)
+    keys = np.where(n > 0, _order_key(p1, p3, nc), 0).reshape(B * nh, nc)
+    np.testing.assert_array_equal(order.cpu().numpy(), _want_order(keys))
     # larger (b, h) blocks, drawn directly: random sorted lists up to the
     # sort's 4096-cube limit, and identical lists (one bucket of every cube)
     rng = np.random.default_rng(64)
-    for n_bh, nc, K, same in ((3, 512, 16, False), (2, 4096, 32, False), (2, 960, 32, True)):
+    for n_bh, nc, K, same in ((3, 512, 16, False), (2, 4096, 32, False), (2, 960, 32, True), (2, 960, 1, False)):
         if same:
             lists = np.broadcast_to(np.arange(K, dtype=np.int32), (n_bh * nc, K))
         else:
@@ -341,9 +372,9 @@ def test_fine_order_sorts_by_middle_entry_and_changes_nothing():
         lists = np.ascontiguousarray(lists, dtype=np.int32)
         order = vsa.vsa_fine_order(torch.from_numpy(lists).cuda(), 1, n_bh, nc, topk=K)
         torch.cuda.synchronize()
-        mid = lists.reshape(n_bh, nc, K)[:, :, K // 2]
-        want = np.concatenate([bh * nc + np.lexsort((np.arange(nc), mid[bh])) for bh in range(n_bh)])
-        np.testing.assert_array_equal(order.cpu().numpy(), want)
+        l3 = lists.reshape(n_bh, nc, K)
+        np.testing.assert_array_equal(order.cpu().numpy(),
+                                      _want_order(_order_key(l3[:, :, K // 4], l3[:, :, (3 * K) // 4], nc)))
 
 
 def test_fine_order_entries_out_of_range_run_nothing():

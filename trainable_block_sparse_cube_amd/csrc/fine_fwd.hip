@@ -25,9 +25,9 @@
 // reads (ds_read_b64_tr_b16).  The epilogue divides by the row sum, mixes
 // in the coarse output with the two gates, rounds once to bf16 and
 // scatters rows back to raster token order.  Query cubes run in the order
-// given (the forward sorts them by their lists' middle entries, so that
-// cubes sweeping similar key ranges share an XCD's L2 at the same time),
-// or in natural order.
+// given (the forward sorts them by where their lists' quarter and
+// three-quarter entries lie, so that cubes sweeping similar key ranges
+// share an XCD's L2 at the same time), or in natural order.
 //
 // fp32 kernel: plain VALU, one 256-thread workgroup per query cube; it
 // serves the fp32 path, where no reduced precision is allowed.

@@ -1,20 +1,25 @@
 // Processing order of the fine stage's query cubes.
 //
-// Each query cube streams the tiles of its selected key cubes in ascending
-// cube order ([VSA-sum, Approach]: the fine stage attends inside the
-// selected cubes; the order within a list is free).  Query cubes whose
-// lists have similar middle entries sweep similar key ranges at the same
-// time, so when such cubes run side by side on one XCD more of their tile
-// reads hit its L2.  This kernel sorts each (batch, head)'s query cubes by
-// the middle entry of their list, cube index breaking ties: one workgroup
-// per (b, h), a stable least-significant-digit radix sort of the 12-bit
-// middle entries in two passes of 6 bits, starting from cube order.  In a
-// pass every wave ranks its 64 entries among those with the same digit
+// Each query cube streams the tiles of its selected key cubes in list order
+// (ascending for the coarse stage's own lists; [VSA-sum, Approach]: the
+// fine stage attends inside the selected cubes, and the order within a
+// list is free).  Query cubes whose lists cover similar key ranges sweep
+// them at the same time, so when such cubes run side by side on one XCD
+// more of their tile reads hit its L2.  This kernel sorts each (batch,
+// head)'s query cubes by a Morton code of two points of their list: the
+// entries at a quarter and at three quarters of it (indices n/4 and 3n/4),
+// each scaled to 9 bits (id * 512 / Nc), interleaved with the first
+// quarter's bits above the second's; cube index breaks ties.  Two points
+// place a list by where its lower and upper halves lie, which groups lists
+// more tightly than their middle entry alone (fewer tile reads beyond L2).
+// One workgroup per (b, h) runs a stable least-significant-digit radix sort
+// of the 18-bit codes in three passes of 6 bits, starting from cube order.
+// In a pass every wave ranks its 64 entries among those with the same digit
 // (peer masks from six ballots), the per-(digit, tile, wave) counts are
-// scanned in (digit, tile, wave) order, and each entry moves to its
-// digit's offset plus its rank, which keeps equal digits in input order.
-// The result only reorders work: every query cube's own arithmetic, hence
-// the output, is unchanged.
+// scanned in (digit, tile, wave) order, and each entry moves to its digit's
+// offset plus its rank, which keeps equal digits in input order.  The
+// result only reorders work: every query cube's own arithmetic, hence the
+// output, is unchanged.
 #include "vsa_device.h"
 #include "vsa_launch.h"
 
@@ -26,16 +31,33 @@ constexpr int kOrderThreads = 1024;
 constexpr int kOrderWaves = kOrderThreads / 64;
 constexpr int kOrderMax = 4096;                        // cubes per (b, h) this sort holds
 constexpr int kOrderTiles = kOrderMax / kOrderThreads;  // entries per thread
-constexpr int kDigitBits = 6;                          // two passes cover ids < 4096
+constexpr int kCoordBits = 9;                          // each list point scaled to 9 bits
+constexpr int kKeyBits = 2 * kCoordBits;                // Morton code of the two points
+constexpr int kDigitBits = 6;
+constexpr int kPasses = (kKeyBits + kDigitBits - 1) / kDigitBits;  // 3
 constexpr int kDigits = 1 << kDigitBits;
 constexpr int kBins = kDigits * kOrderTiles * kOrderWaves;
-static_assert(2 * kDigitBits >= 12 && kOrderMax <= 4096, "two passes of the 12-bit ids");
+static_assert(kPasses * kDigitBits >= kKeyBits, "passes cover the key");
 static_assert(kBins % kOrderThreads == 0, "scan layout");
 
-__global__ __launch_bounds__(kOrderThreads) void order_by_middle_kernel(
+// Entry i of a list of n as a 9-bit coordinate (out-of-range ids count as 0).
+__device__ __forceinline__ uint32_t list_point(const int32_t* __restrict__ ids, int64_t start, int i,
+                                               int nc) {
+  return (uint32_t)(((int64_t)cube_or_0(ids[start + i], nc) << kCoordBits) / nc);
+}
+
+// Bits of a above those of b, interleaved: bit j of a -> 2j + 1, of b -> 2j.
+__device__ __forceinline__ uint32_t morton2(uint32_t a, uint32_t b) {
+  uint32_t key = 0;
+#pragma unroll
+  for (int j = 0; j < kCoordBits; ++j) key |= (((a >> j) & 1u) << (2 * j + 1)) | (((b >> j) & 1u) << (2 * j));
+  return key;
+}
+
+__global__ __launch_bounds__(kOrderThreads) void order_by_quartiles_kernel(
     const int32_t* __restrict__ offs, const int32_t* __restrict__ ids, int topk, int64_t n_ids,
     int nc, int32_t* __restrict__ order) {
-  __shared__ uint16_t mid_of[kOrderMax];  // middle entry of each cube's list
+  __shared__ uint32_t key_of[kOrderMax];  // sort key of each cube's list
   __shared__ uint16_t seq[2][kOrderMax];  // cubes in the current / next order
   __shared__ int32_t bins[kBins];         // counts per (digit, tile, wave), then their offsets
   __shared__ int32_t wsum[kOrderWaves];
@@ -46,13 +68,14 @@ __global__ __launch_bounds__(kOrderThreads) void order_by_middle_kernel(
     int64_t start;
     int n;
     list_range(offs, base + c, topk, n_ids, &start, &n);
-    mid_of[c] = (uint16_t)(n > 0 ? cube_or_0(ids[start + n / 2], nc) : 0);  // an empty list counts as 0
+    // an empty list counts as key 0
+    key_of[c] = n > 0 ? morton2(list_point(ids, start, n / 4, nc), list_point(ids, start, (3 * n) / 4, nc)) : 0u;
     seq[0][c] = (uint16_t)c;
   }
   const uint64_t below = (1ull << lane) - 1ull;
-  for (int pass = 0; pass < 2; ++pass) {
-    const uint16_t* src = seq[pass];
-    uint16_t* dst = seq[pass ^ 1];
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const uint16_t* src = seq[pass & 1];
+    uint16_t* dst = seq[(pass & 1) ^ 1];
     for (int i = tid; i < kBins; i += kOrderThreads) bins[i] = 0;
     __syncthreads();
     int digit[kOrderTiles], rank[kOrderTiles];
@@ -60,7 +83,7 @@ __global__ __launch_bounds__(kOrderThreads) void order_by_middle_kernel(
     for (int u = 0; u < kOrderTiles; ++u) {
       const int idx = u * kOrderThreads + tid;
       const bool live = idx < nc;
-      const int d = live ? (mid_of[src[idx]] >> (kDigitBits * pass)) & (kDigits - 1) : 0;
+      const int d = live ? (int)(key_of[src[idx]] >> (kDigitBits * pass)) & (kDigits - 1) : 0;
       uint64_t peers = __ballot(live);
 #pragma unroll
       for (int b = 0; b < kDigitBits; ++b) {
@@ -106,7 +129,7 @@ __global__ __launch_bounds__(kOrderThreads) void order_by_middle_kernel(
     }
     __syncthreads();
   }
-  for (int i = tid; i < nc; i += kOrderThreads) order[base + i] = (int32_t)(base + seq[0][i]);
+  for (int i = tid; i < nc; i += kOrderThreads) order[base + i] = (int32_t)(base + seq[kPasses & 1][i]);
 }
 
 }  // namespace
@@ -115,7 +138,7 @@ int order_max_cubes() { return kOrderMax; }
 
 hipError_t launch_fine_order(const int32_t* offs, const int32_t* ids, int topk, int64_t n_ids,
                              int n_bh, int nc, int32_t* order, hipStream_t st) {
-  order_by_middle_kernel<<<(unsigned)n_bh, kOrderThreads, 0, st>>>(offs, ids, topk, n_ids, nc, order);
+  order_by_quartiles_kernel<<<(unsigned)n_bh, kOrderThreads, 0, st>>>(offs, ids, topk, n_ids, nc, order);
   return hipGetLastError();
 }
 

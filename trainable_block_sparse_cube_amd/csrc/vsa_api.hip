@@ -199,7 +199,7 @@ int forward_impl(const void* q, const void* k, const void* v, const void* gc, co
   if (!offs) n_ids = (int64_t)rows * topk;
   FineArgs fa{q, kp, vp, oc, gc, gf, s.B, s.heads, s.D, s.T, s.H, s.W,
               offs, offs ? ids : sel, topk, n_ids, bf, out, lse_f, of};
-  if (bf) {  // the MFMA kernel runs the query cubes sorted by their lists' middle entries
+  if (bf) {  // the MFMA kernel runs the query cubes sorted by where their lists lie
     e = launch_fine_order(fa.offs, fa.ids, topk, n_ids, s.B * s.heads, (int)s.nc, w.order, st);
     if (e != hipSuccess) return VSA_ERR_HIP;
     fa.order = w.order;

@@ -94,8 +94,9 @@ struct FineArgs {
   const int32_t* order = nullptr;  // processing order of the query cubes (global ids), optional
 };
 hipError_t launch_fine_forward(const FineArgs& a, hipStream_t st);
-// Query cubes of each (b, h) sorted by the middle entry of their key list
-// (cube index on ties), as global ids bh*nc + c, into order[n_bh*nc].
+// Query cubes of each (b, h) sorted by a Morton code of the entries at a
+// quarter and three quarters of their key list (cube index on ties), as
+// global ids bh*nc + c, into order[n_bh*nc].
 int order_max_cubes();
 hipError_t launch_fine_order(const int32_t* offs, const int32_t* ids, int topk, int64_t n_ids,
                              int n_bh, int nc, int32_t* order, hipStream_t st);

@@ -452,7 +452,8 @@ def vsa_fine_forward(q, kp, vp, oc, gate_c, gate_f, grid, kv_ids, topk=0, kv_off
 
 def vsa_fine_order(kv_ids, B, heads, n_cubes, topk=0, kv_offsets=None):
     """Processing order for the fine stage (each (b, h)'s query cubes sorted
-    by the middle entry of their list).  Returns int32 [B * heads * Nc]."""
+    by a Morton code of their lists' entries at indices n/4 and 3n/4).
+    Returns int32 [B * heads * Nc]."""
     lib = _lib.load()
     _need(kv_ids, "kv_ids", torch.int32, device=kv_ids.device)
     if kv_offsets is not None:
